@@ -1,0 +1,52 @@
+"""Seeded synthetic inputs shared by the tests, the bench and the oracle checks.
+
+This module holds no attention arithmetic: it only draws random tensors.
+Recipe: a CPU ``torch.Generator`` seeded with ``seed`` draws i.i.d. N(0, 1)
+fp32 tensors of shape [B, N, H, d] in the order Q, K, V, dO (dO only when
+asked), optionally multiplied by ``gain``, then cast to the requested dtype
+(bf16 casts round to nearest even).  The oracle is fed the cast values
+upcast to fp64, which is exact for both fp32 and bf16.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+__all__ = ["make_qkv", "to_f64"]
+
+
+def make_qkv(B, N, H, d, dtype=torch.bfloat16, seed=0, with_do=False, gain=1.0):
+    """Return a dict with CPU tensors 'q', 'k', 'v' (and 'do') of shape [B,N,H,d]."""
+    g = torch.Generator().manual_seed(int(seed))
+    names = ["q", "k", "v"] + (["do"] if with_do else [])
+    out = {}
+    for name in names:
+        t = torch.randn((B, N, H, d), generator=g, dtype=torch.float32)
+        if gain != 1.0:
+            t = t * gain
+        out[name] = t.to(dtype).contiguous()
+    return out
+
+
+def to_f64(t):
+    """CPU/GPU torch tensor -> numpy fp64 (exact for fp32 and bf16)."""
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def pick_rows(B, H, N, count, seed=1234, include_edges=True):
+    """Deterministic sample of (b, h, i) query rows for sampled parity checks.
+
+    Always includes the first and last row of the first and last head, so the
+    sample covers the causal edge cases and the ragged tail.
+    """
+    rng = np.random.default_rng(seed)
+    picks = set()
+    if include_edges:
+        for b, h in ((0, 0), (B - 1, H - 1)):
+            for i in (0, 1, N - 2, N - 1):
+                if 0 <= i < N:
+                    picks.add((b, h, i))
+    while len(picks) < count + (8 if include_edges else 0) and len(picks) < B * H * N:
+        picks.add((int(rng.integers(B)), int(rng.integers(H)), int(rng.integers(N))))
+    return sorted(picks)

@@ -1,0 +1,100 @@
+"""Workload catalogue and the work/traffic counting used by the bench.
+
+Counting convention: the forward does 4*N*N*d flops per head (two N x N x d
+products), the backward 2.5 times that (five such products, including the
+recomputation of Q K^T that the pages note makes the total flop count slightly
+higher; "Speicherbedarf und Laufzeitverhalten" on the explainer page), and a
+causal mask halves both.
+
+The compulsory HBM bytes are the tensors that must cross HBM at least once:
+forward reads Q, K, V and writes O and LSE; backward reads Q, K, V, O, dO, LSE
+and writes dQ, dK, dV, plus its own small row-statistic buffer and the fp32
+dQ accumulator.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+
+def score_entries(n: int) -> int:
+    """Entries of one N x N score matrix (explainer page, introduction)."""
+    return n * n
+
+
+def score_bytes(n: int, elem_bytes: int = 2, heads: int = 1) -> int:
+    """Bytes to materialise the N x N score matrix for ``heads`` heads."""
+    return score_entries(n) * elem_bytes * heads
+
+
+def tile_bytes(rows: int, cols: int, elem_bytes: int = 2) -> int:
+    """Bytes of one rows x cols score tile (explainer page, "Tiling")."""
+    return rows * cols * elem_bytes
+
+
+def fwd_flops(B, H, N, d, causal):
+    f = 4.0 * N * N * d * B * H
+    return f / 2 if causal else f
+
+
+def bwd_flops(B, H, N, d, causal):
+    return 2.5 * fwd_flops(B, H, N, d, causal)
+
+
+def fwd_bytes(B, H, N, d, elem=2):
+    """Compulsory HBM bytes of one forward: read Q,K,V, write O, LSE (fp32)."""
+    return B * H * (4 * N * d * elem + 4 * N)
+
+
+def bwd_bytes(B, H, N, d, elem=2):
+    """Compulsory HBM bytes of one backward including the fp32 dQ accumulator.
+
+    Reads Q, K, V, O, dO (5 N d elem) and LSE, writes dQ, dK, dV (3 N d elem),
+    writes then reads the row statistic D (2 x 4N) and the fp32 dQ
+    accumulator (zero-fill, read-modify-write traffic counted once each way:
+    2 x 4 N d), and the final dQ conversion read (4 N d).
+    """
+    return B * H * (8 * N * d * elem + 4 * N + 8 * N + 12 * N * d)
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    causal: bool
+    dtype: str            # "bf16" or "f32"
+    seed: int
+    backward: bool = False
+    gain: float = 1.0
+    note: str = ""
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / (self.d ** 0.5)
+
+
+# The five workloads of the method's evaluation (synthetic N(0,1) inputs).
+SINGLE_HEAD_F32 = Workload("single_head_f32_n1024_d64", 1, 1, 1024, 64, False, "f32", 1,
+                           note="fp32 path, K/V block 256")
+MHA_N4096_D128 = Workload("mha_b4_h32_n4096_d128", 4, 32, 4096, 128, False, "bf16", 2)
+MHA_N4096_D128_CAUSAL = Workload("mha_b4_h32_n4096_d128_causal", 4, 32, 4096, 128, True,
+                                 "bf16", 2)
+LONG_CAUSAL = Workload("long_b1_h32_n16384_d128_causal", 1, 32, 16384, 128, True, "bf16", 3)
+BWD_CAUSAL_D64 = Workload("bwd_b4_h16_n4096_d64_causal", 4, 16, 4096, 64, True, "bf16", 4,
+                          backward=True)
+
+
+def sweep(d: int):
+    """Fixed 16384 tokens per batch, H=16, non-causal, fwd+bwd."""
+    out = []
+    for n in (512, 1024, 2048, 4096, 8192, 16384):
+        out.append(Workload(f"sweep_n{n}_d{d}", 16384 // n, 16, n, d, False, "bf16", 5,
+                            backward=True))
+    return out
+
+
+ALL = [SINGLE_HEAD_F32, MHA_N4096_D128, MHA_N4096_D128_CAUSAL, LONG_CAUSAL, BWD_CAUSAL_D64]

@@ -1,0 +1,226 @@
+"""Plain fp64 CPU oracle for exact (FlashAttention) attention.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, ``__graft_entry__.smoke()``
+and the ``cpu_baseline`` leg of ``bench.py`` may import or call this module.
+The product path (the HIP library and its Python binding) never touches it,
+and this module imports nothing from that path: it takes numpy arrays and
+returns numpy arrays.
+
+What it computes is the *definition* of attention, not the tiled algorithm.
+The pages state that the tiled method is exact up to floating-point rounding
+("FlashAttention" explainer, sections "Speicherbedarf und Laufzeitverhalten"
+and "Grenzen und Einschraenkungen"; glossary page, introduction), so the plain
+definition is the right reference:
+
+* scores  S = scale * Q K^T  (glossary page, "How it works", the standard
+  attention line of its PyTorch sketch; the 1/sqrt(d) scale is the pages'
+  choice and is an argument here),
+* optional causal mask: query i sees key j only when j <= i (the pages name
+  causal vs. bidirectional masks in the "Grenzen, Stolpersteine" section of the
+  kernel-engineering page without defining it; lower-triangular is the
+  reading taken),
+* softmax over the whole row, done in two passes (row max, then exponentials
+  and their sum), the numerically stable form the pages describe,
+* O = P V, and the per-row statistics exported as one log-sum-exp
+  LSE = m + ln(l) (the pages keep "max and sum per row"; LSE carries the same
+  information, P = exp(S - LSE)).
+
+The backward pass has no formula on the pages beyond "recompute the scores
+from Q, K (and V) instead of storing N x N" ("Recomputation beim
+Rueckwaertsdurchlauf"; glossary "How it works").  The oracle uses the textbook
+softmax Jacobian:
+
+    dV = P^T dO,  dP = dO V^T,  Delta_i = sum_j P_ij dP_ij,
+    dS = P * (dP - Delta),  dQ = scale * dS K,  dK = scale * dS^T Q.
+
+Delta is taken in its definition form (a row sum over the N x N product); the
+GPU path uses the equivalent row dot product of dO and O.
+
+Tensors use the [B, N, H, d] layout; LSE uses [B, H, N].
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "head_forward",
+    "head_backward",
+    "head_forward_blockwise",
+    "head_probabilities",
+    "forward",
+    "backward",
+    "forward_rows",
+]
+
+
+def _f64(x):
+    """Upcast any float array (fp32, bf16-as-fp32, fp64) to fp64 exactly."""
+    return np.asarray(x, dtype=np.float64)
+
+
+def _visible(nq: int, nk: int, causal: bool, rows=None):
+    """Boolean mask [len(rows), nk]: True where query row i may see key j.
+
+    Causal means key j is visible to query i when j <= i (square N x N case).
+    """
+    r = np.arange(nq) if rows is None else np.asarray(rows)
+    if not causal:
+        return np.ones((r.shape[0], nk), dtype=bool)
+    return np.arange(nk)[None, :] <= r[:, None]
+
+
+def head_probabilities(q, k, scale, causal, rows=None):
+    """Return (P, m, l) for one head by the two-pass softmax of the definition.
+
+    q: [Nq, d], k: [Nk, d].  ``rows`` optionally selects query rows (absolute
+    indices, used by the causal mask).  Masked scores are -inf, so their
+    probability is exactly 0.
+    """
+    q = _f64(q)
+    k = _f64(k)
+    nq = q.shape[0]
+    if rows is not None:
+        q = q[np.asarray(rows)]
+    s = scale * (q @ k.T)
+    s = np.where(_visible(nq, k.shape[0], causal, rows), s, -np.inf)
+    # pass 1: row maximum
+    m = s.max(axis=1)
+    # pass 2: exponentials relative to the maximum, and their sum
+    e = np.exp(s - m[:, None])
+    l = e.sum(axis=1)
+    return e / l[:, None], m, l
+
+
+def head_forward(q, k, v, scale, causal, rows=None):
+    """One head: O = softmax(scale Q K^T [masked]) V and LSE = m + ln l.
+
+    Returns (O [len(rows) or N, d], LSE [len(rows) or N]) in fp64.
+    """
+    p, m, l = head_probabilities(q, k, scale, causal, rows)
+    o = p @ _f64(v)
+    lse = m + np.log(l)
+    return o, lse
+
+
+def head_backward(q, k, v, do, scale, causal):
+    """One head: (dQ, dK, dV) of L = sum(O * dO) by the softmax Jacobian.
+
+    P is recomputed from the definition (no stored N x N from a forward).
+    """
+    q = _f64(q)
+    k = _f64(k)
+    v = _f64(v)
+    do = _f64(do)
+    p, _, _ = head_probabilities(q, k, scale, causal)
+    dv = p.T @ do
+    dp = do @ v.T
+    delta = (p * dp).sum(axis=1)          # definition form of Delta_i
+    ds = p * (dp - delta[:, None])        # masked entries: p == 0 -> ds == 0
+    dq = scale * (ds @ k)
+    dk = scale * (ds.T @ q)
+    return dq, dk, dv
+
+
+def head_forward_blockwise(q, k, v, scale, causal, block, dtype=np.float64):
+    """The tiled online-softmax forward over key/value blocks, for self-tests.
+
+    This follows the streaming description on the glossary page ("How it
+    works"): for each key/value block compute the scores, raise the running
+    row maximum, rescale the running sum and the partial output by
+    exp(old max - new max), add the block's exponentials and their product
+    with V, and divide by the running sum once at the end.  ``dtype`` selects
+    the arithmetic precision (fp64 by default, fp32 to reproduce the page's
+    worked example).  It is never used to check the GPU; it pins the claim
+    that the blockwise result equals the full softmax.
+    """
+    q = np.asarray(q, dtype=dtype)
+    k = np.asarray(k, dtype=dtype)
+    v = np.asarray(v, dtype=dtype)
+    n, d = q.shape
+    nk = k.shape[0]
+    sc = dtype(scale)
+    run_max = np.full((n, 1), -np.inf, dtype=dtype)
+    run_sum = np.zeros((n, 1), dtype=dtype)
+    acc = np.zeros((n, v.shape[1]), dtype=dtype)
+    qi = np.arange(n)[:, None]
+    largest_tile = (0, 0)
+    for start in range(0, nk, block):
+        kb = k[start:start + block]
+        vb = v[start:start + block]
+        s = (q @ kb.T) * sc
+        largest_tile = max(largest_tile, s.shape)
+        if causal:
+            kj = np.arange(start, start + kb.shape[0])[None, :]
+            s = np.where(kj <= qi, s, dtype(-np.inf))
+        blk_max = s.max(axis=1, keepdims=True)
+        new_max = np.maximum(run_max, blk_max)
+        # a row that has seen no visible key yet keeps max -inf; subtract 0
+        safe = np.where(np.isfinite(new_max), new_max, dtype(0))
+        alpha = np.exp(run_max - safe)
+        p = np.exp(s - safe)
+        run_sum = run_sum * alpha + p.sum(axis=1, keepdims=True)
+        acc = acc * alpha + p @ vb
+        run_max = new_max
+    o = acc / run_sum
+    lse = (run_max + np.log(run_sum))[:, 0]
+    return o, lse, largest_tile
+
+
+def _heads_of(b, h, heads):
+    if heads is None:
+        return [(bi, hi) for bi in range(b) for hi in range(h)]
+    return [tuple(x) for x in heads]
+
+
+def forward(q, k, v, scale, causal, heads=None):
+    """[B,N,H,d] forward.  Returns O [B,N,H,d] and LSE [B,H,N] in fp64.
+
+    ``heads`` optionally restricts the work to a list of (b, h) pairs; the
+    other entries of the outputs are NaN.
+    """
+    B, N, H, d = q.shape
+    o = np.full((B, N, H, v.shape[3]), np.nan)
+    lse = np.full((B, H, N), np.nan)
+    for b, h in _heads_of(B, H, heads):
+        oh, lh = head_forward(q[b, :, h, :], k[b, :, h, :], v[b, :, h, :], scale, causal)
+        o[b, :, h, :] = oh
+        lse[b, h, :] = lh
+    return o, lse
+
+
+def forward_rows(q, k, v, scale, causal, picks):
+    """Forward for selected query rows only.
+
+    ``picks`` is a list of (b, h, i).  Returns (O rows [len, d], LSE [len]).
+    Each row depends only on its query and the visible keys of its head, so
+    this is the definition evaluated row by row; used to sample outputs of
+    workloads too large for a full fp64 N x N per head.
+    """
+    out_o = []
+    out_l = []
+    for b, h, i in picks:
+        oh, lh = head_forward(q[b, :, h, :], k[b, :, h, :], v[b, :, h, :], scale, causal,
+                              rows=[i])
+        out_o.append(oh[0])
+        out_l.append(lh[0])
+    return np.array(out_o), np.array(out_l)
+
+
+def backward(q, k, v, do, scale, causal, heads=None):
+    """[B,N,H,d] backward.  Returns dQ, dK, dV in fp64 ([B,N,H,d]).
+
+    ``heads`` optionally restricts the work to a list of (b, h) pairs; the
+    other entries are NaN.
+    """
+    B, N, H, d = q.shape
+    dq = np.full(q.shape, np.nan)
+    dk = np.full(k.shape, np.nan)
+    dv = np.full(v.shape, np.nan)
+    for b, h in _heads_of(B, H, heads):
+        a, bb, c = head_backward(q[b, :, h, :], k[b, :, h, :], v[b, :, h, :],
+                                 do[b, :, h, :], scale, causal)
+        dq[b, :, h, :] = a
+        dk[b, :, h, :] = bb
+        dv[b, :, h, :] = c
+    return dq, dk, dv

@@ -1,0 +1,368 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+None of these compares the oracle with itself: each check is a closed form,
+an invariant, a textbook special case evaluated by an independent library
+routine, brute-force finite differences, or a number printed on the pages.
+The mutation tests at the bottom plant plausible mistakes in copies of the
+oracle and show that at least one pin catches each of them.
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import (backward, forward, forward_rows, head_backward, head_forward,
+                    head_forward_blockwise, head_probabilities)
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rnd(*shape, seed=0):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+# --------------------------------------------------------------------------
+# Pin helpers: each takes a per-head forward callable f(q, k, v, scale, causal)
+# returning (O, LSE) so the mutation tests can run them on broken oracles.
+# --------------------------------------------------------------------------
+
+def pin_single_key(f):
+    """N = 1: the only key gets probability 1, so O = V and LSE = scale q.k."""
+    for causal in (False, True):
+        q, k, v = rnd(1, 8, seed=1), rnd(1, 8, seed=2), rnd(1, 8, seed=3)
+        o, lse = f(q, k, v, 0.37, causal)
+        assert np.allclose(o, v, atol=1e-14)
+        assert np.allclose(lse, 0.37 * (q @ k.T)[0], atol=1e-14)
+
+
+def pin_identical_keys(f):
+    """All keys equal: uniform weights over the visible keys.
+
+    O_i is the mean of the visible V rows (all of them, or rows 0..i when
+    causal) and LSE_i = scale q_i.k + ln(number of visible keys).
+    """
+    n, d = 11, 6
+    q, v = rnd(n, d, seed=4), rnd(n, d, seed=5)
+    krow = rnd(1, d, seed=6)
+    k = np.repeat(krow, n, axis=0)
+    for causal in (False, True):
+        o, lse = f(q, k, v, 0.5, causal)
+        cnt = np.arange(1, n + 1) if causal else np.full(n, n)
+        mean = (np.cumsum(v, axis=0) / cnt[:, None]) if causal else np.repeat(
+            v.mean(axis=0, keepdims=True), n, axis=0)
+        assert np.allclose(o, mean, atol=1e-13)
+        assert np.allclose(lse, 0.5 * (q @ krow.T)[:, 0] + np.log(cnt), atol=1e-13)
+
+
+def pin_zero_query(f):
+    """Q = 0: every visible score is 0, O = (prefix) mean of V, LSE = ln count."""
+    n, d = 9, 4
+    q = np.zeros((n, d))
+    k, v = rnd(n, d, seed=7), rnd(n, d, seed=8)
+    o, lse = f(q, k, v, 1.0, False)
+    assert np.allclose(o, np.repeat(v.mean(0, keepdims=True), n, 0), atol=1e-13)
+    assert np.allclose(lse, np.log(n), atol=1e-13)
+    o, lse = f(q, k, v, 1.0, True)
+    cnt = np.arange(1, n + 1)
+    assert np.allclose(o, np.cumsum(v, 0) / cnt[:, None], atol=1e-13)
+    assert np.allclose(lse, np.log(cnt), atol=1e-13)
+
+
+def pin_causal_row0(f):
+    """Causal: query 0 sees only key 0, so O_0 = V_0 and LSE_0 = scale q_0.k_0."""
+    n, d = 13, 5
+    q, k, v = rnd(n, d, seed=9), rnd(n, d, seed=10), rnd(n, d, seed=11)
+    o, lse = f(q, k, v, 0.3, True)
+    assert np.allclose(o[0], v[0], atol=1e-14)
+    assert np.isclose(lse[0], 0.3 * q[0] @ k[0], atol=1e-14)
+    # and the last query sees every key: same as the unmasked row
+    o2, lse2 = f(q, k, v, 0.3, False)
+    assert np.allclose(o[-1], o2[-1], atol=1e-13)
+    assert np.isclose(lse[-1], lse2[-1], atol=1e-13)
+
+
+def pin_torch_library(f):
+    """Special case evaluated by an independent library: torch fp64 softmax and
+    logsumexp of the materialised score matrix (the "standard attention" line
+    of the glossary page's sketch)."""
+    n, d = 37, 16
+    q, k, v = rnd(n, d, seed=12), rnd(n, d, seed=13), rnd(n, d, seed=14)
+    for causal in (False, True):
+        o, lse = f(q, k, v, 0.25, causal)
+        s = torch.from_numpy(q) @ torch.from_numpy(k).T * 0.25
+        if causal:
+            s = s.masked_fill(torch.triu(torch.ones(n, n, dtype=torch.bool), 1), float("-inf"))
+        o_t = torch.softmax(s, dim=-1) @ torch.from_numpy(v)
+        l_t = torch.logsumexp(s, dim=-1)
+        assert np.abs(o - o_t.numpy()).max() <= 1e-12
+        assert np.abs(lse - l_t.numpy()).max() <= 1e-12
+
+
+def pin_shift_invariance(f):
+    """K -> K + 1 u^T adds scale q_i.u to every score of row i: O is unchanged
+    and LSE_i shifts by exactly that constant (stable softmax, max subtraction)."""
+    n, d = 10, 7
+    q, k, v = rnd(n, d, seed=15), rnd(n, d, seed=16), rnd(n, d, seed=17)
+    u = rnd(1, d, seed=18)
+    for causal in (False, True):
+        o1, l1 = f(q, k, v, 0.4, causal)
+        o2, l2 = f(q, k + u, v, 0.4, causal)
+        assert np.allclose(o1, o2, atol=1e-12)
+        assert np.allclose(l2 - l1, 0.4 * (q @ u.T)[:, 0], atol=1e-12)
+
+
+def pin_linearity_in_v(f):
+    """O(Q, K, aV + 1 b^T) = a O + 1 b^T because each row of P sums to one."""
+    n, d = 12, 5
+    q, k, v = rnd(n, d, seed=19), rnd(n, d, seed=20), rnd(n, d, seed=21)
+    b = rnd(1, d, seed=22)
+    for causal in (False, True):
+        o1, _ = f(q, k, v, 0.6, causal)
+        o2, _ = f(q, k, -1.7 * v + b, 0.6, causal)
+        assert np.allclose(o2, -1.7 * o1 + b, atol=1e-12)
+
+
+def pin_permutations(f):
+    """Non-causal: permuting keys with their values leaves O and LSE unchanged;
+    permuting queries permutes the output rows."""
+    n, d = 15, 4
+    q, k, v = rnd(n, d, seed=23), rnd(n, d, seed=24), rnd(n, d, seed=25)
+    p = np.random.default_rng(26).permutation(n)
+    o1, l1 = f(q, k, v, 0.7, False)
+    o2, l2 = f(q, k[p], v[p], 0.7, False)
+    assert np.allclose(o1, o2, atol=1e-12) and np.allclose(l1, l2, atol=1e-12)
+    o3, l3 = f(q[p], k, v, 0.7, False)
+    assert np.allclose(o3, o1[p], atol=1e-12) and np.allclose(l3, l1[p], atol=1e-12)
+
+
+FWD_PINS = [pin_single_key, pin_identical_keys, pin_zero_query, pin_causal_row0,
+            pin_torch_library, pin_shift_invariance, pin_linearity_in_v, pin_permutations]
+
+
+@pytest.mark.parametrize("pin", FWD_PINS, ids=lambda p: p.__name__)
+def test_forward_pin(pin):
+    pin(head_forward)
+
+
+def test_rows_sum_to_one_and_mask_is_zero():
+    n, d = 20, 3
+    q, k = rnd(n, d, seed=27), rnd(n, d, seed=28)
+    for causal in (False, True):
+        p, _, _ = head_probabilities(q, k, 0.9, causal)
+        assert np.allclose(p.sum(1), 1.0, atol=1e-14)
+        if causal:
+            assert np.all(p[np.triu_indices(n, 1)] == 0.0)
+            assert np.all(p[np.tril_indices(n)] > 0.0)
+
+
+@pytest.mark.parametrize("block", [1, 3, 64, 256])
+@pytest.mark.parametrize("causal", [False, True])
+def test_blockwise_equals_full(block, causal):
+    """The pages: the blockwise online softmax is mathematically identical to
+    the full softmax.  In fp64 the two agree to rounding (ragged N = 300)."""
+    n, d = 300, 16
+    q, k, v = rnd(n, d, seed=29), rnd(n, d, seed=30), rnd(n, d, seed=31)
+    o, lse = head_forward(q, k, v, 0.25, causal)
+    ob, lb, tile = head_forward_blockwise(q, k, v, 0.25, causal, block)
+    assert np.abs(o - ob).max() <= 1e-12
+    assert np.abs(lse - lb).max() <= 1e-12
+    assert tile == (n, min(block, n))
+
+
+def test_glossary_worked_example():
+    """The glossary page's fp32 example: seed 0, n=4096, d=64, block 256.
+
+    The largest score tile is (4096, 256) = 1/16 of the full matrix, and the
+    fp32 blockwise output differs from exact attention by fp32 rounding only
+    (the page prints 4.3e-07)."""
+    with open(os.path.join(GOLDEN, "glossary_worked_example.json")) as fh:
+        g = json.load(fh)
+    gen = torch.Generator().manual_seed(g["seed"])
+    q, k, v = (t.numpy() for t in torch.randn((3, g["n"], g["d"]), generator=gen).unbind(0))
+    o64, _ = head_forward(q, k, v, g["scale"], g["causal"])
+    o32, _, tile = head_forward_blockwise(q, k, v, g["scale"], g["causal"], g["block"],
+                                          dtype=np.float32)
+    assert list(tile) == g["printed_largest_tile"]
+    assert tile[0] * tile[1] / (g["n"] * g["n"]) == g["printed_tile_fraction_of_full"]
+    err = float(np.abs(o32.astype(np.float64) - o64).max())
+    printed = g["printed_max_abs_diff_fp32"]
+    assert printed / 50 <= err <= printed * 5, err
+
+
+def test_lse_statistical_sanity():
+    """For N(0,1) keys, sum_j exp(s_j) ~ N exp(scale^2 |q|^2 / 2), so
+    LSE_i ~ ln N + |q_i|^2 / (2 d) at scale 1/sqrt(d).  Catches a wrong log
+    base or a missing scale."""
+    n, d = 4096, 128
+    q, k, v = rnd(n, d, seed=32), rnd(n, d, seed=33), rnd(n, d, seed=34)
+    _, lse = head_forward(q, k, v, d ** -0.5, False)
+    pred = np.log(n) + (q * q).sum(1) / (2 * d)
+    assert np.median(np.abs(lse - pred)) < 0.05
+
+
+# --------------------------------------------------------------------------
+# Backward pins
+# --------------------------------------------------------------------------
+
+def _loss(q, k, v, do, scale, causal):
+    o, _ = head_forward(q, k, v, scale, causal)
+    return float((o * do).sum())
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_finite_differences(causal):
+    """Brute force: central differences of L = sum(O * dO) on a tiny input."""
+    n, d = 6, 3
+    q, k, v, do = (rnd(n, d, seed=s) for s in (35, 36, 37, 38))
+    dq, dk, dv = head_backward(q, k, v, do, 0.8, causal)
+    h = 1e-6
+    for x, g in ((q, dq), (k, dk), (v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            keep = x[idx]
+            x[idx] = keep + h
+            lp = _loss(q, k, v, do, 0.8, causal)
+            x[idx] = keep - h
+            lm = _loss(q, k, v, do, 0.8, causal)
+            x[idx] = keep
+            num[idx] = (lp - lm) / (2 * h)
+        rel = np.abs(num - g).max() / max(np.abs(g).max(), 1e-30)
+        assert rel <= 1e-6, rel
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_torch_autograd(causal):
+    """Independent library: torch.autograd in fp64 through the materialised form."""
+    n, d = 33, 8
+    arrs = [rnd(n, d, seed=s) for s in (39, 40, 41, 42)]
+    dq, dk, dv = head_backward(*arrs, 0.35, causal)
+    q, k, v = (torch.tensor(a, requires_grad=True) for a in arrs[:3])
+    s = q @ k.T * 0.35
+    if causal:
+        s = s.masked_fill(torch.triu(torch.ones(n, n, dtype=torch.bool), 1), float("-inf"))
+    o = torch.softmax(s, -1) @ v
+    (o * torch.from_numpy(arrs[3])).sum().backward()
+    for mine, ref in ((dq, q.grad), (dk, k.grad), (dv, v.grad)):
+        assert np.abs(mine - ref.numpy()).max() <= 1e-10
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_invariants(causal):
+    """Rows of dS sum to 0 -> sum_j dK_j = 0; rows of P sum to 1 ->
+    sum_j dV_j = sum_i dO_i; Delta_i = dO_i . O_i."""
+    n, d = 25, 6
+    q, k, v, do = (rnd(n, d, seed=s) for s in (43, 44, 45, 46))
+    dq, dk, dv = head_backward(q, k, v, do, 0.45, causal)
+    assert np.allclose(dk.sum(0), 0.0, atol=1e-12)
+    assert np.allclose(dv.sum(0), do.sum(0), atol=1e-12)
+    p, _, _ = head_probabilities(q, k, 0.45, causal)
+    o, _ = head_forward(q, k, v, 0.45, causal)
+    dp = do @ v.T
+    assert np.allclose((p * dp).sum(1), (do * o).sum(1), atol=1e-12)
+
+
+def test_backward_zero_query_closed_form():
+    """Q = 0, non-causal: P = 1/N everywhere, so dV_j = (1/N) sum_i dO_i."""
+    n, d = 10, 4
+    q = np.zeros((n, d))
+    k, v, do = rnd(n, d, seed=47), rnd(n, d, seed=48), rnd(n, d, seed=49)
+    _, _, dv = head_backward(q, k, v, do, 1.0, False)
+    assert np.allclose(dv, np.repeat(do.mean(0, keepdims=True), n, 0), atol=1e-13)
+
+
+def test_batched_wrappers_and_rows():
+    """[B,N,H,d] wrappers place heads correctly; the row sampler matches."""
+    B, N, H, d = 2, 9, 3, 4
+    q, k, v, do = (rnd(B, N, H, d, seed=s) for s in (50, 51, 52, 53))
+    for causal in (False, True):
+        o, lse = forward(q, k, v, 0.5, causal)
+        for b in range(B):
+            for h in range(H):
+                oh, lh = head_forward(q[b, :, h], k[b, :, h], v[b, :, h], 0.5, causal)
+                assert np.array_equal(o[b, :, h], oh) and np.array_equal(lse[b, h], lh)
+        picks = [(0, 0, 0), (1, 2, 8), (1, 0, 4)]
+        ro, rl = forward_rows(q, k, v, 0.5, causal, picks)
+        for j, (b, h, i) in enumerate(picks):
+            assert np.allclose(ro[j], o[b, i, h], atol=1e-14)
+            assert np.isclose(rl[j], lse[b, h, i], atol=1e-14)
+        dq, dk, dv = backward(q, k, v, do, 0.5, causal, heads=[(1, 1)])
+        a, bb, c = head_backward(q[1, :, 1], k[1, :, 1], v[1, :, 1], do[1, :, 1], 0.5, causal)
+        assert np.array_equal(dq[1, :, 1], a) and np.array_equal(dk[1, :, 1], bb)
+        assert np.isnan(dv[0, 0, 0, 0])
+
+
+# --------------------------------------------------------------------------
+# Mutation tests: a plausible mistake planted in a copy of the oracle must
+# make at least one pin fail.
+# --------------------------------------------------------------------------
+
+def _mut_dropped_scale(q, k, v, scale, causal):
+    return head_forward(q, k, v, 1.0, causal)
+
+
+def _mut_swapped_kv(q, k, v, scale, causal):
+    return head_forward(q, v, k, scale, causal)
+
+
+def _mut_flipped_mask(q, k, v, scale, causal):
+    if not causal:
+        return head_forward(q, k, v, scale, causal)
+    o, lse = head_forward(q[::-1], k[::-1], v[::-1], scale, True)
+    return o[::-1], lse[::-1]
+
+
+def _mut_log2_lse(q, k, v, scale, causal):
+    o, lse = head_forward(q, k, v, scale, causal)
+    p, m, l = head_probabilities(q, k, scale, causal)
+    return o, m + np.log2(l)
+
+
+def _mut_no_max_in_lse(q, k, v, scale, causal):
+    p, m, l = head_probabilities(q, k, scale, causal)
+    return p @ v, np.log(l)
+
+
+def _mut_unnormalised(q, k, v, scale, causal):
+    p, m, l = head_probabilities(q, k, scale, causal)
+    return (p * l[:, None]) @ v, m + np.log(l)
+
+
+@pytest.mark.parametrize("mutant", [_mut_dropped_scale, _mut_swapped_kv, _mut_flipped_mask,
+                                    _mut_log2_lse, _mut_no_max_in_lse, _mut_unnormalised],
+                         ids=lambda m: m.__name__)
+def test_pins_catch_planted_mistakes(mutant):
+    failed = 0
+    for pin in FWD_PINS:
+        try:
+            pin(mutant)
+        except AssertionError:
+            failed += 1
+    assert failed >= 1
+
+
+def test_finite_differences_catch_backward_mistakes():
+    """A transposed operand in dK or a missing scale in dQ fails the brute-force pin."""
+    n, d = 5, 3
+    q, k, v, do = (rnd(n, d, seed=s) for s in (54, 55, 56, 57))
+    dq, dk, dv = head_backward(q, k, v, do, 0.8, False)
+    h = 1e-6
+    num = np.zeros_like(k)
+    for idx in np.ndindex(*k.shape):
+        keep = k[idx]
+        k[idx] = keep + h
+        lp = _loss(q, k, v, do, 0.8, False)
+        k[idx] = keep - h
+        lm = _loss(q, k, v, do, 0.8, False)
+        k[idx] = keep
+        num[idx] = (lp - lm) / (2 * h)
+    assert np.abs(num - dk).max() < 1e-6
+    p, _, _ = head_probabilities(q, k, 0.8, False)
+    dp = do @ v.T
+    ds = p * (dp - (p * dp).sum(1)[:, None])
+    wrong_dk = 0.8 * (ds @ q)          # dS instead of dS^T
+    assert np.abs(num - wrong_dk).max() > 1e-3
+    wrong_dq = ds @ k                  # scale dropped
+    assert np.abs(wrong_dq - dq).max() > 1e-3
