@@ -1,0 +1,135 @@
+"""Thin ctypes binding of libfa.so (C ABI in include/fa.h).
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, outputs are allocated with torch, and raw device pointers plus the
+current HIP stream are handed to the library.  Every arithmetic step runs in
+the library's HIP kernels; there is no fallback.  If the shared library is
+missing this module raises instead of computing anything.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfa.so")
+
+EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_bwd_workspace_size", "fa_bwd", "fa_strerror")
+
+FA_OK = 0
+FA_ERR_INVALID_ARG = -1
+FA_ERR_UNSUPPORTED = -2
+FA_ERR_MISALIGNED = -3
+FA_ERR_WORKSPACE = -4
+FA_ERR_LAUNCH = -5
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load libfa.so once and declare the C signatures; raises if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} not found: build it with `python -m exact_io_aware_55_amd.build` "
+            "(the attention kernels have no other implementation)")
+    lib = ctypes.CDLL(path)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
+    lib.fa_fwd.restype = i
+    lib.fa_fwd_f32.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
+    lib.fa_fwd_f32.restype = i
+    lib.fa_bwd_workspace_size.argtypes = [i, i, i, i]
+    lib.fa_bwd_workspace_size.restype = sz
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, sz, vp]
+    lib.fa_bwd.restype = i
+    lib.fa_strerror.argtypes = [i]
+    lib.fa_strerror.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def strerror(code: int) -> str:
+    return load().fa_strerror(code).decode()
+
+
+def _check(rc: int):
+    if rc != FA_OK:
+        raise RuntimeError(f"libfa error {rc}: {strerror(rc)}")
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _check_inputs(dtype, *ts):
+    shape = ts[0].shape
+    if len(shape) != 4:
+        raise ValueError("tensors must be [B, N, H, d]")
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must be on the GPU")
+        if t.dtype != dtype:
+            raise ValueError(f"expected {dtype}, got {t.dtype}")
+        if t.shape != shape:
+            raise ValueError("q, k, v (and o, dO) must have the same shape")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous [B, N, H, d]")
+    return shape
+
+
+def _scale(scale, d):
+    return float(d) ** -0.5 if scale is None else float(scale)
+
+
+def forward(q, k, v, causal=False, scale=None, out=None, lse=None):
+    """bf16 forward.  Returns (O [B,N,H,d] bf16, LSE [B,H,N] fp32)."""
+    lib = load()
+    B, N, H, d = _check_inputs(torch.bfloat16, q, k, v)
+    o = torch.empty_like(q) if out is None else out
+    lse_t = torch.empty((B, H, N), device=q.device, dtype=torch.float32) if lse is None else lse
+    _check(lib.fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), B, H, N, d,
+                      _scale(scale, d), int(bool(causal)), _stream()))
+    return o, lse_t
+
+
+def forward_f32(q, k, v, causal=False, scale=None, out=None, lse=None):
+    """fp32 forward.  Returns (O [B,N,H,d] fp32, LSE [B,H,N] fp32)."""
+    lib = load()
+    B, N, H, d = _check_inputs(torch.float32, q, k, v)
+    o = torch.empty_like(q) if out is None else out
+    lse_t = torch.empty((B, H, N), device=q.device, dtype=torch.float32) if lse is None else lse
+    _check(lib.fa_fwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), B, H, N, d,
+                          _scale(scale, d), int(bool(causal)), _stream()))
+    return o, lse_t
+
+
+def bwd_workspace_size(B, H, N, d) -> int:
+    return int(load().fa_bwd_workspace_size(B, H, N, d))
+
+
+def backward(q, k, v, o, do, lse, causal=False, scale=None, workspace=None, out=None):
+    """bf16 backward by recomputation.  Returns (dQ, dK, dV), bf16 [B,N,H,d]."""
+    lib = load()
+    B, N, H, d = _check_inputs(torch.bfloat16, q, k, v, o, do)
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous fp32 [B, H, N]")
+    need = bwd_workspace_size(B, H, N, d)
+    ws = torch.empty(need, device=q.device, dtype=torch.uint8) if workspace is None else workspace
+    if out is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    else:
+        dq, dk, dv = out
+    _check(lib.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk),
+                      _ptr(dv), B, H, N, d, _scale(scale, d), int(bool(causal)), _ptr(ws),
+                      ws.numel() * ws.element_size(), _stream()))
+    return dq, dk, dv

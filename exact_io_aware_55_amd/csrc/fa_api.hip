@@ -1,0 +1,100 @@
+// C ABI of the attention library (declared in include/fa.h).
+//
+// Every entry point validates its arguments on the host before any HIP call,
+// so invalid calls return an error code without touching device state.  The
+// library never allocates, frees or synchronises; launches go to the caller's
+// stream.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/fa.h"
+#include "fa_launch.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+int check_shape(int B, int H, int N, int d, float scale) {
+    if (B < 1 || H < 1 || N < 1) return FA_ERR_INVALID_ARG;
+    if (!isfinite(scale)) return FA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if ((long long)N * H * d >= (1LL << 31)) return FA_ERR_UNSUPPORTED;
+    // grid size: B * H * ceil(N / 64) workgroups must fit a 32-bit grid
+    if ((long long)B * H * ((N + 63) / 64) >= (1LL << 31)) return FA_ERR_UNSUPPORTED;
+    return FA_OK;
+}
+
+int fwd_common(const void* q, const void* k, const void* v, const void* o, const void* lse, int B,
+               int H, int N, int d, float scale) {
+    if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+    const int rc = check_shape(B, H, N, d, scale);
+    if (rc != FA_OK) return rc;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+        return FA_ERR_MISALIGNED;
+    return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+           int d, float scale, int causal, hipStream_t stream) {
+    const int rc = fwd_common(q, k, v, o, lse, B, H, N, d, scale);
+    if (rc != FA_OK) return rc;
+    if (fa::launch_fwd_bf16(q, k, v, o, lse, B, H, N, d, scale, causal != 0, stream) != hipSuccess)
+        return FA_ERR_LAUNCH;
+    return FA_OK;
+}
+
+int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H,
+               int N, int d, float scale, int causal, hipStream_t stream) {
+    const int rc = fwd_common(q, k, v, o, lse, B, H, N, d, scale);
+    if (rc != FA_OK) return rc;
+    if (fa::launch_fwd_f32(q, k, v, o, lse, B, H, N, d, scale, causal != 0, stream) != hipSuccess)
+        return FA_ERR_LAUNCH;
+    return FA_OK;
+}
+
+size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
+    if (check_shape(B, H, N, d, 1.0f) != FA_OK) return 0;
+    const size_t rows = (size_t)B * H * N;
+    return align256(rows * sizeof(float)) + align256(rows * (size_t)d * sizeof(float));
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
+           int causal, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
+    const int rc = check_shape(B, H, N, d, scale);
+    if (rc != FA_OK) return rc;
+    const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return FA_ERR_MISALIGNED;
+    const size_t need = fa_bwd_workspace_size(B, H, N, d);
+    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) || workspace_bytes < need)
+        return FA_ERR_WORKSPACE;
+    float* delta = static_cast<float*>(workspace);
+    float* dq_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                             align256((size_t)B * H * N * sizeof(float)));
+    if (fa::launch_bwd_bf16(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal != 0, delta,
+                            dq_acc, stream) != hipSuccess)
+        return FA_ERR_LAUNCH;
+    return FA_OK;
+}
+
+const char* fa_strerror(int code) {
+    switch (code) {
+        case FA_OK: return "success";
+        case FA_ERR_INVALID_ARG: return "invalid argument (null pointer, B/H/N < 1 or non-finite scale)";
+        case FA_ERR_UNSUPPORTED: return "unsupported shape (d must be 64 or 128, N*H*d < 2^31)";
+        case FA_ERR_MISALIGNED: return "pointer not 16-byte aligned";
+        case FA_ERR_WORKSPACE: return "workspace null, not 256-byte aligned or smaller than fa_bwd_workspace_size()";
+        case FA_ERR_LAUNCH: return "kernel launch failed";
+        default: return "unknown error code";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,70 @@
+// Shared device helpers for the gfx950 attention kernels: vector types, the
+// bf16 MFMA wrapper, global/LDS vector access and the LDS layout functions.
+//
+// MFMA lane layout used throughout (v_mfma_f32_32x32x16_bf16, 64 lanes):
+//   A (32 x 16):  lane l holds row (l & 31), eight k-slots 8*(l >> 5) + e
+//   B (16 x 32):  lane l holds column (l & 31), eight k-slots 8*(l >> 5) + e
+//   C (32 x 32):  lane l holds column (l & 31); register r holds row
+//                 8*(r >> 2) + 4*(l >> 5) + (r & 3)
+// A contraction only needs A and B to agree on which data sits in which
+// k-slot, so the kernels are free to place keys (or queries) in k-slots in
+// any order, as long as both operands use the same order.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ u32x4 ld_global16(const void* p) {
+    return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void st_lds16(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
+__device__ __forceinline__ void st_lds8(void* p, const u32x2& v) { *reinterpret_cast<u32x2*>(p) = v; }
+__device__ __forceinline__ void st_lds4(void* p, uint32_t v) { *reinterpret_cast<uint32_t*>(p) = v; }
+__device__ __forceinline__ bf16x8 ld_lds_bf16x8(const void* p) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Packs two floats into one dword of two bf16 (round to nearest even).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    bf16x2 v;
+    v[0] = (__bf16)lo;
+    v[1] = (__bf16)hi;
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// Key (or query) order inside one 16-wide k-chunk.  The C layout gives a lane
+// the rows 8g + 4h + t (g, t in 0..3, h = lane half); taking registers
+// 8c..8c+7 of a C tile as the B operand of the next product places row
+// 16c' + 8a + 4h + t (a = e >> 2, t = e & 3) in k-slot 8h + 4a + t.  The
+// matching A operand must therefore store index 8a + 4b + t of a chunk at
+// position 8b + 4a + t: bits 2 and 3 of the index swap places.
+__device__ __forceinline__ int kslot_pos(int idx) {
+    return (idx & ~15) | (((idx >> 2) & 1) << 3) | (((idx >> 3) & 1) << 2) | (idx & 3);
+}
+
+// XOR swizzle of 16-byte chunks within a 128-byte LDS row (8 chunks): keeps
+// 16-lane 128-bit reads of one logical chunk from consecutive rows on
+// distinct banks, for both 32- and 64-bank LDS organisations.
+__device__ __forceinline__ int swz8(int row) { return (row ^ (row >> 3)) & 7; }
+
+}  // namespace fa

@@ -1,0 +1,101 @@
+/*
+ * fa.h -- exact attention (FlashAttention) forward and backward on AMD gfx950.
+ *
+ * What is computed.  For every batch b and head h, with X_bh the N x d matrix
+ * X[b, :, h, :]:
+ *
+ *     S = scale * Q K^T                       (optionally causal: key j is
+ *                                              visible to query i iff j <= i)
+ *     P = softmax over each row of S          (online, block by block)
+ *     O = P V,   LSE_i = log(sum_j exp(S_ij))  (natural log)
+ *
+ * The forward streams K/V blocks through on-chip memory and keeps a running
+ * row maximum and sum, rescaling the partial output when the maximum grows;
+ * only O and one statistic per row go back to memory.  (Explainer page
+ * "Flash Attention", sections "Tiling" and "Speicherbedarf und
+ * Laufzeitverhalten"; glossary page "Flash Attention", section "How it
+ * works".)  The per-row statistic is exported as LSE = m + ln(l), which
+ * carries the page's "maximum and sum per row".
+ *
+ * The backward recomputes P = exp(S - LSE) tile by tile instead of storing
+ * the N x N matrix (explainer page, "Recomputation beim Rueckwaertsdurchlauf";
+ * glossary page, "How it works") and returns the gradients of
+ * L = sum(O * dO):
+ *
+ *     dV = P^T dO,  dP = dO V^T,  D_i = sum_k dO_ik O_ik,
+ *     dS = P * (dP - D),  dQ = scale dS K,  dK = scale dS^T Q.
+ *
+ * Layouts.  q, k, v, o, dout, dq, dk, dv: [B, N, H, d] contiguous, row-major
+ * (d fastest).  lse: [B, H, N] contiguous fp32.  bf16 entry points take
+ * bfloat16 tensors; arithmetic is fp32 (P and dS are rounded to bf16 before
+ * their matrix products, outputs are rounded to bf16 once).  The fp32 entry
+ * point takes and returns fp32 and computes in fp32 throughout.
+ *
+ * Supported: d in {64, 128}; B, H, N >= 1; N * H * d < 2^31; any finite
+ * scale.  Pointers must be device pointers aligned to 16 bytes.
+ *
+ * Ownership and streams.  The caller owns every buffer (including the
+ * backward workspace).  The library never allocates, frees or synchronises:
+ * each call validates its arguments on the host, enqueues kernels on
+ * `stream` and returns.  Outputs are valid once the stream reaches that point.
+ * O and LSE of fa_fwd are the inputs fa_bwd expects.  The forward never reads
+ * `o` or `lse`.  Calls are thread-safe.
+ *
+ * Errors.  0 on success, otherwise a negative FA_ERR_* code.  All argument
+ * checks happen before any HIP call, so an invalid call touches no device
+ * state.  FA_ERR_LAUNCH reports a failed kernel launch; faults during
+ * execution surface on the stream as usual.  NaN or Inf inputs propagate.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* hipStream_t;
+
+enum {
+    FA_OK = 0,
+    FA_ERR_INVALID_ARG = -1, /* null pointer, B/H/N < 1, non-finite scale */
+    FA_ERR_UNSUPPORTED = -2, /* d not in {64, 128}, or N*H*d >= 2^31     */
+    FA_ERR_MISALIGNED = -3,  /* a pointer not 16-byte aligned             */
+    FA_ERR_WORKSPACE = -4,   /* workspace null, misaligned or too small   */
+    FA_ERR_LAUNCH = -5       /* the HIP runtime rejected a kernel launch  */
+};
+
+/* bf16 forward.  q, k, v: bf16 [B,N,H,d] inputs; o: bf16 [B,N,H,d] output;
+ * lse: fp32 [B,H,N] output.  Tiled online softmax over K/V blocks. */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
+
+/* fp32 forward: same contract with fp32 tensors and fp32 arithmetic
+ * (K/V blocks of 256 rows for d = 64, 128 rows for d = 128). */
+int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+               int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
+
+/* Bytes of device workspace fa_bwd needs for this shape (0 if the shape is
+ * invalid).  It holds the fp32 row statistic D [B,H,N] and an fp32 dQ
+ * accumulator [B,N,H,d], each 256-byte aligned. */
+size_t fa_bwd_workspace_size(int B, int H, int N, int d);
+
+/* bf16 backward with recomputation.  q, k, v, o, dout: bf16 [B,N,H,d]
+ * inputs (o and lse as produced by fa_fwd with the same scale and causal);
+ * dq, dk, dv: bf16 [B,N,H,d] outputs.  workspace: device memory of at least
+ * fa_bwd_workspace_size(B,H,N,d) bytes, 256-byte aligned, owned by the
+ * caller; its contents on entry are ignored and on exit are scratch. */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv,
+           int B, int H, int N, int d, float scale, int causal,
+           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Human-readable text for a return code (static storage). */
+const char* fa_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

@@ -1,0 +1,110 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry point
+declared in include/fa.h, and rejects invalid arguments before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from exact_io_aware_55_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+FAKE = 0x10000  # a non-null, 256-byte aligned address; never dereferenced here
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return binding.load()
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(binding.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_strerror(lib):
+    for code in (0, -1, -2, -3, -4, -5):
+        assert len(binding.strerror(code)) > 3
+    assert "unknown" in binding.strerror(-99)
+
+
+def _fwd(lib, fn="fa_fwd", ptrs=(FAKE,) * 5, B=1, H=1, N=8, d=64, scale=0.125, causal=0):
+    f = getattr(lib, fn)
+    return f(*[ctypes.c_void_p(p) if p else None for p in ptrs], B, H, N, d, scale, causal, None)
+
+
+@pytest.mark.parametrize("fn", ["fa_fwd", "fa_fwd_f32"])
+def test_forward_argument_errors(lib, fn):
+    for i in range(5):
+        ptrs = [FAKE] * 5
+        ptrs[i] = 0
+        assert _fwd(lib, fn, ptrs) == binding.FA_ERR_INVALID_ARG
+    assert _fwd(lib, fn, B=0) == binding.FA_ERR_INVALID_ARG
+    assert _fwd(lib, fn, H=-1) == binding.FA_ERR_INVALID_ARG
+    assert _fwd(lib, fn, N=0) == binding.FA_ERR_INVALID_ARG
+    assert _fwd(lib, fn, scale=float("nan")) == binding.FA_ERR_INVALID_ARG
+    assert _fwd(lib, fn, scale=float("inf")) == binding.FA_ERR_INVALID_ARG
+    for d in (0, 32, 96, 256):
+        assert _fwd(lib, fn, d=d) == binding.FA_ERR_UNSUPPORTED
+    assert _fwd(lib, fn, N=1 << 20, H=64, d=128) == binding.FA_ERR_UNSUPPORTED
+    for i in range(5):
+        ptrs = [FAKE] * 5
+        ptrs[i] = FAKE + 8
+        assert _fwd(lib, fn, ptrs) == binding.FA_ERR_MISALIGNED
+
+
+def test_workspace_size(lib):
+    B, H, N, d = 4, 16, 4096, 64
+    rows = B * H * N
+    want = ((rows * 4 + 255) // 256) * 256 + ((rows * d * 4 + 255) // 256) * 256
+    assert lib.fa_bwd_workspace_size(B, H, N, d) == want
+    assert lib.fa_bwd_workspace_size(1, 1, 7, 128) == 256 + ((7 * 128 * 4 + 255) // 256) * 256
+    assert lib.fa_bwd_workspace_size(0, 1, 8, 64) == 0
+    assert lib.fa_bwd_workspace_size(1, 1, 8, 80) == 0
+
+
+def _bwd(lib, ptrs=(FAKE,) * 9, B=1, H=1, N=8, d=64, scale=0.125, ws=FAKE, ws_bytes=1 << 20):
+    args = [ctypes.c_void_p(p) if p else None for p in ptrs]
+    return lib.fa_bwd(*args, B, H, N, d, scale, 1, ctypes.c_void_p(ws) if ws else None, ws_bytes,
+                      None)
+
+
+def test_backward_argument_errors(lib):
+    for i in range(9):
+        ptrs = [FAKE] * 9
+        ptrs[i] = 0
+        assert _bwd(lib, ptrs) == binding.FA_ERR_INVALID_ARG
+    assert _bwd(lib, B=0) == binding.FA_ERR_INVALID_ARG
+    assert _bwd(lib, scale=float("nan")) == binding.FA_ERR_INVALID_ARG
+    assert _bwd(lib, d=100) == binding.FA_ERR_UNSUPPORTED
+    for i in range(9):
+        ptrs = [FAKE] * 9
+        ptrs[i] = FAKE + 4
+        assert _bwd(lib, ptrs) == binding.FA_ERR_MISALIGNED
+    need = lib.fa_bwd_workspace_size(1, 1, 8, 64)
+    assert _bwd(lib, ws=0) == binding.FA_ERR_WORKSPACE
+    assert _bwd(lib, ws=FAKE + 16) == binding.FA_ERR_WORKSPACE
+    assert _bwd(lib, ws_bytes=need - 1) == binding.FA_ERR_WORKSPACE
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    saved = binding._lib
+    binding._lib = None
+    try:
+        with pytest.raises(RuntimeError, match="not found"):
+            binding.load(str(tmp_path / "nope.so"))
+    finally:
+        binding._lib = saved
