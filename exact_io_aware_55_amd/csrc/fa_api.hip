@@ -7,6 +7,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <initializer_list>
+
 #include "../../include/fa.h"
 #include "fa_launch.h"
 
@@ -64,25 +66,82 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
     return align256(rows * sizeof(float)) + align256(rows * (size_t)d * sizeof(float));
 }
 
-int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
-           const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
-           int causal, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-    if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
-    const int rc = check_shape(B, H, N, d, scale);
-    if (rc != FA_OK) return rc;
-    const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv};
-    for (const void* p : ptrs)
-        if (!aligned16(p)) return FA_ERR_MISALIGNED;
+namespace {
+struct Workspace {
+    float* delta;
+    float* dq_acc;
+};
+
+int check_workspace(void* workspace, size_t workspace_bytes, int B, int H, int N, int d, Workspace* ws) {
     const size_t need = fa_bwd_workspace_size(B, H, N, d);
     if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) || workspace_bytes < need)
         return FA_ERR_WORKSPACE;
-    float* delta = static_cast<float*>(workspace);
-    float* dq_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                             align256((size_t)B * H * N * sizeof(float)));
-    if (fa::launch_bwd_bf16(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal != 0, delta,
-                            dq_acc, stream) != hipSuccess)
+    ws->delta = static_cast<float*>(workspace);
+    ws->dq_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                          align256((size_t)B * H * N * sizeof(float)));
+    return FA_OK;
+}
+
+int all_aligned(std::initializer_list<const void*> ptrs) {
+    for (const void* p : ptrs)
+        if (!p) return FA_ERR_INVALID_ARG;
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return FA_ERR_MISALIGNED;
+    return FA_OK;
+}
+}  // namespace
+
+int fa_bwd_preprocess(const void* o, const void* dout, int B, int H, int N, int d, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+    int rc = all_aligned({o, dout});
+    if (rc != FA_OK) return rc;
+    if ((rc = check_shape(B, H, N, d, 1.0f)) != FA_OK) return rc;
+    Workspace ws;
+    if ((rc = check_workspace(workspace, workspace_bytes, B, H, N, d, &ws)) != FA_OK) return rc;
+    if (fa::launch_bwd_preprocess(o, dout, B, H, N, d, ws.delta, ws.dq_acc, stream) != hipSuccess)
         return FA_ERR_LAUNCH;
     return FA_OK;
+}
+
+int fa_bwd_kv_blocks(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                     void* dk, void* dv, int B, int H, int N, int d, float scale, int causal,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    int rc = all_aligned({q, k, v, dout, lse, dk, dv});
+    if (rc != FA_OK) return rc;
+    if ((rc = check_shape(B, H, N, d, scale)) != FA_OK) return rc;
+    Workspace ws;
+    if ((rc = check_workspace(workspace, workspace_bytes, B, H, N, d, &ws)) != FA_OK) return rc;
+    if (fa::launch_bwd_kv_blocks(q, k, v, dout, lse, dk, dv, B, H, N, d, scale, causal != 0, ws.delta,
+                                 ws.dq_acc, stream) != hipSuccess)
+        return FA_ERR_LAUNCH;
+    return FA_OK;
+}
+
+int fa_bwd_dq_convert(void* dq, int B, int H, int N, int d, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+    int rc = all_aligned({dq});
+    if (rc != FA_OK) return rc;
+    if ((rc = check_shape(B, H, N, d, 1.0f)) != FA_OK) return rc;
+    Workspace ws;
+    if ((rc = check_workspace(workspace, workspace_bytes, B, H, N, d, &ws)) != FA_OK) return rc;
+    if (fa::launch_bwd_dq_convert(dq, B, H, N, d, ws.dq_acc, stream) != hipSuccess) return FA_ERR_LAUNCH;
+    return FA_OK;
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
+           int causal, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    // validate everything before the first launch
+    int rc = all_aligned({q, k, v, o, dout, lse, dq, dk, dv});
+    if (rc != FA_OK) return rc;
+    if ((rc = check_shape(B, H, N, d, scale)) != FA_OK) return rc;
+    Workspace ws;
+    if ((rc = check_workspace(workspace, workspace_bytes, B, H, N, d, &ws)) != FA_OK) return rc;
+    if ((rc = fa_bwd_preprocess(o, dout, B, H, N, d, workspace, workspace_bytes, stream)) != FA_OK) return rc;
+    if ((rc = fa_bwd_kv_blocks(q, k, v, dout, lse, dk, dv, B, H, N, d, scale, causal, workspace,
+                               workspace_bytes, stream)) != FA_OK)
+        return rc;
+    return fa_bwd_dq_convert(dq, B, H, N, d, workspace, workspace_bytes, stream);
 }
 
 const char* fa_strerror(int code) {

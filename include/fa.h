@@ -91,6 +91,29 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
            int B, int H, int N, int d, float scale, int causal,
            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* The three steps fa_bwd runs, exported separately so a caller can schedule
+ * or time them individually.  All share fa_bwd's workspace layout and must
+ * run in this order on one stream for one backward:
+ *   fa_bwd_preprocess: D_i = sum_k dO_ik O_ik (fp32, into the workspace) and
+ *                      zero the fp32 dQ accumulator.  The row statistic D is
+ *                      the softmax-Jacobian term of the backward (not on the
+ *                      pages, which only require recomputation).
+ *   fa_bwd_kv_blocks:  for each block of keys, walk the query blocks that can
+ *                      see them, recompute P = exp(scale QK^T - LSE), and form
+ *                      dV, dK (written as bf16) and the block's contribution to
+ *                      dQ (added to the fp32 accumulator with float atomics,
+ *                      so dQ is not bitwise repeatable; dK and dV are).
+ *   fa_bwd_dq_convert: dQ = bf16(accumulator).
+ * Arguments have the meaning and layout given for fa_bwd. */
+int fa_bwd_preprocess(const void* o, const void* dout, int B, int H, int N, int d,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+int fa_bwd_kv_blocks(const void* q, const void* k, const void* v, const void* dout,
+                     const float* lse, void* dk, void* dv, int B, int H, int N, int d,
+                     float scale, int causal, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream);
+int fa_bwd_dq_convert(void* dq, int B, int H, int N, int d, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream);
+
 /* Human-readable text for a return code (static storage). */
 const char* fa_strerror(int code);
 

@@ -37,3 +37,52 @@ def assert_f32_close(got, ref, what=""):
     ma = max_abs(got, ref)
     assert ma <= F32_MAX_ABS, f"{what}: max_abs={ma:.3e}"
     return ma
+
+
+# --------------------------------------------------------------------------
+# Element-wise a-priori error bound of the bf16 backward arithmetic.
+#
+# The bf16 path rounds (round to nearest even, unit roundoff u = 2^-8) the
+# forward's O, the probabilities P before dV = P^T dO, dS before dK and dQ,
+# and each output once; everything else accumulates in fp32.  First-order
+# propagation of those roundings gives, per element:
+#   |dO_err| row statistic:  dD_i  <= sum_k |dO_ik| (u|O_ik| + u (P|V|)_ik)
+#   dS error:                edS_ij <= P_ij dD_i + u |dS_ij|
+#   dV: u (P^T|dO|) + u|dV|
+#   dK: |scale| (edS^T |Q|) + u|dK|
+#   dQ: |scale| (edS |K|) + u|dQ|
+# plus an fp32 accumulation allowance.  A correct kernel stays inside this
+# bound at any size and scale, including degenerate shapes where the fixed
+# max-abs / relative-L2 tolerances are tighter than the bf16 arithmetic allows.
+# --------------------------------------------------------------------------
+U_BF16 = 2.0 ** -8
+F32_ALLOW = 1e-5
+
+
+def bwd_error_bounds(q, k, v, do, scale, causal):
+    """Return (bound_dQ, bound_dK, bound_dV) for one head (fp64 inputs)."""
+    import oracle
+
+    p, _, _ = oracle.head_probabilities(q, k, scale, causal)
+    o = p @ v
+    dp = do @ v.T
+    delta = (p * dp).sum(1)
+    ds = p * (dp - delta[:, None])
+    dq, dk, dv = oracle.head_backward(q, k, v, do, scale, causal)
+    u = U_BF16
+    o_err = u * np.abs(o) + u * (p @ np.abs(v))
+    d_err = (np.abs(do) * o_err).sum(1)
+    eds = p * d_err[:, None] + u * np.abs(ds)
+    s = abs(scale)
+    b_dv = u * (p.T @ np.abs(do)) + u * np.abs(dv) + F32_ALLOW * (p.T @ np.abs(do))
+    b_dk = s * (eds.T @ np.abs(q)) + u * np.abs(dk) + F32_ALLOW * s * (np.abs(ds).T @ np.abs(q))
+    b_dq = s * (eds @ np.abs(k)) + u * np.abs(dq) + F32_ALLOW * s * (np.abs(ds) @ np.abs(k))
+    return b_dq, b_dk, b_dv
+
+
+def assert_within_bound(got, ref, bound, what="", slack=1.25):
+    err = np.abs(np.asarray(got, np.float64) - ref)
+    lim = slack * bound + 1e-6
+    bad = err > lim
+    assert not bad.any(), (f"{what}: {int(bad.sum())} elements outside the bf16 rounding bound; "
+                           f"worst excess {float((err - lim).max()):.3e}")

@@ -100,6 +100,26 @@ def test_backward_argument_errors(lib):
     assert _bwd(lib, ws_bytes=need - 1) == binding.FA_ERR_WORKSPACE
 
 
+def test_backward_step_argument_errors(lib):
+    V = ctypes.c_void_p
+    f = lib.fa_bwd_preprocess
+    assert f(None, V(FAKE), 1, 1, 8, 64, V(FAKE), 1 << 20, None) == binding.FA_ERR_INVALID_ARG
+    assert f(V(FAKE + 2), V(FAKE), 1, 1, 8, 64, V(FAKE), 1 << 20, None) == binding.FA_ERR_MISALIGNED
+    assert f(V(FAKE), V(FAKE), 1, 1, 8, 96, V(FAKE), 1 << 20, None) == binding.FA_ERR_UNSUPPORTED
+    assert f(V(FAKE), V(FAKE), 1, 1, 8, 64, V(FAKE), 16, None) == binding.FA_ERR_WORKSPACE
+    g = lib.fa_bwd_kv_blocks
+    ok = [V(FAKE)] * 7
+    assert g(*ok, 1, 1, 8, 64, float("inf"), 0, V(FAKE), 1 << 20, None) == binding.FA_ERR_INVALID_ARG
+    assert g(*ok, 1, 0, 8, 64, 0.1, 0, V(FAKE), 1 << 20, None) == binding.FA_ERR_INVALID_ARG
+    assert g(*ok, 1, 1, 8, 64, 0.1, 0, None, 1 << 20, None) == binding.FA_ERR_WORKSPACE
+    bad = list(ok)
+    bad[4] = V(FAKE + 8)
+    assert g(*bad, 1, 1, 8, 64, 0.1, 0, V(FAKE), 1 << 20, None) == binding.FA_ERR_MISALIGNED
+    h = lib.fa_bwd_dq_convert
+    assert h(None, 1, 1, 8, 64, V(FAKE), 1 << 20, None) == binding.FA_ERR_INVALID_ARG
+    assert h(V(FAKE), 1, 1, 8, 64, V(FAKE + 128), 1 << 20, None) == binding.FA_ERR_WORKSPACE
+
+
 def test_missing_library_fails_loudly(tmp_path):
     saved = binding._lib
     binding._lib = None

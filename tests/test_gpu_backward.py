@@ -1,0 +1,134 @@
+"""GPU parity of fa_bwd (recomputation backward) against the fp64 oracle.
+
+The backward takes O and LSE from fa_fwd (its documented contract) and is
+compared with the oracle's gradients of L = sum(O * dO), computed from Q, K, V
+and dO by the definition."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_io_aware_55_amd import inputs, workloads
+from parity import assert_bf16_close, assert_within_bound, bwd_error_bounds
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def run(lib, x, causal, scale=None):
+    q, k, v, do = (x[n].to(DEV) for n in ("q", "k", "v", "do"))
+    o, lse = lib.forward(q, k, v, causal=causal, scale=scale)
+    dq, dk, dv = lib.backward(q, k, v, o, do, lse, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+def compare_heads(x, grads, scale, causal, heads, what, strict=True):
+    """Every head: inside the element-wise bf16 rounding bound.  strict: also the
+    fixed tolerances (max-abs <= 2e-2, relative L2 <= 5e-3) that the method's
+    workloads are held to."""
+    qn, kn, vn, dn = (inputs.to_f64(x[n]) for n in ("q", "k", "v", "do"))
+    for b, h in heads:
+        args = (qn[b, :, h], kn[b, :, h], vn[b, :, h], dn[b, :, h], scale, causal)
+        ref = oracle.head_backward(*args)
+        bounds = bwd_error_bounds(*args)
+        for name, g, r, bd in zip(("dQ", "dK", "dV"), grads, ref, bounds):
+            got = inputs.to_f64(g[b, :, h])
+            assert_within_bound(got, r, bd, f"{what} head {(b, h)} {name}")
+            if strict:
+                assert_bf16_close(got, r, f"{what} head {(b, h)} {name}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 2, 7, 31, 64, 65, 127, 128, 129, 200, 513])
+def test_bwd_small_shapes(gpu_lib, N, d, causal):
+    print(f"\n[bwd] N={N} d={d} causal={causal}", flush=True)
+    B, H = 2, 2
+    x = inputs.make_qkv(B, N, H, d, torch.bfloat16, seed=300 + N, with_do=True)
+    grads = run(gpu_lib, x, causal)
+    # below ~128 keys a row's few probabilities are large and their bf16
+    # rounding dominates; those shapes are held to the rounding bound only
+    compare_heads(x, grads, d ** -0.5, causal, [(b, h) for b in range(B) for h in range(H)],
+                  f"N{N} d{d} causal={causal}", strict=N >= 128)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_scale_edge_cases(gpu_lib, causal):
+    for sc in (0.0, -0.3):
+        print(f"\n[bwd] scale={sc} causal={causal}", flush=True)
+        x = inputs.make_qkv(1, 150, 2, 64, torch.bfloat16, seed=17, with_do=True)
+        grads = run(gpu_lib, x, causal, scale=sc)
+        compare_heads(x, grads, sc, causal, [(0, 0), (0, 1)], f"scale={sc}", strict=False)
+
+
+def full_size_properties(x, grads):
+    """Invariants at any size: sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i per head."""
+    dq, dk, dv = grads
+    for t in grads:
+        assert torch.isfinite(t.float()).all()
+    dk_sum = dk.double().sum(1)                          # [B, H, d]
+    dk_scale = dk.double().abs().sum(1)
+    assert (dk_sum.abs() <= 2e-2 * dk_scale + 1e-3).all()
+    dv_sum = dv.double().sum(1).cpu()
+    do_sum = x["do"].double().sum(1)
+    assert torch.allclose(dv_sum, do_sum, rtol=2e-2, atol=0.5)
+
+
+def test_bwd_causal_n4096_d64(gpu_lib):
+    w = workloads.BWD_CAUSAL_D64
+    print(f"\n[bwd] {w.name}", flush=True)
+    x = inputs.make_qkv(w.B, w.N, w.H, w.d, torch.bfloat16, seed=w.seed, with_do=True)
+    grads = run(gpu_lib, x, w.causal)
+    compare_heads(x, grads, w.scale, w.causal, [(0, 0), (w.B - 1, w.H - 1), (1, 7)], w.name)
+    full_size_properties(x, grads)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [512, 1024, 2048, 4096, 8192])
+def test_bwd_sweep(gpu_lib, N, d):
+    """Fixed 16384 tokens per batch, H=16, non-causal (one head checked fully)."""
+    w = next(s for s in workloads.sweep(d) if s.N == N)
+    print(f"\n[bwd] {w.name}", flush=True)
+    x = inputs.make_qkv(w.B, w.N, w.H, w.d, torch.bfloat16, seed=w.seed, with_do=True)
+    grads = run(gpu_lib, x, w.causal)
+    compare_heads(x, grads, w.scale, w.causal, [(w.B - 1, w.H // 2)], w.name)
+    full_size_properties(x, grads)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_bwd_sweep_n16384(gpu_lib, d):
+    """Longest sweep point: one head against the oracle (2 GiB fp64 per N x N)."""
+    w = next(s for s in workloads.sweep(d) if s.N == 16384)
+    print(f"\n[bwd] {w.name}", flush=True)
+    x = inputs.make_qkv(w.B, w.N, w.H, w.d, torch.bfloat16, seed=w.seed, with_do=True)
+    grads = run(gpu_lib, x, w.causal)
+    compare_heads(x, grads, w.scale, w.causal, [(0, 3)], w.name)
+    full_size_properties(x, grads)
+
+
+def test_bwd_dk_dv_deterministic(gpu_lib):
+    """dK and dV have no atomics: bitwise repeatable.  dQ is summed with float
+    atomics, so only its tolerance is checked by the parity tests."""
+    x = inputs.make_qkv(2, 700, 3, 128, torch.bfloat16, seed=21, with_do=True)
+    g1 = run(gpu_lib, x, True)
+    g2 = run(gpu_lib, x, True)
+    assert torch.equal(g1[1], g2[1]) and torch.equal(g1[2], g2[2])
+
+
+def test_bwd_workspace_is_not_read(gpu_lib):
+    """fa_bwd ignores whatever the workspace held before the call."""
+    x = inputs.make_qkv(1, 300, 2, 64, torch.bfloat16, seed=22, with_do=True)
+    q, k, v, do = (x[n].to(DEV) for n in ("q", "k", "v", "do"))
+    o, lse = gpu_lib.forward(q, k, v, causal=True)
+    need = gpu_lib.bwd_workspace_size(1, 2, 300, 64)
+    ws = torch.full((need,), 0x7f, dtype=torch.uint8, device=DEV)   # garbage floats
+    g1 = gpu_lib.backward(q, k, v, o, do, lse, causal=True, workspace=ws)
+    ws.fill_(0xff)                                                  # NaN patterns
+    g2 = gpu_lib.backward(q, k, v, o, do, lse, causal=True, workspace=ws)
+    torch.cuda.synchronize()
+    for a, b in zip(g1, g2):
+        assert torch.isfinite(a.float()).all()
+        assert torch.allclose(a.float(), b.float(), atol=1e-2)
