@@ -1,0 +1,277 @@
+"""Benchmark of the exact-attention hot path on one MI355X.
+
+One step = one pass of the whole hot path over one batch: the forward
+(fa_fwd: tiled online softmax, writes O and LSE) followed by the backward by
+recomputation (fa_bwd_preprocess, fa_bwd_kv_blocks, fa_bwd_dq_convert).
+Default workload: B=4, H=32, N=4096, d=128, bf16, non-causal, scale 1/sqrt(d),
+seeded N(0,1) inputs resident in HBM before timing starts.
+
+Counted work: 4 N^2 d flops per head forward, 2.5x that backward, halved when
+causal.  Peak: MI355X dense bf16 MFMA = 256 CU x 4096 flop/clk x 2.4 GHz =
+2516.6 TFLOP/s.
+
+Prints one JSON line (rank 0).  Beside the kernel it reports a naive
+materialised-attention baseline on the same GPU (torch bf16 bmm + softmax,
+scores and probabilities written to HBM, explicit backward) and the fp64 CPU
+oracle timed on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PEAK_BF16_TFLOPS = 2516.6
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--B", type=int, default=4)
+    ap.add_argument("--H", type=int, default=32)
+    ap.add_argument("--N", type=int, default=4096)
+    ap.add_argument("--d", type=int, default=128)
+    ap.add_argument("--causal", action="store_true")
+    ap.add_argument("--seed", type=int, default=2)
+    ap.add_argument("--no-naive", action="store_true", help="skip the naive GPU baseline")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def source_digest(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "exact_io_aware_55_amd", "csrc", n), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+# kernel name -> (sources that define it, how its algorithmic work is counted)
+KERNELS = {
+    "fwd": ("fa_fwd.hip", "fa_common.h"),
+    "bwd_preprocess": ("fa_bwd.hip", "fa_common.h"),
+    "bwd_kv_blocks": ("fa_bwd.hip", "fa_common.h"),
+    "bwd_dq_convert": ("fa_bwd.hip", "fa_common.h"),
+}
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from committed rocprofv3 counter runs, or None when
+    absent or taken on a different version of the kernel's sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        table = json.load(fh)
+    rec = table.get(f"{kernel}@{workload}")
+    if not rec or rec.get("source_sha") != source_digest(*KERNELS[kernel]):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def naive_step(torch, q, k, v, do, scale, causal):
+    """Standard attention materialised in HBM (bf16), forward and backward."""
+    B, N, H, d = q.shape
+    bh = lambda t: t.permute(0, 2, 1, 3).reshape(B * H, N, d).contiguous()
+    qh, kh, vh, doh = bh(q), bh(k), bh(v), bh(do)
+    s = torch.bmm(qh, kh.transpose(1, 2).contiguous()) * scale
+    if causal:
+        s.masked_fill_(torch.ones(N, N, device=q.device, dtype=torch.bool).triu_(1), float("-inf"))
+    p = torch.softmax(s, dim=-1)
+    o = torch.bmm(p, vh)
+    dv = torch.bmm(p.transpose(1, 2).contiguous(), doh)
+    dp = torch.bmm(doh, vh.transpose(1, 2).contiguous())
+    delta = (doh.float() * o.float()).sum(-1, keepdim=True)
+    ds = (p.float() * (dp.float() - delta)).to(torch.bfloat16)
+    dq = torch.bmm(ds, kh) * scale
+    dk = torch.bmm(ds.transpose(1, 2).contiguous(), qh) * scale
+    return o, dq, dk, dv
+
+
+def cpu_baseline(x, args, flops_per_head):
+    """fp64 oracle (forward + backward per head) on a bounded sample of heads."""
+    import numpy as np
+    import threadpoolctl
+
+    import oracle
+    from exact_io_aware_55_amd import inputs
+
+    qn, kn, vn, dn = (inputs.to_f64(x[n]) for n in ("q", "k", "v", "do"))
+    scale = args.d ** -0.5
+    heads = [(b, h) for b in range(args.B) for h in range(args.H)]
+    done = 0
+    t0 = time.perf_counter()
+    for b, h in heads:
+        a = (qn[b, :, h], kn[b, :, h], vn[b, :, h])
+        oracle.head_forward(*a, scale, args.causal)
+        oracle.head_backward(*a, dn[b, :, h], scale, args.causal)
+        done += 1
+        if time.perf_counter() - t0 >= args.cpu_seconds:
+            break
+    el = time.perf_counter() - t0
+    info = threadpoolctl.threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+    return {
+        "value": flops_per_head * done / el / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{done} of {len(heads)} heads (fp64 forward + backward per head, N={args.N}, "
+                  f"d={args.d}, causal={args.causal}) in {el:.1f} s; BLAS threads={threads}, "
+                  f"host cpus={os.cpu_count()}",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: every (batch, head) is independent and this build "
+              "has no multi-GPU path; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    sys.path.insert(0, ROOT)
+    from exact_io_aware_55_amd import binding, inputs, workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    binding.load()
+    dev = torch.device("cuda:0")
+    B, H, N, d, causal = args.B, args.H, args.N, args.d, args.causal
+    scale = d ** -0.5
+    wl = f"b{B}_h{H}_n{N}_d{d}{'_causal' if causal else ''}_fwd_bwd"
+
+    x = inputs.make_qkv(B, N, H, d, torch.bfloat16, seed=args.seed, with_do=True)
+    q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "do"))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), device=dev, dtype=torch.float32)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(binding.bwd_workspace_size(B, H, N, d), device=dev, dtype=torch.uint8)
+
+    def fwd():
+        binding.forward(q, k, v, causal=causal, scale=scale, out=o, lse=lse)
+
+    fwd()
+    _, bwd_calls = binding.backward_steps(q, k, v, o, do, lse, causal=causal, scale=scale,
+                                          workspace=ws, out=(dq, dk, dv))
+    stages = [("fwd", fwd)] + list(zip(("bwd_preprocess", "bwd_kv_blocks", "bwd_dq_convert"),
+                                       bwd_calls))
+    for _ in range(args.warmup):
+        for _, f in stages:
+            f()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        ev[s][0].record(stream)
+        for j, (_, f) in enumerate(stages):
+            f()
+            ev[s][j + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per = {name: sum(ev[s][j].elapsed_time(ev[s][j + 1]) for s in range(args.steps)) / args.steps
+           for j, (name, _) in enumerate(stages)}
+    fwd_fl = workloads.fwd_flops(B, H, N, d, causal)
+    bwd_fl = workloads.bwd_flops(B, H, N, d, causal)
+    step_fl = fwd_fl + bwd_fl
+    ms_per_step = wall / args.steps * 1e3
+    value = step_fl / (ms_per_step * 1e-3) / 1e12
+
+    rows = B * H * N
+    algo = {
+        "fwd": ("mfma", fwd_fl),
+        "bwd_kv_blocks": ("mfma", bwd_fl),
+        # HBM-bound helpers: read O, dO (bf16) + write D and the zeroed fp32 accumulator
+        "bwd_preprocess": ("hbm", rows * d * 2 * 2 + rows * 4 + rows * d * 4),
+        # read the fp32 accumulator, write bf16 dQ
+        "bwd_dq_convert": ("hbm", rows * d * 4 + rows * d * 2),
+    }
+    kernels = {}
+    for name, ms in per.items():
+        bound, work = algo[name]
+        if bound == "mfma":
+            ach = work / (ms * 1e-3) / 1e12
+            kernels[name] = {"ms": round(ms, 4), "tflops": round(ach, 1),
+                             "frac": round(ach / PEAK_BF16_TFLOPS, 4)}
+        else:
+            ach = work / (ms * 1e-3) / 1e9
+            kernels[name] = {"ms": round(ms, 4), "gbs": round(ach, 1),
+                             "frac": round(ach / PEAK_HBM_GBS, 4)}
+    dom = max(per, key=per.get)
+    bound, work = algo[dom]
+    if bound == "mfma":
+        ach, peak, unit = work / (per[dom] * 1e-3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
+    else:
+        ach, peak, unit = work / (per[dom] * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s"
+    roofline = {"bound": bound, "kernel": dom, "achieved": round(ach, 2), "peak": peak,
+                "unit": unit, "frac": round(ach / peak, 4),
+                "traffic": measured_traffic(dom, wl)}
+
+    out = {
+        "metric": "attention TFLOP/s (fwd+bwd) bf16 N=4096 d=128 on 1 GPU; % of MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl, "B": B, "H": H, "N": N, "d": d, "causal": causal,
+                   "layout": "[B,N,H,d]", "scale": "1/sqrt(d)", "parallelism": "single GPU"},
+        "fwd_tflops": round(fwd_fl / (per["fwd"] * 1e-3) / 1e12, 1),
+        "bwd_tflops": round(bwd_fl / (sum(per[n] for n in per if n != "fwd") * 1e-3) / 1e12, 1),
+        "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "kernels": kernels,
+        "roofline": roofline,
+    }
+
+    if not args.no_naive:
+        try:
+            for _ in range(2):
+                naive_step(torch, q, k, v, do, scale, causal)
+            torch.cuda.synchronize()
+            reps = max(3, min(10, args.steps))
+            t1 = time.perf_counter()
+            for _ in range(reps):
+                naive_step(torch, q, k, v, do, scale, causal)
+            torch.cuda.synchronize()
+            nms = (time.perf_counter() - t1) / reps * 1e3
+            out["naive_gpu_baseline"] = {
+                "value": round(step_fl / (nms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+                "ms_per_step": round(nms, 3),
+                "kind": "torch bf16 materialised scores + softmax + explicit backward",
+                "speedup_of_kernel": round(nms / ms_per_step, 2)}
+        except RuntimeError as exc:   # e.g. out of memory at very large shapes
+            out["naive_gpu_baseline"] = {"error": str(exc)[:200]}
+        torch.cuda.empty_cache()
+
+    if not args.no_cpu:
+        per_head = (fwd_fl + bwd_fl) / (B * H)
+        out["cpu_baseline"] = cpu_baseline(x, args, per_head)
+
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

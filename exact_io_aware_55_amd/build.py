@@ -25,7 +25,7 @@ ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-munsafe-fp-atomics", "-Wall", "-Wno-unused-function",
+    "-munsafe-fp-atomics", "-Wall", "-Wno-unused-function", "-Wno-inline-asm",
 ]
 
 

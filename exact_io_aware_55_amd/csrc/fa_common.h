@@ -41,7 +41,37 @@ __device__ __forceinline__ void st_lds4(void* p, uint32_t v) { *reinterpret_cast
 __device__ __forceinline__ bf16x8 ld_lds_bf16x8(const void* p) {
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
 }
+// LDS (address space 3) byte pointers, for reads whose offsets should fold
+// into the instruction's immediate field
+typedef __attribute__((address_space(3))) char lds_char;
+__device__ __forceinline__ bf16x8 lds_read_b128(const lds_char* p) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(p));
+}
+__device__ __forceinline__ bf16x4 lds_read_tr16(const lds_char* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(p));
+}
+__device__ __forceinline__ const lds_char* as_lds(const void* p) {
+    return (const lds_char*)(p);
+}
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
+
+// 16-byte direct global -> LDS load (global_load_lds_dwordx4): every lane
+// reads 16 bytes at base + offset and the wave writes them to LDS at
+// lds_base + 16 * lane.  Issued through asm so the compiler does not order
+// later LDS reads behind it (it cannot tell which LDS bytes a DMA writes);
+// callers wait on vmcnt themselves.  M0 carries the LDS base; nothing else
+// in these kernels uses M0.
+__device__ __forceinline__ unsigned lds_offset(const void* p) {
+    return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+__device__ __forceinline__ void dma16(const void* base, unsigned offset, unsigned lds_base) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(offset), "s"(base), "s"(lds_base)
+                 : "memory", "m0");
+}
+// s_waitcnt vmcnt(n) only (expcnt and lgkmcnt left alone), n <= 15
+#define FA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | (n))
 
 // Packs two floats into one dword of two bf16 (round to nearest even).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -60,6 +90,25 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // position 8b + 4a + t: bits 2 and 3 of the index swap places.
 __device__ __forceinline__ int kslot_pos(int idx) {
     return (idx & ~15) | (((idx >> 2) & 1) << 3) | (((idx >> 3) & 1) << 2) | (idx & 3);
+}
+
+// Combines a per-lane value with the lane 32 apart (the other half of the
+// same MFMA column) using v_permlane32_swap: r[0] is the value of lane l & 31,
+// r[1] that of lane 32 + (l & 31).
+__device__ __forceinline__ float halves_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
+                                                    __builtin_bit_cast(unsigned, x), false, false);
+    return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+__device__ __forceinline__ float halves_min(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
+                                                    __builtin_bit_cast(unsigned, x), false, false);
+    return fminf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
+                                                    __builtin_bit_cast(unsigned, x), false, false);
+    return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
 }
 
 // XOR swizzle of 16-byte chunks within a 128-byte LDS row (8 chunks): keeps

@@ -21,15 +21,19 @@
 //    into registers while the current one is multiplied: one barrier per block.
 //  * exponentials are v_exp_f32 (base 2) with scale * log2(e) folded into one
 //    FMA per score.
+#include <type_traits>
+
 #include "fa_common.h"
 #include "fa_launch.h"
 
 namespace fa {
 
 namespace fwd {
-constexpr int BR = 128;     // queries per workgroup
+constexpr int BR = 256;     // queries per workgroup (8 waves x 32)
 constexpr int BC = 64;      // keys per K/V block
-constexpr int NT = 256;     // threads per workgroup (4 waves)
+constexpr int NT = 512;     // threads per workgroup
+constexpr int NW = NT / 64; // waves
+constexpr int NSTAGE = 3;   // K/V blocks resident in the LDS ring
 }  // namespace fwd
 
 // Maps a linear workgroup id to (head, query block) so that the workgroups the
@@ -41,22 +45,35 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
     return x * per + (x < rem ? x : rem) + i;
 }
 
+// LDS layout of one K or V block (BC keys): D/32 sub-tiles [BC keys][32
+// features] with 64-byte rows (4 chunks of 16 bytes), chunk c of row R stored
+// at chunk c ^ swizzle(R).
+//  * K is read 16 bytes per lane down 32 consecutive rows (A operand of
+//    S^T = K Q^T); its swizzle ((R >> 1) ^ (R >> 2)) & 3 keeps the rows read
+//    together on distinct banks.
+//  * V is read with ds_read_tr16_b64 (A operand of O^T = V^T P^T): each
+//    16-lane group reads 4 consecutive rows x 32 bytes; swizzle 2((R >> 1) & 1).
+// Both swizzles depend only on the lane for every read of a block, so each
+// read is a per-lane base plus an immediate offset.
+__device__ __forceinline__ int k_swz(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
+__device__ __forceinline__ int v_swz(int row) { return ((row >> 1) & 1) << 1; }
+
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(fwd::NT) void fwd_bf16_kernel(
+__global__ __launch_bounds__(fwd::NT, 1) void fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     __bf16* __restrict__ O, float* __restrict__ LSE, int H, int N, float scale_log2, int nqb) {
     using namespace fwd;
-    constexpr int KP = D * 2 + 16;             // K row pitch (bytes)
-    constexpr int K_BYTES = BC * KP;
-    constexpr int VT_BYTES = D * BC * 2;       // V^T rows of 64 keys = 128 B
-    constexpr int STAGE = K_BYTES + VT_BYTES;
+    constexpr int TILE = BC * D * 2;           // one K or V block
+    constexpr int STAGE = 2 * TILE;            // K then V
+    constexpr int SUB = BC * 64;               // one sub-tile (32 features)
     constexpr int DC = D / 16;                 // k-chunks over the feature dim
-    constexpr int DT = D / 32;                 // 32-row tiles of O^T
-    constexpr int CPR = D / 8;                 // 16-byte chunks per row
-    constexpr int KLD = BC * CPR / NT;         // K chunks loaded per thread
-    constexpr int KPT = D / 32;                // keys per thread in the V transpose
+    constexpr int DT = D / 32;                 // 32-row tiles of O^T (= sub-tiles)
+    constexpr int SEGS = TILE / 1024;          // 1 KB segments per block (one wave load each)
+    constexpr int SEG_W = SEGS / NW;           // segments per wave per tensor
+    constexpr int SEG_SUB = SUB / 1024;        // segments per sub-tile
+    static_assert(SEGS % NW == 0, "segments per wave");
 
-    __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+    __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * STAGE];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hl = lane >> 5;
@@ -67,172 +84,210 @@ __global__ __launch_bounds__(fwd::NT) void fwd_bf16_kernel(
     int qb = logical - bh * nqb;
     if (CAUSAL) qb = nqb - 1 - qb;             // longest rows first
     const int b = bh / H, h = bh - b * H;
-    const long row_stride = (long)H * D;       // elements between sequence rows
+    const int row_stride = H * D;              // elements between sequence rows (N*H*D < 2^31)
     const long head_off = ((long)b * N * H + h) * D;
-    const __bf16* Qh = Q + head_off;
-    const __bf16* Kh = K + head_off;
-    const __bf16* Vh = V + head_off;
+    const char* Kh = reinterpret_cast<const char*>(K + head_off);
+    const char* Vh = reinterpret_cast<const char*>(V + head_off);
 
     const int q0 = qb * BR;
     const int qw = q0 + wave * 32;             // first query of this wave
     const int my_q = qw + l32;
 
-    // Queries of this lane, as B-operand chunks of S^T = K Q^T.
-    bf16x8 qreg[DC];
-    {
-        const bool ok = my_q < N;
-        const __bf16* src = Qh + (long)(ok ? my_q : 0) * row_stride + 8 * hl;
-#pragma unroll
-        for (int c = 0; c < DC; ++c) {
-            u32x4 v = ok ? ld_global16(src + 16 * c) : u32x4{0, 0, 0, 0};
-            qreg[c] = as_bf16x8(v);
-        }
-    }
-
     const int kv_end = CAUSAL ? min(N, q0 + BR) : N;
     const int ntiles = (kv_end + BC - 1) / BC;
 
-    // ---- register staging of one K/V block ----
-    u32x4 kst[KLD];
-    u32x4 vst[KPT];
-    auto load_tile = [&](int t) {
+    // Direct global -> LDS loads of one K/V block: each wave fills SEG_W 1 KB
+    // segments of K and of V; lane i writes bytes [16 i, 16 i + 16) of its
+    // segment (row 16 (seg % SEG_SUB) + i / 4 of sub-tile seg / SEG_SUB,
+    // physical chunk i % 4), so it loads the global chunk that belongs there.
+    // Keys past N read row N - 1 (finite data; their scores are masked, so
+    // their V rows get weight exactly 0).
+    int ld_row[SEG_W], k_col[SEG_W], v_col[SEG_W];
+#pragma unroll
+    for (int i = 0; i < SEG_W; ++i) {
+        const int seg = wave * SEG_W + i;
+        const int sub = seg / SEG_SUB, r = (seg % SEG_SUB) * 16 + lane / 4;
+        ld_row[i] = r;
+        k_col[i] = sub * 64 + (((lane & 3) ^ k_swz(r)) << 4);   // bytes within the global row
+        v_col[i] = sub * 64 + (((lane & 3) ^ v_swz(r)) << 4);
+    }
+    const unsigned row_bytes = (unsigned)row_stride * 2u;
+    const unsigned lds0 = lds_offset(smem);
+    auto issue_tile = [&](int t) {
         const int j0 = t * BC;
+        const unsigned kb = lds0 + (t % NSTAGE) * STAGE;
 #pragma unroll
-        for (int i = 0; i < KLD; ++i) {
-            const int c = tid + NT * i;
-            const int r = c / CPR, cc = c % CPR;
-            const int key = j0 + r;
-            kst[i] = key < N ? ld_global16(Kh + (long)key * row_stride + cc * 8) : u32x4{0, 0, 0, 0};
-        }
-        const int dblk = tid % CPR, kg = tid / CPR;
-#pragma unroll
-        for (int i = 0; i < KPT; ++i) {
-            const int key = j0 + kg * KPT + i;
-            vst[i] = key < N ? ld_global16(Vh + (long)key * row_stride + dblk * 8) : u32x4{0, 0, 0, 0};
+        for (int i = 0; i < SEG_W; ++i) {
+            const int seg = wave * SEG_W + i;
+            const unsigned ro = (unsigned)min(j0 + ld_row[i], N - 1) * row_bytes;
+            dma16(Kh, ro + k_col[i], __builtin_amdgcn_readfirstlane(kb + seg * 1024));
+            dma16(Vh, ro + v_col[i], __builtin_amdgcn_readfirstlane(kb + TILE + seg * 1024));
         }
     };
-    auto store_tile = [&](int buf) {
-        char* kb = smem + buf * STAGE;
-        char* vb = kb + K_BYTES;
+
+    issue_tile(0);
+    if (ntiles > 1) issue_tile(1);
+
+    // Queries of this lane, as B-operand chunks of S^T = K Q^T.  Rows past N
+    // read row N-1 (finite data whose results are never stored).
+    bf16x8 qreg[DC];
+    {
+        const __bf16* src = Q + head_off + (long)min(my_q, N - 1) * row_stride + 8 * hl;
 #pragma unroll
-        for (int i = 0; i < KLD; ++i) {
-            const int c = tid + NT * i;
-            const int r = c / CPR, cc = c % CPR;
-            st_lds16(kb + r * KP + cc * 16, kst[i]);
-        }
-        // transpose KPT keys x 8 features into 8 rows of V^T
-        const int dblk = tid % CPR, kg = tid / CPR;
-        const int pos = kslot_pos(kg * KPT);
+        for (int c = 0; c < DC; ++c) qreg[c] = as_bf16x8(ld_global16(src + 16 * c));
+    }
+    // Consume the Q registers here (the empty asm reads them), so the compiler
+    // waits for the Q loads before the loop rather than inside it, where the
+    // wait would also stall on the block prefetch.
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int d = dblk * 8 + e;
-            const int w = e >> 1, sh = (e & 1) * 16;
-            char* dst = vb + d * 128 + (((pos >> 3) ^ swz8(d)) << 4) + (pos & 7) * 2;
-            if constexpr (KPT == 4) {
-                const uint32_t a0 = (vst[0][w] >> sh) & 0xffffu, a1 = (vst[1][w] >> sh) & 0xffffu;
-                const uint32_t a2 = (vst[2][w] >> sh) & 0xffffu, a3 = (vst[3][w] >> sh) & 0xffffu;
-                st_lds8(dst, u32x2{a0 | (a1 << 16), a2 | (a3 << 16)});
-            } else {
-                const uint32_t a0 = (vst[0][w] >> sh) & 0xffffu, a1 = (vst[1][w] >> sh) & 0xffffu;
-                st_lds4(dst, a0 | (a1 << 16));
-            }
-        }
-    };
+    for (int c = 0; c < DC; ++c) asm volatile("" : "+v"(qreg[c]));
 
     f32x16 oacc[DT];
 #pragma unroll
     for (int i = 0; i < DT; ++i) oacc[i] = f32x16{};
-    float m_run = -INFINITY;   // running max of scale*log2(e)*s for this lane's query
+    // Running max of scale*log2(e)*s for this lane's query.  It is raised only
+    // when a block's maximum exceeds it by more than kLazy (log2 units), so
+    // P = exp2(x - m) stays below 2^kLazy; the output and LSE use the same m,
+    // so the result is exact whichever m was used.
+    constexpr float kLazy = 8.f;
+    float m_run = -INFINITY;
     float l_run = 0.f;         // running sum over this lane's half of the keys
     const bool pos_scale = scale_log2 >= 0.f;
     const float masked = pos_scale ? -INFINITY : INFINITY;
 
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
+    // per-lane LDS byte offsets of the operand reads (within a stage)
+    const int k_rd0 = l32 * 64 + ((hl ^ k_swz(l32)) << 4);          // even k-chunks c
+    const int k_rd1 = l32 * 64 + (((2 + hl) ^ k_swz(l32)) << 4);    // odd k-chunks c
+    const int tr_g = lane >> 4, tr_j = lane & 15;
+    const int tr_row = 4 * (tr_g >> 1) + (tr_j >> 2);                // + 16 cc + 8 w
+    const int v_rd = TILE + tr_row * 64 + (((2 * (tr_g & 1) + ((tr_j & 3) >> 1)) ^ v_swz(tr_row)) << 4) +
+                     ((tr_j & 1) << 3);
 
+#pragma clang loop unroll(disable)
     for (int t = 0; t < ntiles; ++t) {
-        const int buf = t & 1;
-        const bool has_next = t + 1 < ntiles;
-        if (has_next) load_tile(t + 1);
+        // block t landed (block t+1 may still be in flight), then make every
+        // wave's part visible; the barrier also retires all reads of block t-1
+        // (plain s_barrier, no fence: a fence would wait for block t+1 too)
+        if (t + 1 < ntiles) FA_WAIT_VMCNT(2 * SEG_W);
+        else FA_WAIT_VMCNT(0);
+        __builtin_amdgcn_s_barrier();
+        if (t + 2 < ntiles) issue_tile(t + 2);
 
         const int j0 = t * BC;
         const bool wave_active = !CAUSAL || j0 <= qw + 31;
         if (wave_active) {
-            const char* kb = smem + buf * STAGE;
-            const char* vb = kb + K_BYTES;
+            // per-iteration bases; the empty asm keeps the compiler from
+            // hoisting base + offset sums into separate registers, so the
+            // offsets fold into the LDS instructions
+            const lds_char* stage = as_lds(smem) + (t % NSTAGE) * STAGE;
+            const lds_char* kb0 = stage + k_rd0;
+            const lds_char* kb1 = stage + k_rd1;
+            const lds_char* vb = stage + v_rd;
+            asm volatile("" : "+v"(kb0), "+v"(kb1), "+v"(vb));
             // S^T = K Q^T for two 32-key tiles
             f32x16 s[2];
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt) {
                 s[kt] = f32x16{};
-                const char* krow = kb + (kt * 32 + l32) * KP + hl * 16;
 #pragma unroll
-                for (int c = 0; c < DC; ++c) s[kt] = mfma32x32x16(ld_lds_bf16x8(krow + c * 32), qreg[c], s[kt]);
-            }
-            // masks: keys past N (ragged tail) and, for causal, keys after the query
-            const bool need_mask = (j0 + BC > N) || (CAUSAL && j0 + BC - 1 > qw);
-            if (need_mask) {
-#pragma unroll
-                for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = j0 + kt * 32 + (r >> 2) * 8 + hl * 4 + (r & 3);
-                        const bool vis = key < N && (!CAUSAL || key <= my_q);
-                        s[kt][r] = vis ? s[kt][r] : masked;
-                    }
-            }
-            // block maximum of the scaled scores for this query (both lane halves)
-            float mx = s[0][0];
-            if (pos_scale) {
-#pragma unroll
-                for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
-            } else {
-#pragma unroll
-                for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) mx = fminf(mx, s[kt][r]);
-            }
-            mx = pos_scale ? fmaxf(mx, __shfl_xor(mx, 32)) : fminf(mx, __shfl_xor(mx, 32));
-            const float m_new = fmaxf(m_run, mx * scale_log2);
-            const float m_sub = m_new == -INFINITY ? 0.f : m_new;
-            const float alpha = fast_exp2(m_run - m_sub);
-            m_run = m_new;
-            // P = exp2(s * scale*log2e - m); row sum; pack to bf16 k-chunks
-            bf16x8 pb[4];
-            float lsum = 0.f;
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float p = fast_exp2(__builtin_fmaf(s[kt][r], scale_log2, -m_sub));
-                    // a masked score must give exactly 0, also when scale == 0
-                    if (need_mask) p = s[kt][r] == masked ? 0.f : p;
-                    lsum += p;
-                    pb[kt * 2 + (r >> 3)][r & 7] = (__bf16)p;
+                for (int c = 0; c < DC; ++c) {
+                    const lds_char* a = ((c & 1) ? kb1 : kb0) + (c >> 1) * SUB + kt * 32 * 64;
+                    s[kt] = mfma32x32x16(lds_read_b128(a), qreg[c], s[kt]);
                 }
-            l_run = l_run * alpha + lsum;
+            }
+            // keep the V reads below the softmax (register pressure)
+            __builtin_amdgcn_sched_barrier(0);
+            u32x4 pw[4];
+            // MASK: keys past N and, for causal, keys after the query.  The two
+            // variants cover only the block max and the exponentials; the
+            // rescale of O sits between them, outside both, so the compiler
+            // keeps O in place across that (rarely taken) branch.
+            const bool need_mask = (j0 + BC > N) || (CAUSAL && j0 + BC - 1 > qw);
+            auto block_max = [&](auto mask_tag) {
+                constexpr bool MASK = decltype(mask_tag)::value;
+                if constexpr (MASK) {
+                    // key of register r = j0 + 4 hl + off(kt, r), off a constant:
+                    // compare the constant with one per-lane limit
+                    const int lim_n = N - j0 - 4 * hl;            // visible iff off < lim_n
+                    const int lim_c = my_q - j0 - 4 * hl;         // causal: off <= lim_c
 #pragma unroll
-            for (int i = 0; i < DT; ++i) oacc[i] *= alpha;
-            // O^T += V^T P^T
+                    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int off = kt * 32 + (r >> 2) * 8 + (r & 3);
+                            const bool vis = off < lim_n && (!CAUSAL || off <= lim_c);
+                            s[kt][r] = vis ? s[kt][r] : masked;
+                        }
+                }
+                float mx = s[0][0];
+                if (pos_scale) {
+#pragma unroll
+                    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
+                    return halves_max(mx);
+                } else {
+#pragma unroll
+                    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) mx = fminf(mx, s[kt][r]);
+                    return halves_min(mx);
+                }
+            };
+            const float mt = (need_mask ? block_max(std::true_type{}) : block_max(std::false_type{})) * scale_log2;
+            if (__builtin_amdgcn_ballot_w64(mt > m_run + kLazy) != 0) {
+                const float m_new = fmaxf(m_run, mt);
+                const float alpha = fast_exp2(m_run - m_new);
+                m_run = m_new;
+                l_run *= alpha;
+#pragma unroll
+                for (int i = 0; i < DT; ++i) oacc[i] *= alpha;
+            }
+            const float m_sub = m_run == -INFINITY ? 0.f : m_run;
+            // P = exp2(x - m): the row sum accumulates in fp32 (so LSE keeps
+            // fp32 accuracy); the PV product uses P rounded to bf16
+            auto block_exp = [&](auto mask_tag) {
+                constexpr bool MASK = decltype(mask_tag)::value;
+                float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                    for (int r = 0; r < 16; r += 2) {
+                        float p0 = fast_exp2(__builtin_fmaf(s[kt][r], scale_log2, -m_sub));
+                        float p1 = fast_exp2(__builtin_fmaf(s[kt][r + 1], scale_log2, -m_sub));
+                        // a masked score must give exactly 0, also when scale == 0
+                        if constexpr (MASK) {
+                            p0 = s[kt][r] == masked ? 0.f : p0;
+                            p1 = s[kt][r + 1] == masked ? 0.f : p1;
+                        }
+                        ls0 += p0;
+                        ls1 += p1;
+                        pw[kt * 2 + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(p0, p1);
+                    }
+                l_run += ls0 + ls1;
+            };
+            if (need_mask) block_exp(std::true_type{});
+            else block_exp(std::false_type{});
+            __builtin_amdgcn_sched_barrier(0);
+            // O^T += V^T P^T; the A operand (8 keys of one feature row) comes
+            // from two transposing reads: keys 16cc + 4h + 0..3 and +8.
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
-                const int d = dt * 32 + l32;
-                const char* vrow = vb + d * 128;
-                const int sw = swz8(d);
 #pragma unroll
-                for (int cc = 0; cc < 4; ++cc)
-                    oacc[dt] = mfma32x32x16(ld_lds_bf16x8(vrow + (((2 * cc + hl) ^ sw) << 4)), pb[cc], oacc[dt]);
+                for (int cc = 0; cc < 4; ++cc) {
+                    const lds_char* a0 = vb + dt * SUB + cc * 16 * 64;
+                    const bf16x4 lo = lds_read_tr16(a0);
+                    const bf16x4 hi = lds_read_tr16(a0 + 8 * 64);
+                    const bf16x8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                    oacc[dt] = mfma32x32x16(va, __builtin_bit_cast(bf16x8, pw[cc]), oacc[dt]);
+                }
             }
         }
-        if (has_next) store_tile(buf ^ 1);
-        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
     }
 
     // ---- epilogue: O = O / l, LSE = m ln2 + ln l ----
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float l_tot = halves_sum(l_run);
     const float inv = 1.f / l_tot;
     if (my_q < N) {
         __bf16* dst = O + head_off + (long)my_q * row_stride;
