@@ -49,9 +49,9 @@ def load(path: str = LIB_PATH):
     lib.fa_bwd_workspace_size.restype = sz
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, sz, vp]
     lib.fa_bwd.restype = i
-    lib.fa_bwd_preprocess.argtypes = [vp, vp, i, i, i, i, vp, sz, vp]
+    lib.fa_bwd_preprocess.argtypes = [vp, vp, vp, i, i, i, i, vp, sz, vp]
     lib.fa_bwd_preprocess.restype = i
-    lib.fa_bwd_kv_blocks.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, sz, vp]
+    lib.fa_bwd_kv_blocks.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, sz, vp]
     lib.fa_bwd_kv_blocks.restype = i
     lib.fa_bwd_dq_convert.argtypes = [vp, i, i, i, i, vp, sz, vp]
     lib.fa_bwd_dq_convert.restype = i
@@ -157,9 +157,10 @@ def backward_steps(q, k, v, o, do, lse, causal=False, scale=None, workspace=None
     sc = _scale(scale, d)
     c = int(bool(causal))
     calls = [
-        lambda: _check(lib.fa_bwd_preprocess(_ptr(o), _ptr(do), B, H, N, d, _ptr(ws), nbytes, _stream())),
-        lambda: _check(lib.fa_bwd_kv_blocks(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(dk),
-                                            _ptr(dv), B, H, N, d, sc, c, _ptr(ws), nbytes, _stream())),
+        lambda: _check(lib.fa_bwd_preprocess(_ptr(o), _ptr(do), _ptr(lse), B, H, N, d, _ptr(ws), nbytes,
+                                             _stream())),
+        lambda: _check(lib.fa_bwd_kv_blocks(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dk), _ptr(dv),
+                                            B, H, N, d, sc, c, _ptr(ws), nbytes, _stream())),
         lambda: _check(lib.fa_bwd_dq_convert(_ptr(dq), B, H, N, d, _ptr(ws), nbytes, _stream())),
     ]
     for call in calls:

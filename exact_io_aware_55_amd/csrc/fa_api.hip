@@ -22,7 +22,8 @@ int check_shape(int B, int H, int N, int d, float scale) {
     if (B < 1 || H < 1 || N < 1) return FA_ERR_INVALID_ARG;
     if (!isfinite(scale)) return FA_ERR_INVALID_ARG;
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
-    if ((long long)N * H * d >= (1LL << 31)) return FA_ERR_UNSUPPORTED;
+    // per-lane byte offsets within one batch's [N, H, d] rows stay below 2^31
+    if ((long long)N * H * d >= (1LL << 30)) return FA_ERR_UNSUPPORTED;
     // grid size: B * H * ceil(N / 64) workgroups must fit a 32-bit grid
     if ((long long)B * H * ((N + 63) / 64) >= (1LL << 31)) return FA_ERR_UNSUPPORTED;
     return FA_OK;
@@ -62,23 +63,26 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
 
 size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
     if (check_shape(B, H, N, d, 1.0f) != FA_OK) return 0;
-    const size_t rows = (size_t)B * H * N;
-    return align256(rows * sizeof(float)) + align256(rows * (size_t)d * sizeof(float));
+    const size_t stat_rows = (size_t)B * H * fa::bwd_rows_padded(N);
+    return 2 * align256(stat_rows * sizeof(float)) + align256((size_t)B * N * H * d * sizeof(float));
 }
 
 namespace {
 struct Workspace {
-    float* delta;
-    float* dq_acc;
+    float* lse2;     // LSE * log2(e), [B, H, Npad] (padding +inf)
+    float* delta;    // D = rowsum(dO * O), [B, H, Npad] (padding 0)
+    float* dq_acc;   // fp32 dQ accumulator, [B, N, H, d]
 };
 
 int check_workspace(void* workspace, size_t workspace_bytes, int B, int H, int N, int d, Workspace* ws) {
     const size_t need = fa_bwd_workspace_size(B, H, N, d);
     if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) || workspace_bytes < need)
         return FA_ERR_WORKSPACE;
-    ws->delta = static_cast<float*>(workspace);
-    ws->dq_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                          align256((size_t)B * H * N * sizeof(float)));
+    const size_t stat = align256((size_t)B * H * fa::bwd_rows_padded(N) * sizeof(float));
+    char* w = static_cast<char*>(workspace);
+    ws->lse2 = reinterpret_cast<float*>(w);
+    ws->delta = reinterpret_cast<float*>(w + stat);
+    ws->dq_acc = reinterpret_cast<float*>(w + 2 * stat);
     return FA_OK;
 }
 
@@ -89,29 +93,37 @@ int all_aligned(std::initializer_list<const void*> ptrs) {
         if (!aligned16(p)) return FA_ERR_MISALIGNED;
     return FA_OK;
 }
+
+// the key-block kernel addresses the row statistics with 32-bit byte offsets
+int check_bwd_shape(int B, int H, int N, int d, float scale) {
+    const int rc = check_shape(B, H, N, d, scale);
+    if (rc != FA_OK) return rc;
+    if ((long long)B * H * fa::bwd_rows_padded(N) >= (1LL << 28)) return FA_ERR_UNSUPPORTED;
+    return FA_OK;
+}
 }  // namespace
 
-int fa_bwd_preprocess(const void* o, const void* dout, int B, int H, int N, int d, void* workspace,
-                      size_t workspace_bytes, hipStream_t stream) {
-    int rc = all_aligned({o, dout});
+int fa_bwd_preprocess(const void* o, const void* dout, const float* lse, int B, int H, int N, int d,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    int rc = all_aligned({o, dout, lse});
     if (rc != FA_OK) return rc;
-    if ((rc = check_shape(B, H, N, d, 1.0f)) != FA_OK) return rc;
+    if ((rc = check_bwd_shape(B, H, N, d, 1.0f)) != FA_OK) return rc;
     Workspace ws;
     if ((rc = check_workspace(workspace, workspace_bytes, B, H, N, d, &ws)) != FA_OK) return rc;
-    if (fa::launch_bwd_preprocess(o, dout, B, H, N, d, ws.delta, ws.dq_acc, stream) != hipSuccess)
+    if (fa::launch_bwd_preprocess(o, dout, lse, B, H, N, d, ws.lse2, ws.delta, ws.dq_acc, stream) != hipSuccess)
         return FA_ERR_LAUNCH;
     return FA_OK;
 }
 
-int fa_bwd_kv_blocks(const void* q, const void* k, const void* v, const void* dout, const float* lse,
-                     void* dk, void* dv, int B, int H, int N, int d, float scale, int causal,
-                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
-    int rc = all_aligned({q, k, v, dout, lse, dk, dv});
+int fa_bwd_kv_blocks(const void* q, const void* k, const void* v, const void* dout, void* dk, void* dv,
+                     int B, int H, int N, int d, float scale, int causal, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
+    int rc = all_aligned({q, k, v, dout, dk, dv});
     if (rc != FA_OK) return rc;
-    if ((rc = check_shape(B, H, N, d, scale)) != FA_OK) return rc;
+    if ((rc = check_bwd_shape(B, H, N, d, scale)) != FA_OK) return rc;
     Workspace ws;
     if ((rc = check_workspace(workspace, workspace_bytes, B, H, N, d, &ws)) != FA_OK) return rc;
-    if (fa::launch_bwd_kv_blocks(q, k, v, dout, lse, dk, dv, B, H, N, d, scale, causal != 0, ws.delta,
+    if (fa::launch_bwd_kv_blocks(q, k, v, dout, dk, dv, B, H, N, d, scale, causal != 0, ws.lse2, ws.delta,
                                  ws.dq_acc, stream) != hipSuccess)
         return FA_ERR_LAUNCH;
     return FA_OK;
@@ -121,7 +133,7 @@ int fa_bwd_dq_convert(void* dq, int B, int H, int N, int d, void* workspace, siz
                       hipStream_t stream) {
     int rc = all_aligned({dq});
     if (rc != FA_OK) return rc;
-    if ((rc = check_shape(B, H, N, d, 1.0f)) != FA_OK) return rc;
+    if ((rc = check_bwd_shape(B, H, N, d, 1.0f)) != FA_OK) return rc;
     Workspace ws;
     if ((rc = check_workspace(workspace, workspace_bytes, B, H, N, d, &ws)) != FA_OK) return rc;
     if (fa::launch_bwd_dq_convert(dq, B, H, N, d, ws.dq_acc, stream) != hipSuccess) return FA_ERR_LAUNCH;
@@ -134,11 +146,12 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
     // validate everything before the first launch
     int rc = all_aligned({q, k, v, o, dout, lse, dq, dk, dv});
     if (rc != FA_OK) return rc;
-    if ((rc = check_shape(B, H, N, d, scale)) != FA_OK) return rc;
+    if ((rc = check_bwd_shape(B, H, N, d, scale)) != FA_OK) return rc;
     Workspace ws;
     if ((rc = check_workspace(workspace, workspace_bytes, B, H, N, d, &ws)) != FA_OK) return rc;
-    if ((rc = fa_bwd_preprocess(o, dout, B, H, N, d, workspace, workspace_bytes, stream)) != FA_OK) return rc;
-    if ((rc = fa_bwd_kv_blocks(q, k, v, dout, lse, dk, dv, B, H, N, d, scale, causal, workspace,
+    if ((rc = fa_bwd_preprocess(o, dout, lse, B, H, N, d, workspace, workspace_bytes, stream)) != FA_OK)
+        return rc;
+    if ((rc = fa_bwd_kv_blocks(q, k, v, dout, dk, dv, B, H, N, d, scale, causal, workspace,
                                workspace_bytes, stream)) != FA_OK)
         return rc;
     return fa_bwd_dq_convert(dq, B, H, N, d, workspace, workspace_bytes, stream);
@@ -148,7 +161,7 @@ const char* fa_strerror(int code) {
     switch (code) {
         case FA_OK: return "success";
         case FA_ERR_INVALID_ARG: return "invalid argument (null pointer, B/H/N < 1 or non-finite scale)";
-        case FA_ERR_UNSUPPORTED: return "unsupported shape (d must be 64 or 128, N*H*d < 2^31)";
+        case FA_ERR_UNSUPPORTED: return "unsupported shape (d must be 64 or 128, N*H*d < 2^30)";
         case FA_ERR_MISALIGNED: return "pointer not 16-byte aligned";
         case FA_ERR_WORKSPACE: return "workspace null, not 256-byte aligned or smaller than fa_bwd_workspace_size()";
         case FA_ERR_LAUNCH: return "kernel launch failed";

@@ -65,9 +65,16 @@ __device__ __forceinline__ unsigned lds_offset(const void* p) {
     return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
 __device__ __forceinline__ void dma16(const void* base, unsigned offset, unsigned lds_base) {
+    // the base must be wave-uniform; readfirstlane puts it in SGPRs.  The
+    // builtin returns a signed int: widen through unsigned, or a low half
+    // with bit 31 set would sign-extend over the high half.
+    const unsigned long long b = reinterpret_cast<unsigned long long>(base);
+    const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)(b >> 32));
+    const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)b);
+    const unsigned long long sb = ((unsigned long long)hi << 32) | (unsigned long long)lo;
     asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                  :
-                 : "v"(offset), "s"(base), "s"(lds_base)
+                 : "v"(offset), "s"(sb), "s"(lds_base)
                  : "memory", "m0");
 }
 // s_waitcnt vmcnt(n) only (expcnt and lgkmcnt left alone), n <= 15
@@ -115,5 +122,14 @@ __device__ __forceinline__ float halves_sum(float x) {
 // 16-lane 128-bit reads of one logical chunk from consecutive rows on
 // distinct banks, for both 32- and 64-bank LDS organisations.
 __device__ __forceinline__ int swz8(int row) { return (row ^ (row >> 3)) & 7; }
+
+// Swizzle of 16-byte chunks in 64-byte LDS rows for tiles read both ways:
+// 16 bytes per lane down 32 consecutive rows (ds_read_b128) and transposed
+// (ds_read_tr16_b64, 4 consecutive rows x 32 bytes per 16-lane group).
+// chunk' = chunk ^ (R2 | (R1 ^ R3) << 1) keeps both patterns at the minimum
+// number of LDS cycles for 128-byte/clock banking.
+__device__ __forceinline__ int dual_swz(int row) {
+    return ((row >> 2) & 1) | ((((row >> 1) ^ (row >> 3)) & 1) << 1);
+}
 
 }  // namespace fa

@@ -31,8 +31,8 @@
  * their matrix products, outputs are rounded to bf16 once).  The fp32 entry
  * point takes and returns fp32 and computes in fp32 throughout.
  *
- * Supported: d in {64, 128}; B, H, N >= 1; N * H * d < 2^31; any finite
- * scale.  Pointers must be device pointers aligned to 16 bytes.
+ * Supported: d in {64, 128}; B, H, N >= 1; N * H * d < 2^30 (per-lane
+ * 32-bit byte offsets within one batch's rows); any finite scale.  Pointers must be device pointers aligned to 16 bytes.
  *
  * Ownership and streams.  The caller owns every buffer (including the
  * backward workspace).  The library never allocates, frees or synchronises:
@@ -60,7 +60,7 @@ typedef struct ihipStream_t* hipStream_t;
 enum {
     FA_OK = 0,
     FA_ERR_INVALID_ARG = -1, /* null pointer, B/H/N < 1, non-finite scale */
-    FA_ERR_UNSUPPORTED = -2, /* d not in {64, 128}, or N*H*d >= 2^31     */
+    FA_ERR_UNSUPPORTED = -2, /* d not in {64, 128}, or N*H*d >= 2^30     */
     FA_ERR_MISALIGNED = -3,  /* a pointer not 16-byte aligned             */
     FA_ERR_WORKSPACE = -4,   /* workspace null, misaligned or too small   */
     FA_ERR_LAUNCH = -5       /* the HIP runtime rejected a kernel launch  */
@@ -77,8 +77,9 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
                int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
 
 /* Bytes of device workspace fa_bwd needs for this shape (0 if the shape is
- * invalid).  It holds the fp32 row statistic D [B,H,N] and an fp32 dQ
- * accumulator [B,N,H,d], each 256-byte aligned. */
+ * invalid).  It holds two fp32 row statistics per head, padded to a multiple
+ * of 64 rows ([B,H,Npad]: LSE * log2(e) and D = rowsum(dO * O)), and an fp32
+ * dQ accumulator [B,N,H,d], each 256-byte aligned. */
 size_t fa_bwd_workspace_size(int B, int H, int N, int d);
 
 /* bf16 backward with recomputation.  q, k, v, o, dout: bf16 [B,N,H,d]
@@ -94,9 +95,9 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
 /* The three steps fa_bwd runs, exported separately so a caller can schedule
  * or time them individually.  All share fa_bwd's workspace layout and must
  * run in this order on one stream for one backward:
- *   fa_bwd_preprocess: D_i = sum_k dO_ik O_ik (fp32, into the workspace) and
- *                      zero the fp32 dQ accumulator.  The row statistic D is
- *                      the softmax-Jacobian term of the backward (not on the
+ *   fa_bwd_preprocess: D_i = sum_k dO_ik O_ik and LSE_i * log2(e) into the
+ *                      workspace, and zero the fp32 dQ accumulator.  D is the
+ *                      softmax-Jacobian term of the backward (not on the
  *                      pages, which only require recomputation).
  *   fa_bwd_kv_blocks:  for each block of keys, walk the query blocks that can
  *                      see them, recompute P = exp(scale QK^T - LSE), and form
@@ -104,13 +105,14 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
  *                      dQ (added to the fp32 accumulator with float atomics,
  *                      so dQ is not bitwise repeatable; dK and dV are).
  *   fa_bwd_dq_convert: dQ = bf16(accumulator).
- * Arguments have the meaning and layout given for fa_bwd. */
-int fa_bwd_preprocess(const void* o, const void* dout, int B, int H, int N, int d,
-                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+ * Arguments have the meaning and layout given for fa_bwd.  Backward calls
+ * also require B * H * Npad < 2^28 (Npad = N rounded up to a multiple of 64),
+ * else FA_ERR_UNSUPPORTED. */
+int fa_bwd_preprocess(const void* o, const void* dout, const float* lse, int B, int H, int N,
+                      int d, void* workspace, size_t workspace_bytes, hipStream_t stream);
 int fa_bwd_kv_blocks(const void* q, const void* k, const void* v, const void* dout,
-                     const float* lse, void* dk, void* dv, int B, int H, int N, int d,
-                     float scale, int causal, void* workspace, size_t workspace_bytes,
-                     hipStream_t stream);
+                     void* dk, void* dv, int B, int H, int N, int d, float scale, int causal,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 int fa_bwd_dq_convert(void* dq, int B, int H, int N, int d, void* workspace,
                       size_t workspace_bytes, hipStream_t stream);
 

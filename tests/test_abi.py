@@ -67,11 +67,12 @@ def test_forward_argument_errors(lib, fn):
 
 
 def test_workspace_size(lib):
-    B, H, N, d = 4, 16, 4096, 64
-    rows = B * H * N
-    want = ((rows * 4 + 255) // 256) * 256 + ((rows * d * 4 + 255) // 256) * 256
-    assert lib.fa_bwd_workspace_size(B, H, N, d) == want
-    assert lib.fa_bwd_workspace_size(1, 1, 7, 128) == 256 + ((7 * 128 * 4 + 255) // 256) * 256
+    def want(B, H, N, d):
+        a256 = lambda x: (x + 255) // 256 * 256
+        npad = (N + 63) // 64 * 64
+        return 2 * a256(B * H * npad * 4) + a256(B * N * H * d * 4)
+    assert lib.fa_bwd_workspace_size(4, 16, 4096, 64) == want(4, 16, 4096, 64)
+    assert lib.fa_bwd_workspace_size(1, 1, 7, 128) == want(1, 1, 7, 128) == 2 * 256 + 3584
     assert lib.fa_bwd_workspace_size(0, 1, 8, 64) == 0
     assert lib.fa_bwd_workspace_size(1, 1, 8, 80) == 0
 
@@ -103,12 +104,15 @@ def test_backward_argument_errors(lib):
 def test_backward_step_argument_errors(lib):
     V = ctypes.c_void_p
     f = lib.fa_bwd_preprocess
-    assert f(None, V(FAKE), 1, 1, 8, 64, V(FAKE), 1 << 20, None) == binding.FA_ERR_INVALID_ARG
-    assert f(V(FAKE + 2), V(FAKE), 1, 1, 8, 64, V(FAKE), 1 << 20, None) == binding.FA_ERR_MISALIGNED
-    assert f(V(FAKE), V(FAKE), 1, 1, 8, 96, V(FAKE), 1 << 20, None) == binding.FA_ERR_UNSUPPORTED
-    assert f(V(FAKE), V(FAKE), 1, 1, 8, 64, V(FAKE), 16, None) == binding.FA_ERR_WORKSPACE
+    ok3 = [V(FAKE)] * 3
+    assert f(None, V(FAKE), V(FAKE), 1, 1, 8, 64, V(FAKE), 1 << 20, None) == binding.FA_ERR_INVALID_ARG
+    assert f(V(FAKE), V(FAKE), None, 1, 1, 8, 64, V(FAKE), 1 << 20, None) == binding.FA_ERR_INVALID_ARG
+    assert f(V(FAKE + 2), V(FAKE), V(FAKE), 1, 1, 8, 64, V(FAKE), 1 << 20, None) == binding.FA_ERR_MISALIGNED
+    assert f(*ok3, 1, 1, 8, 96, V(FAKE), 1 << 20, None) == binding.FA_ERR_UNSUPPORTED
+    assert f(*ok3, 1, 1, 8, 64, V(FAKE), 16, None) == binding.FA_ERR_WORKSPACE
+    assert f(*ok3, 1 << 12, 1 << 8, 1 << 9, 64, V(FAKE), 1 << 20, None) == binding.FA_ERR_UNSUPPORTED
     g = lib.fa_bwd_kv_blocks
-    ok = [V(FAKE)] * 7
+    ok = [V(FAKE)] * 6
     assert g(*ok, 1, 1, 8, 64, float("inf"), 0, V(FAKE), 1 << 20, None) == binding.FA_ERR_INVALID_ARG
     assert g(*ok, 1, 0, 8, 64, 0.1, 0, V(FAKE), 1 << 20, None) == binding.FA_ERR_INVALID_ARG
     assert g(*ok, 1, 1, 8, 64, 0.1, 0, None, 1 << 20, None) == binding.FA_ERR_WORKSPACE
