@@ -2,7 +2,7 @@
 
 One step = one pass of the whole hot path over one batch: the forward
 (fa_fwd: tiled online softmax, writes O and LSE) followed by the backward by
-recomputation (fa_bwd_preprocess, fa_bwd_kv_blocks, fa_bwd_dq_convert).
+recomputation (fa_bwd_preprocess, fa_bwd_dkdv, fa_bwd_dq).
 Default workload: B=4, H=32, N=4096, d=128, bf16, non-causal, scale 1/sqrt(d),
 seeded N(0,1) inputs resident in HBM before timing starts.
 
@@ -45,7 +45,24 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain device-to-device copy of 1 GiB (3 times), the "
+                         "reference for scaling HBM byte counters")
     return ap.parse_args()
+
+
+def copy_calibration():
+    """A plain 1 GiB device copy: reads 1 GiB and writes 1 GiB per launch."""
+    import torch
+
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
+                      "launches": 3}), flush=True)
 
 
 def source_digest(*names):
@@ -60,8 +77,8 @@ def source_digest(*names):
 KERNELS = {
     "fwd": ("fa_fwd.hip", "fa_common.h"),
     "bwd_preprocess": ("fa_bwd.hip", "fa_common.h"),
-    "bwd_kv_blocks": ("fa_bwd.hip", "fa_common.h"),
-    "bwd_dq_convert": ("fa_bwd.hip", "fa_common.h"),
+    "bwd_dkdv": ("fa_bwd.hip", "fa_common.h"),
+    "bwd_dq": ("fa_bwd.hip", "fa_common.h"),
 }
 
 
@@ -139,6 +156,10 @@ def main():
               "has no multi-GPU path; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
     import torch
 
     sys.path.insert(0, ROOT)
@@ -166,8 +187,7 @@ def main():
     fwd()
     _, bwd_calls = binding.backward_steps(q, k, v, o, do, lse, causal=causal, scale=scale,
                                           workspace=ws, out=(dq, dk, dv))
-    stages = [("fwd", fwd)] + list(zip(("bwd_preprocess", "bwd_kv_blocks", "bwd_dq_convert"),
-                                       bwd_calls))
+    stages = [("fwd", fwd)] + list(zip(("bwd_preprocess", "bwd_dkdv", "bwd_dq"), bwd_calls))
     for _ in range(args.warmup):
         for _, f in stages:
             f()
@@ -195,13 +215,18 @@ def main():
     value = step_fl / (ms_per_step * 1e-3) / 1e12
 
     rows = B * H * N
+    # Work each kernel must do in this design.  The backward splits into a
+    # key-block kernel (S, dP, dV, dK: 8 N^2 d per head) and a query-block
+    # kernel (S, dP, dQ: 6 N^2 d per head); the metric itself counts the
+    # backward as 10 N^2 d per head (2.5x the forward), so the two kernels
+    # execute 1.4x the counted backward work.
+    half = 0.5 if causal else 1.0
     algo = {
         "fwd": ("mfma", fwd_fl),
-        "bwd_kv_blocks": ("mfma", bwd_fl),
-        # HBM-bound helpers: read O, dO (bf16) + write D and the zeroed fp32 accumulator
-        "bwd_preprocess": ("hbm", rows * d * 2 * 2 + rows * 4 + rows * d * 4),
-        # read the fp32 accumulator, write bf16 dQ
-        "bwd_dq_convert": ("hbm", rows * d * 4 + rows * d * 2),
+        "bwd_dkdv": ("mfma", 8.0 * N * N * d * B * H * half),
+        "bwd_dq": ("mfma", 6.0 * N * N * d * B * H * half),
+        # HBM-bound helper: read O, dO (bf16) and LSE, write the two padded row statistics
+        "bwd_preprocess": ("hbm", rows * d * 2 * 2 + rows * 4 + 2 * B * H * ((N + 63) // 64 * 64) * 4),
     }
     kernels = {}
     for name, ms in per.items():

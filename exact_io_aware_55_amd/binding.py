@@ -18,7 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfa.so")
 
 EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_bwd_workspace_size", "fa_bwd", "fa_bwd_preprocess",
-           "fa_bwd_kv_blocks", "fa_bwd_dq_convert", "fa_strerror")
+           "fa_bwd_dkdv", "fa_bwd_dq", "fa_strerror")
 
 FA_OK = 0
 FA_ERR_INVALID_ARG = -1
@@ -51,10 +51,10 @@ def load(path: str = LIB_PATH):
     lib.fa_bwd.restype = i
     lib.fa_bwd_preprocess.argtypes = [vp, vp, vp, i, i, i, i, vp, sz, vp]
     lib.fa_bwd_preprocess.restype = i
-    lib.fa_bwd_kv_blocks.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, sz, vp]
-    lib.fa_bwd_kv_blocks.restype = i
-    lib.fa_bwd_dq_convert.argtypes = [vp, i, i, i, i, vp, sz, vp]
-    lib.fa_bwd_dq_convert.restype = i
+    lib.fa_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, sz, vp]
+    lib.fa_bwd_dkdv.restype = i
+    lib.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, sz, vp]
+    lib.fa_bwd_dq.restype = i
     lib.fa_strerror.argtypes = [i]
     lib.fa_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -146,8 +146,8 @@ def backward_steps(q, k, v, o, do, lse, causal=False, scale=None, workspace=None
     """The same backward as :func:`backward`, issued as its three C-ABI steps.
 
     Returns ((dQ, dK, dV), calls) where ``calls`` is a list of three
-    zero-argument callables (preprocess, key blocks, dQ conversion) that
-    enqueue the steps again on the current stream, for timing."""
+    zero-argument callables (preprocess, dK/dV, dQ) that enqueue the steps
+    again on the current stream, for timing."""
     lib = load()
     B, N, H, d = _check_inputs(torch.bfloat16, q, k, v, o, do)
     need = bwd_workspace_size(B, H, N, d)
@@ -159,9 +159,10 @@ def backward_steps(q, k, v, o, do, lse, causal=False, scale=None, workspace=None
     calls = [
         lambda: _check(lib.fa_bwd_preprocess(_ptr(o), _ptr(do), _ptr(lse), B, H, N, d, _ptr(ws), nbytes,
                                              _stream())),
-        lambda: _check(lib.fa_bwd_kv_blocks(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dk), _ptr(dv),
-                                            B, H, N, d, sc, c, _ptr(ws), nbytes, _stream())),
-        lambda: _check(lib.fa_bwd_dq_convert(_ptr(dq), B, H, N, d, _ptr(ws), nbytes, _stream())),
+        lambda: _check(lib.fa_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dk), _ptr(dv),
+                                       B, H, N, d, sc, c, _ptr(ws), nbytes, _stream())),
+        lambda: _check(lib.fa_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dq), B, H, N, d, sc, c,
+                                     _ptr(ws), nbytes, _stream())),
     ]
     for call in calls:
         call()

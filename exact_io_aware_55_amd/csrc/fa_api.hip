@@ -64,14 +64,13 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
 size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
     if (check_shape(B, H, N, d, 1.0f) != FA_OK) return 0;
     const size_t stat_rows = (size_t)B * H * fa::bwd_rows_padded(N);
-    return 2 * align256(stat_rows * sizeof(float)) + align256((size_t)B * N * H * d * sizeof(float));
+    return 2 * align256(stat_rows * sizeof(float));
 }
 
 namespace {
 struct Workspace {
     float* lse2;     // LSE * log2(e), [B, H, Npad] (padding +inf)
     float* delta;    // D = rowsum(dO * O), [B, H, Npad] (padding 0)
-    float* dq_acc;   // fp32 dQ accumulator, [B, N, H, d]
 };
 
 int check_workspace(void* workspace, size_t workspace_bytes, int B, int H, int N, int d, Workspace* ws) {
@@ -82,7 +81,6 @@ int check_workspace(void* workspace, size_t workspace_bytes, int B, int H, int N
     char* w = static_cast<char*>(workspace);
     ws->lse2 = reinterpret_cast<float*>(w);
     ws->delta = reinterpret_cast<float*>(w + stat);
-    ws->dq_acc = reinterpret_cast<float*>(w + 2 * stat);
     return FA_OK;
 }
 
@@ -110,33 +108,36 @@ int fa_bwd_preprocess(const void* o, const void* dout, const float* lse, int B, 
     if ((rc = check_bwd_shape(B, H, N, d, 1.0f)) != FA_OK) return rc;
     Workspace ws;
     if ((rc = check_workspace(workspace, workspace_bytes, B, H, N, d, &ws)) != FA_OK) return rc;
-    if (fa::launch_bwd_preprocess(o, dout, lse, B, H, N, d, ws.lse2, ws.delta, ws.dq_acc, stream) != hipSuccess)
+    if (fa::launch_bwd_preprocess(o, dout, lse, B, H, N, d, ws.lse2, ws.delta, stream) != hipSuccess)
         return FA_ERR_LAUNCH;
     return FA_OK;
 }
 
-int fa_bwd_kv_blocks(const void* q, const void* k, const void* v, const void* dout, void* dk, void* dv,
-                     int B, int H, int N, int d, float scale, int causal, void* workspace,
-                     size_t workspace_bytes, hipStream_t stream) {
+int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, void* dk, void* dv, int B,
+                int H, int N, int d, float scale, int causal, void* workspace, size_t workspace_bytes,
+                hipStream_t stream) {
     int rc = all_aligned({q, k, v, dout, dk, dv});
     if (rc != FA_OK) return rc;
     if ((rc = check_bwd_shape(B, H, N, d, scale)) != FA_OK) return rc;
     Workspace ws;
     if ((rc = check_workspace(workspace, workspace_bytes, B, H, N, d, &ws)) != FA_OK) return rc;
-    if (fa::launch_bwd_kv_blocks(q, k, v, dout, dk, dv, B, H, N, d, scale, causal != 0, ws.lse2, ws.delta,
-                                 ws.dq_acc, stream) != hipSuccess)
+    if (fa::launch_bwd_dkdv(q, k, v, dout, dk, dv, B, H, N, d, scale, causal != 0, ws.lse2, ws.delta,
+                            stream) != hipSuccess)
         return FA_ERR_LAUNCH;
     return FA_OK;
 }
 
-int fa_bwd_dq_convert(void* dq, int B, int H, int N, int d, void* workspace, size_t workspace_bytes,
-                      hipStream_t stream) {
-    int rc = all_aligned({dq});
+int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, void* dq, int B, int H,
+              int N, int d, float scale, int causal, void* workspace, size_t workspace_bytes,
+              hipStream_t stream) {
+    int rc = all_aligned({q, k, v, dout, dq});
     if (rc != FA_OK) return rc;
-    if ((rc = check_bwd_shape(B, H, N, d, 1.0f)) != FA_OK) return rc;
+    if ((rc = check_bwd_shape(B, H, N, d, scale)) != FA_OK) return rc;
     Workspace ws;
     if ((rc = check_workspace(workspace, workspace_bytes, B, H, N, d, &ws)) != FA_OK) return rc;
-    if (fa::launch_bwd_dq_convert(dq, B, H, N, d, ws.dq_acc, stream) != hipSuccess) return FA_ERR_LAUNCH;
+    if (fa::launch_bwd_dq(q, k, v, dout, dq, B, H, N, d, scale, causal != 0, ws.lse2, ws.delta, stream) !=
+        hipSuccess)
+        return FA_ERR_LAUNCH;
     return FA_OK;
 }
 
@@ -151,10 +152,10 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
     if ((rc = check_workspace(workspace, workspace_bytes, B, H, N, d, &ws)) != FA_OK) return rc;
     if ((rc = fa_bwd_preprocess(o, dout, lse, B, H, N, d, workspace, workspace_bytes, stream)) != FA_OK)
         return rc;
-    if ((rc = fa_bwd_kv_blocks(q, k, v, dout, dk, dv, B, H, N, d, scale, causal, workspace,
-                               workspace_bytes, stream)) != FA_OK)
+    if ((rc = fa_bwd_dkdv(q, k, v, dout, dk, dv, B, H, N, d, scale, causal, workspace, workspace_bytes,
+                          stream)) != FA_OK)
         return rc;
-    return fa_bwd_dq_convert(dq, B, H, N, d, workspace, workspace_bytes, stream);
+    return fa_bwd_dq(q, k, v, dout, dq, B, H, N, d, scale, causal, workspace, workspace_bytes, stream);
 }
 
 const char* fa_strerror(int code) {

@@ -11,25 +11,29 @@
 // Three kernels run on the caller's stream:
 //   1. bwd_pre:  D_i = rowsum(dO * O) and LSE_i * log2(e) into per-head rows
 //      padded to a multiple of 64 (padding: D = 0, LSE = +inf, so padded
-//      queries get P = 0), and zero the fp32 dQ accumulator.
-//   2. bwd_kv:   one workgroup per block of 128 keys of one head (4 waves, one
-//      per SIMD, 32 keys each).  K and V of a wave's keys, and the K^T slice
-//      the wave needs for dQ, stay in registers.  The workgroup walks the
-//      query blocks of 64 rows that can see its keys; Q, dO and the row
-//      statistics stream into a 3-stage LDS ring by direct global -> LDS
-//      loads.  Per block it recomputes S = Q K^T and P, forms dP = dO V^T and
-//      dS, accumulates dV^T += dO^T P and dK^T += Q^T dS in registers, and
-//      adds its share of dQ = dS K into the fp32 accumulator with hardware
-//      float atomics.  Workgroups of one head start at different query
-//      blocks so their atomics and loads spread over the dQ rows.
-//   3. bwd_dq_convert: dQ accumulator (fp32) -> bf16.
+//      queries get P = 0).
+//   2. bwd_dkdv: one workgroup per block of 128 keys of one head (4 waves, one
+//      per SIMD, 32 keys each).  K and V of a wave's keys stay in registers.
+//      The workgroup walks the query blocks of 64 rows that can see its keys;
+//      Q, dO and the row statistics stream into a 3-stage LDS ring by direct
+//      global -> LDS loads.  Per block it recomputes S = Q K^T and P, forms
+//      dP = dO V^T and dS, and accumulates dV^T += dO^T P and dK^T += Q^T dS
+//      in registers.
+//   3. bwd_dq:   one workgroup per block of 256 queries (8 waves, 32 queries
+//      each, two waves per SIMD), laid out like the forward: Q and dO of a
+//      wave's queries stay in registers, K/V blocks of 64 keys stream through
+//      a 3-stage LDS ring.  Per block it recomputes S^T = K Q^T, P^T and
+//      dP^T = V dO^T (one query per lane, so LSE and D are per-lane scalars),
+//      forms dS^T and accumulates dQ^T += K^T dS^T with dS^T straight from
+//      registers.  Splitting dQ out costs two extra matrix products (S and dP
+//      are formed twice) but needs no atomics and no LDS round trip for dS,
+//      and every gradient is bitwise repeatable.
 //
-// MFMA orientation: S = Q K_w^T puts one key per lane (lane & 31) and the
-// queries in registers, so P and dS in registers are directly the B operand
-// of dV^T += dO^T P and dK^T += Q^T dS (contraction over queries).  dO^T and
-// Q^T come from the row-major tiles by transposing LDS reads
-// (ds_read_b64_tr_b16).  dS crosses lanes once: each lane writes its key's
-// column of dS^T to LDS and the dQ product reads it back transposed.
+// MFMA orientation in bwd_dkdv: S = Q K_w^T puts one key per lane (lane & 31)
+// and the queries in registers, so P and dS in registers are directly the B
+// operand of dV^T += dO^T P and dK^T += Q^T dS (contraction over queries).
+// dO^T and Q^T come from the row-major tiles by transposing LDS reads
+// (ds_read_b64_tr_b16).  In bwd_dq the transposing read gives K^T.
 #include "fa_common.h"
 #include "fa_launch.h"
 
@@ -51,7 +55,7 @@ __device__ __forceinline__ int xcd_remap_b(int bid, int nblocks) {
 }
 
 // ---------------------------------------------------------------------------
-// 1. D_i = sum_k dO_ik O_ik, LSE_i * log2(e) (padded rows), dQ accumulator := 0.
+// 1. D_i = sum_k dO_ik O_ik and LSE_i * log2(e) (padded rows).
 // Rows are enumerated in [B, H, Npad] order.
 // ---------------------------------------------------------------------------
 template <int D>
@@ -59,8 +63,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* __restrict__
                                                       const __bf16* __restrict__ dO,
                                                       const float* __restrict__ LSE,
                                                       float* __restrict__ lse2,
-                                                      float* __restrict__ delta,
-                                                      float* __restrict__ dq_acc, int H, int N,
+                                                      float* __restrict__ delta, int H, int N,
                                                       int Npad, long rows) {
     constexpr int TPR = D / 8;                 // threads per row (8 elements each)
     constexpr int RPB = 256 / TPR;             // rows per block
@@ -82,9 +85,6 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* __restrict__
             acc = __builtin_fmaf(a0, g0, acc);
             acc = __builtin_fmaf(a1, g1, acc);
         }
-        const f32x4 z = {0, 0, 0, 0};
-        *reinterpret_cast<f32x4*>(dq_acc + off) = z;
-        *reinterpret_cast<f32x4*>(dq_acc + off + 4) = z;
     }
 #pragma unroll
     for (int s = TPR / 2; s > 0; s >>= 1) acc += __shfl_xor(acc, s);
@@ -95,14 +95,14 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* __restrict__
 }
 
 // ---------------------------------------------------------------------------
-// 2. key-block kernel
+// 2. dK, dV: key-block kernel
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(bwd::NT, 1) void bwd_kv_kernel(
+__global__ __launch_bounds__(bwd::NT, 1) void bwd_dkdv_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const __bf16* __restrict__ dO, const float* __restrict__ stats, int delta_off,
-    float* __restrict__ dq_acc, __bf16* __restrict__ dK, __bf16* __restrict__ dV, int H, int N,
-    int Npad, float scale, float scale_log2, int nkb) {
+    __bf16* __restrict__ dK, __bf16* __restrict__ dV, int H, int N, int Npad, float scale,
+    float scale_log2, int nkb) {
     using namespace bwd;
     constexpr int DC = D / 16;                 // k-chunks over features
     constexpr int DT = D / 32;                 // 32-feature sub-tiles
@@ -110,15 +110,14 @@ __global__ __launch_bounds__(bwd::NT, 1) void bwd_kv_kernel(
     constexpr int SUBQ = BR * 64;              // Q/dO sub-tile: BR rows x 32 features
     constexpr int STAGE = 2 * QT + NW * 1024;  // Q, dO, one stats copy per wave
     constexpr int KVB = KB * D * 2;            // bytes of a K or V block
-    constexpr int SUBK = KB * 64;              // K/V/dS^T sub-tile: KB rows x 32 columns
+    constexpr int SUBK = KB * 64;              // K/V sub-tile: KB rows x 32 features
     constexpr int RING = NSTAGE * STAGE;
-    constexpr int DST = KB * BR * 2;           // dS^T tile
     constexpr int SEG_QO = 2 * QT / 1024 / NW; // Q + dO segments per wave per step
     constexpr int DMA_W = SEG_QO + 1;          // direct loads per wave per step
     constexpr int SEG_KV = KVB / 1024 / NW;    // K (and V) segments per wave at start
     static_assert(2 * KVB <= RING, "K/V staging fits in the ring");
     static_assert(DMA_W <= 15, "vmcnt immediate");
-    __shared__ __attribute__((aligned(1024))) char smem[RING + DST];
+    __shared__ __attribute__((aligned(1024))) char smem[RING];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hl = lane >> 5;
@@ -135,7 +134,6 @@ __global__ __launch_bounds__(bwd::NT, 1) void bwd_kv_kernel(
     const char* Kh = reinterpret_cast<const char*>(K + head_off);
     const char* Vh = reinterpret_cast<const char*>(V + head_off);
     const char* dOh = reinterpret_cast<const char*>(dO + head_off);
-    float* dQh = dq_acc + head_off;
     const unsigned lds0 = lds_offset(smem);
     const lds_char* L = as_lds(smem);
 
@@ -174,18 +172,6 @@ __global__ __launch_bounds__(bwd::NT, 1) void bwd_kv_kernel(
             kreg[c] = lds_read_b128(L + off);
             vreg[c] = lds_read_b128(L + KVB + off);
         }
-    }
-    // B operand of dQ[:, 32 dq_dt + ..] = dS K: feature column 32 dq_dt + l32,
-    // k-slots = keys in the transposing-read order (same as the dS A operand)
-    constexpr int DQT = D / 32;                // feature tiles of dQ
-    const int dq_dt = wave % DQT, dq_qt0 = wave / DQT;   // D=128: qt 0,1 ; D=64: qt = wave/2
-    constexpr int DQ_NQ = (BR / 32) * DQT / NW;          // query tiles per wave (2 or 1)
-    bf16x8 ktreg[KB / 16];
-#pragma unroll
-    for (int c = 0; c < KB / 16; ++c) {
-        const lds_char* p = L + dq_dt * SUBK + c * 16 * 64;
-        const bf16x4 lo = lds_read_tr16(p + tr0), hi = lds_read_tr16(p + tr1);
-        ktreg[c] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     }
     // the ring overwrites the K/V staging: everyone must have read it
     __builtin_amdgcn_s_waitcnt(0xC07F);        // lgkmcnt(0)
@@ -237,8 +223,6 @@ __global__ __launch_bounds__(bwd::NT, 1) void bwd_kv_kernel(
     // per-lane LDS offsets (within a stage) of the operand reads
     const int a_rd0 = l32 * 64 + ((hl ^ dual_swz(l32)) << 4);        // Q/dO rows, even c
     const int a_rd1 = l32 * 64 + (((2 + hl) ^ dual_swz(l32)) << 4);  // odd c
-    const int ds_wr = RING + key_local * 64 + (hl << 3);              // dS^T row of this key
-    const int ds_sw = dual_swz(key_local);
 
 #pragma clang loop unroll(disable)
     for (int it = 0; it < nst; ++it) {
@@ -248,6 +232,9 @@ __global__ __launch_bounds__(bwd::NT, 1) void bwd_kv_kernel(
         if (it + 2 < nst) issue_step(it + 2);
 
         const int i0 = step_of(it) * BR;
+        const bool wave_on = !CAUSAL || (k0 + wave * 32 <= i0 + BR - 1);
+        if (!wave_on) continue;                // keys all after the step's queries
+
         const lds_char* stage = L + (it % NSTAGE) * STAGE;
         const lds_char* qa0 = stage + a_rd0;
         const lds_char* qa1 = stage + a_rd1;
@@ -256,107 +243,65 @@ __global__ __launch_bounds__(bwd::NT, 1) void bwd_kv_kernel(
         const lds_char* sw = stage + 2 * QT + wave * 1024 + hl * 16;
         asm volatile("" : "+v"(qa0), "+v"(qa1), "+v"(t0), "+v"(t1), "+v"(sw));
 
-        const bool wave_on = !CAUSAL || (k0 + wave * 32 <= i0 + BR - 1);
-        if (wave_on) {
-            u32x4 pb[BR / 16], dsb[BR / 16];
-            const bool need_mask = (i0 + BR > N) || (k0 + KB > N) || (CAUSAL && k0 + KB - 1 > i0);
+        u32x4 pb[BR / 16], dsb[BR / 16];
+        const bool need_mask = (i0 + BR > N) || (k0 + KB > N) || (CAUSAL && k0 + KB - 1 > i0);
 #pragma unroll
-            for (int m = 0; m < BR / 32; ++m) {
-                // S = Q K_w^T, dP = dO V_w^T: 32 queries (registers) x 32 keys (lanes)
-                f32x16 sacc = f32x16{}, pacc = f32x16{};
+        for (int m = 0; m < BR / 32; ++m) {
+            // S = Q K_w^T, dP = dO V_w^T: 32 queries (registers) x 32 keys (lanes)
+            f32x16 sacc = f32x16{}, pacc = f32x16{};
 #pragma unroll
-                for (int c = 0; c < DC; ++c) {
-                    const lds_char* a = ((c & 1) ? qa1 : qa0) + (c >> 1) * SUBQ + m * 32 * 64;
-                    sacc = mfma32x32x16(lds_read_b128(a), kreg[c], sacc);
-                    pacc = mfma32x32x16(lds_read_b128(a + QT), vreg[c], pacc);
-                }
-                // statistics of the lane's queries 32m + 8g + 4hl + (0..3)
-                f32x4 lse4[4], dl4[4];
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    lse4[g] = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(sw + (32 * m + 8 * g) * 4);
-                    dl4[g] = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(sw + 256 + (32 * m + 8 * g) * 4);
-                }
-                float pv[16], dsv[16];
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float p = fast_exp2(__builtin_fmaf(sacc[r], scale_log2, -lse4[r >> 2][r & 3]));
-                    pv[r] = p;
-                    dsv[r] = p * (pacc[r] - dl4[r >> 2][r & 3]);
-                }
-                if (need_mask) {
-                    // query of register r = i0 + 4 hl + off, off = 32m + 8(r>>2) + (r&3)
-                    const int lim_n = N - i0 - 4 * hl;            // q < N      <=> off < lim_n
-                    const int lim_c = my_key - i0 - 4 * hl;       // key <= q   <=> off >= lim_c
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int off = 32 * m + 8 * (r >> 2) + (r & 3);
-                        const bool vis = key_ok && off < lim_n && (!CAUSAL || off >= lim_c);
-                        pv[r] = vis ? pv[r] : 0.f;
-                        dsv[r] = vis ? dsv[r] : 0.f;
-                    }
-                }
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const uint32_t p01 = pack_bf16x2(pv[4 * g], pv[4 * g + 1]);
-                    const uint32_t p23 = pack_bf16x2(pv[4 * g + 2], pv[4 * g + 3]);
-                    const uint32_t d01 = pack_bf16x2(dsv[4 * g], dsv[4 * g + 1]);
-                    const uint32_t d23 = pack_bf16x2(dsv[4 * g + 2], dsv[4 * g + 3]);
-                    pb[2 * m + (g >> 1)][2 * (g & 1)] = p01;
-                    pb[2 * m + (g >> 1)][2 * (g & 1) + 1] = p23;
-                    dsb[2 * m + (g >> 1)][2 * (g & 1)] = d01;
-                    dsb[2 * m + (g >> 1)][2 * (g & 1) + 1] = d23;
-                    // dS^T[key][queries 32m + 8g + 4hl .. +3]
-                    st_lds8(smem + ds_wr + m * SUBK + ((g ^ ds_sw) << 4), u32x2{d01, d23});
-                }
+            for (int c = 0; c < DC; ++c) {
+                const lds_char* a = ((c & 1) ? qa1 : qa0) + (c >> 1) * SUBQ + m * 32 * 64;
+                sacc = mfma32x32x16(lds_read_b128(a), kreg[c], sacc);
+                pacc = mfma32x32x16(lds_read_b128(a + QT), vreg[c], pacc);
             }
-            // dV^T += dO^T P and dK^T += Q^T dS over the step's queries
+            // statistics of the lane's queries 32m + 8g + 4hl + (0..3)
+            f32x4 lse4[4], dl4[4];
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-                for (int cq = 0; cq < BR / 16; ++cq) {
-                    const int off = dt * SUBQ + cq * 16 * 64;
-                    const bf16x8 ot = __builtin_shufflevector(lds_read_tr16(t0 + QT + off), lds_read_tr16(t1 + QT + off),
-                                                              0, 1, 2, 3, 4, 5, 6, 7);
-                    dvacc[dt] = mfma32x32x16(ot, __builtin_bit_cast(bf16x8, pb[cq]), dvacc[dt]);
-                    const bf16x8 qt = __builtin_shufflevector(lds_read_tr16(t0 + off), lds_read_tr16(t1 + off),
-                                                              0, 1, 2, 3, 4, 5, 6, 7);
-                    dkacc[dt] = mfma32x32x16(qt, __builtin_bit_cast(bf16x8, dsb[cq]), dkacc[dt]);
-                }
-        } else {
-            // keys all after the step's queries: contribute dS = 0 to dQ
-#pragma unroll
-            for (int m = 0; m < BR / 32; ++m)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) st_lds8(smem + ds_wr + m * SUBK + ((g ^ ds_sw) << 4), u32x2{0u, 0u});
-        }
-        __builtin_amdgcn_s_waitcnt(0xC07F);    // this wave's dS^T writes done
-        __builtin_amdgcn_s_barrier();          // everyone's dS^T visible
-
-        // dQ[queries 32 qt.., features 32 dq_dt..] += dS K over the block's keys
-        const lds_char* d0 = L + RING + tr0;
-        const lds_char* d1 = L + RING + tr1;
-        asm volatile("" : "+v"(d0), "+v"(d1));
-#pragma unroll
-        for (int qi = 0; qi < DQ_NQ; ++qi) {
-            const int qt = dq_qt0 + qi * (NW / DQT);
-            f32x16 acc = f32x16{};
-#pragma unroll
-            for (int c = 0; c < KB / 16; ++c) {
-                const int off = qt * SUBK + c * 16 * 64;
-                const bf16x8 dsa = __builtin_shufflevector(lds_read_tr16(d0 + off), lds_read_tr16(d1 + off),
-                                                           0, 1, 2, 3, 4, 5, 6, 7);
-                acc = mfma32x32x16(dsa, ktreg[c], acc);
+            for (int g = 0; g < 4; ++g) {
+                lse4[g] = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(sw + (32 * m + 8 * g) * 4);
+                dl4[g] = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(sw + 256 + (32 * m + 8 * g) * 4);
             }
-            // C layout: lane = feature column, registers = queries 32qt + 8(r>>2) + 4hl + (r&3)
-            const int lim_n = N - i0 - 32 * qt - 4 * hl;
-            float* dst = dQh + (long)(i0 + 32 * qt + 4 * hl) * row_stride + dq_dt * 32 + l32;
+            float pv[16], dsv[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int off = 8 * (r >> 2) + (r & 3);
-                if (off < lim_n) unsafeAtomicAdd(dst + (long)off * row_stride, acc[r] * scale);
+                const float p = fast_exp2(__builtin_fmaf(sacc[r], scale_log2, -lse4[r >> 2][r & 3]));
+                pv[r] = p;
+                dsv[r] = p * (pacc[r] - dl4[r >> 2][r & 3]);
+            }
+            if (need_mask) {
+                // query of register r = i0 + 4 hl + off, off = 32m + 8(r>>2) + (r&3)
+                const int lim_n = N - i0 - 4 * hl;            // q < N      <=> off < lim_n
+                const int lim_c = my_key - i0 - 4 * hl;       // key <= q   <=> off >= lim_c
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int off = 32 * m + 8 * (r >> 2) + (r & 3);
+                    const bool vis = key_ok && off < lim_n && (!CAUSAL || off >= lim_c);
+                    pv[r] = vis ? pv[r] : 0.f;
+                    dsv[r] = vis ? dsv[r] : 0.f;
+                }
+            }
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                pb[2 * m + (g >> 1)][2 * (g & 1)] = pack_bf16x2(pv[4 * g], pv[4 * g + 1]);
+                pb[2 * m + (g >> 1)][2 * (g & 1) + 1] = pack_bf16x2(pv[4 * g + 2], pv[4 * g + 3]);
+                dsb[2 * m + (g >> 1)][2 * (g & 1)] = pack_bf16x2(dsv[4 * g], dsv[4 * g + 1]);
+                dsb[2 * m + (g >> 1)][2 * (g & 1) + 1] = pack_bf16x2(dsv[4 * g + 2], dsv[4 * g + 3]);
             }
         }
+        // dV^T += dO^T P and dK^T += Q^T dS over the step's queries
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int cq = 0; cq < BR / 16; ++cq) {
+                const int off = dt * SUBQ + cq * 16 * 64;
+                const bf16x8 ot = __builtin_shufflevector(lds_read_tr16(t0 + QT + off), lds_read_tr16(t1 + QT + off),
+                                                          0, 1, 2, 3, 4, 5, 6, 7);
+                dvacc[dt] = mfma32x32x16(ot, __builtin_bit_cast(bf16x8, pb[cq]), dvacc[dt]);
+                const bf16x8 qt = __builtin_shufflevector(lds_read_tr16(t0 + off), lds_read_tr16(t1 + off),
+                                                          0, 1, 2, 3, 4, 5, 6, 7);
+                dkacc[dt] = mfma32x32x16(qt, __builtin_bit_cast(bf16x8, dsb[cq]), dkacc[dt]);
+            }
     }
 
     // epilogue: dK = scale * (dK^T)^T, dV; C layout of dV^T / dK^T: lane = key
@@ -381,23 +326,188 @@ __global__ __launch_bounds__(bwd::NT, 1) void bwd_kv_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// 3. dQ accumulator (fp32) -> bf16
+// 3. dQ: query-block kernel
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void bwd_dq_convert_kernel(const float* __restrict__ acc,
-                                                             __bf16* __restrict__ dq, long n8) {
-    const long i = (long)blockIdx.x * 256 + threadIdx.x;
-    if (i >= n8) return;
-    const f32x4 a = *reinterpret_cast<const f32x4*>(acc + i * 8);
-    const f32x4 c = *reinterpret_cast<const f32x4*>(acc + i * 8 + 4);
-    *reinterpret_cast<u32x4*>(dq + i * 8) =
-        u32x4{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(c[0], c[1]), pack_bf16x2(c[2], c[3])};
+namespace bwdq {
+constexpr int BR = 256;      // queries per workgroup (8 waves x 32)
+constexpr int BC = 64;       // keys per K/V block
+constexpr int NT = 512;
+constexpr int NW = 8;
+constexpr int NSTAGE = 3;
+}  // namespace bwdq
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(bwdq::NT, 1) void bwd_dq_kernel(
+    const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
+    const __bf16* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ delta,
+    __bf16* __restrict__ dQ, int H, int N, int Npad, float scale, float scale_log2, int nqb) {
+    using namespace bwdq;
+    constexpr int DC = D / 16;
+    constexpr int DT = D / 32;
+    constexpr int TILE = BC * D * 2;           // one K or V block
+    constexpr int STAGE = 2 * TILE;
+    constexpr int SUB = BC * 64;               // sub-tile: BC rows x 32 features
+    constexpr int SEGS = TILE / 1024;
+    constexpr int SEG_W = SEGS / NW;           // segments per wave per tensor
+    constexpr int SEG_SUB = SUB / 1024;
+    static_assert(SEGS % NW == 0, "segments per wave");
+    __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * STAGE];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, hl = lane >> 5;
+    const int tg = lane >> 4, tj = lane & 15;
+
+    const int logical = xcd_remap_b(blockIdx.x, gridDim.x);
+    const int bh = logical / nqb;
+    int qb = logical - bh * nqb;
+    if (CAUSAL) qb = nqb - 1 - qb;             // longest rows first
+    const int b = bh / H, h = bh - b * H;
+    const int row_stride = H * D;
+    const unsigned row_bytes = (unsigned)row_stride * 2u;
+    const long head_off = ((long)b * N * H + h) * D;
+    const char* Kh = reinterpret_cast<const char*>(K + head_off);
+    const char* Vh = reinterpret_cast<const char*>(V + head_off);
+    const unsigned lds0 = lds_offset(smem);
+    const lds_char* L = as_lds(smem);
+
+    const int q0 = qb * BR;
+    const int qw = q0 + wave * 32;
+    const int my_q = qw + l32;
+    const int q_rd = min(my_q, N - 1);         // rows past N: finite data, never stored
+
+    const int kv_end = CAUSAL ? min(N, q0 + BR) : N;
+    const int ntiles = (kv_end + BC - 1) / BC;
+
+    int ld_row[SEG_W], ld_col[SEG_W];
+#pragma unroll
+    for (int i = 0; i < SEG_W; ++i) {
+        const int seg = wave * SEG_W + i;
+        const int sub = seg / SEG_SUB, r = (seg % SEG_SUB) * 16 + (lane >> 2);
+        ld_row[i] = r;
+        ld_col[i] = sub * 64 + (((lane & 3) ^ dual_swz(r)) << 4);
+    }
+    auto issue_tile = [&](int t) {
+        const int j0 = t * BC;
+        const unsigned kb = lds0 + (t % NSTAGE) * STAGE;
+#pragma unroll
+        for (int i = 0; i < SEG_W; ++i) {
+            const int seg = wave * SEG_W + i;
+            const unsigned go = (unsigned)min(j0 + ld_row[i], N - 1) * row_bytes + ld_col[i];
+            dma16(Kh, go, __builtin_amdgcn_readfirstlane(kb + seg * 1024));
+            dma16(Vh, go, __builtin_amdgcn_readfirstlane(kb + TILE + seg * 1024));
+        }
+    };
+    issue_tile(0);
+    if (ntiles > 1) issue_tile(1);
+
+    // this lane's query: Q and dO as B operands (features 16c + 8hl ..), LSE, D
+    bf16x8 qreg[DC], oreg[DC];
+    {
+        const __bf16* qs = Q + head_off + (long)q_rd * row_stride + 8 * hl;
+        const __bf16* os = dO + head_off + (long)q_rd * row_stride + 8 * hl;
+#pragma unroll
+        for (int c = 0; c < DC; ++c) {
+            qreg[c] = as_bf16x8(ld_global16(qs + 16 * c));
+            oreg[c] = as_bf16x8(ld_global16(os + 16 * c));
+        }
+    }
+    float lq = lse2[(long)bh * Npad + q_rd];
+    float dq_row = delta[(long)bh * Npad + q_rd];
+    // consume the loads here so no wait for them lands inside the loop
+#pragma unroll
+    for (int c = 0; c < DC; ++c) asm volatile("" : "+v"(qreg[c]), "+v"(oreg[c]));
+    asm volatile("" : "+v"(lq), "+v"(dq_row));
+
+    f32x16 dqacc[DT];
+#pragma unroll
+    for (int i = 0; i < DT; ++i) dqacc[i] = f32x16{};
+
+    const int a_rd0 = l32 * 64 + ((hl ^ dual_swz(l32)) << 4);        // K/V rows, even c
+    const int a_rd1 = l32 * 64 + (((2 + hl) ^ dual_swz(l32)) << 4);  // odd c
+    const int tr_r0 = 4 * (tg >> 1) + (tj >> 2), tr_r1 = tr_r0 + 8;
+    const int tr_cl = 2 * (tg & 1) + ((tj & 3) >> 1);
+    const int tr0 = tr_r0 * 64 + ((tr_cl ^ dual_swz(tr_r0)) << 4) + ((tj & 1) << 3);
+    const int tr1 = tr_r1 * 64 + ((tr_cl ^ dual_swz(tr_r1)) << 4) + ((tj & 1) << 3);
+
+#pragma clang loop unroll(disable)
+    for (int t = 0; t < ntiles; ++t) {
+        if (t + 1 < ntiles) FA_WAIT_VMCNT(2 * SEG_W);
+        else FA_WAIT_VMCNT(0);
+        __builtin_amdgcn_s_barrier();
+        if (t + 2 < ntiles) issue_tile(t + 2);
+
+        const int j0 = t * BC;
+        const bool wave_active = !CAUSAL || j0 <= qw + 31;
+        if (wave_active) {
+            const lds_char* stage = L + (t % NSTAGE) * STAGE;
+            const lds_char* ka0 = stage + a_rd0;
+            const lds_char* ka1 = stage + a_rd1;
+            const lds_char* kt0 = stage + tr0;
+            const lds_char* kt1 = stage + tr1;
+            asm volatile("" : "+v"(ka0), "+v"(ka1), "+v"(kt0), "+v"(kt1));
+            // S^T = K Q^T and dP^T = V dO^T for two 32-key tiles (lane = query)
+            f32x16 s[2], dp[2];
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+                s[kt] = f32x16{};
+                dp[kt] = f32x16{};
+#pragma unroll
+                for (int c = 0; c < DC; ++c) {
+                    const lds_char* a = ((c & 1) ? ka1 : ka0) + (c >> 1) * SUB + kt * 32 * 64;
+                    s[kt] = mfma32x32x16(lds_read_b128(a), qreg[c], s[kt]);
+                    dp[kt] = mfma32x32x16(lds_read_b128(a + TILE), oreg[c], dp[kt]);
+                }
+            }
+            // dS^T = P^T (dP^T - D), P^T = exp2(S^T scale log2e - LSE log2e)
+            u32x4 dsb[4];
+            const bool need_mask = (j0 + BC > N) || (CAUSAL && j0 + BC - 1 > qw);
+            const int lim_n = N - j0 - 4 * hl;        // key = j0 + 4hl + off: key < N <=> off < lim_n
+            const int lim_c = my_q - j0 - 4 * hl;     // causal: key <= q <=> off <= lim_c
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int r = 0; r < 16; r += 2) {
+                    float d0 = fast_exp2(__builtin_fmaf(s[kt][r], scale_log2, -lq)) * (dp[kt][r] - dq_row);
+                    float d1 = fast_exp2(__builtin_fmaf(s[kt][r + 1], scale_log2, -lq)) * (dp[kt][r + 1] - dq_row);
+                    if (need_mask) {
+                        const int o0 = kt * 32 + (r >> 2) * 8 + (r & 3);
+                        d0 = (o0 < lim_n && (!CAUSAL || o0 <= lim_c)) ? d0 : 0.f;
+                        d1 = (o0 + 1 < lim_n && (!CAUSAL || o0 + 1 <= lim_c)) ? d1 : 0.f;
+                    }
+                    dsb[kt * 2 + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(d0, d1);
+                }
+            // dQ^T += K^T dS^T; A operand = K^T from the row-major K block
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int cc = 0; cc < 4; ++cc) {
+                    const int off = dt * SUB + cc * 16 * 64;
+                    const bf16x8 ka = __builtin_shufflevector(lds_read_tr16(kt0 + off), lds_read_tr16(kt1 + off),
+                                                              0, 1, 2, 3, 4, 5, 6, 7);
+                    dqacc[dt] = mfma32x32x16(ka, __builtin_bit_cast(bf16x8, dsb[cc]), dqacc[dt]);
+                }
+        }
+    }
+
+    // epilogue: dQ = scale * dQ^T^T -> bf16; lane = query, registers = features
+    if (my_q < N) {
+        __bf16* dst = dQ + head_off + (long)my_q * row_stride;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d = dt * 32 + g * 8 + hl * 4;
+                *reinterpret_cast<u32x2*>(dst + d) =
+                    u32x2{pack_bf16x2(dqacc[dt][g * 4] * scale, dqacc[dt][g * 4 + 1] * scale),
+                          pack_bf16x2(dqacc[dt][g * 4 + 2] * scale, dqacc[dt][g * 4 + 3] * scale)};
+            }
+    }
 }
 
 int bwd_rows_padded(int N) { return (N + bwd::ROWPAD - 1) / bwd::ROWPAD * bwd::ROWPAD; }
 
 hipError_t launch_bwd_preprocess(const void* o, const void* dout, const float* lse, int B, int H,
-                                 int N, int d, float* lse2, float* delta, float* dq_acc,
-                                 hipStream_t stream) {
+                                 int N, int d, float* lse2, float* delta, hipStream_t stream) {
     auto Op = static_cast<const __bf16*>(o);
     auto dOp = static_cast<const __bf16*>(dout);
     const int Npad = bwd_rows_padded(N);
@@ -405,16 +515,15 @@ hipError_t launch_bwd_preprocess(const void* o, const void* dout, const float* l
     const int rpb = 256 / (d / 8);
     const dim3 grid((unsigned)((rows + rpb - 1) / rpb));
     if (d == 128)
-        hipLaunchKernelGGL((bwd_pre_kernel<128>), grid, dim3(256), 0, stream, Op, dOp, lse, lse2, delta, dq_acc, H, N, Npad, rows);
+        hipLaunchKernelGGL((bwd_pre_kernel<128>), grid, dim3(256), 0, stream, Op, dOp, lse, lse2, delta, H, N, Npad, rows);
     else
-        hipLaunchKernelGGL((bwd_pre_kernel<64>), grid, dim3(256), 0, stream, Op, dOp, lse, lse2, delta, dq_acc, H, N, Npad, rows);
+        hipLaunchKernelGGL((bwd_pre_kernel<64>), grid, dim3(256), 0, stream, Op, dOp, lse, lse2, delta, H, N, Npad, rows);
     return hipGetLastError();
 }
 
-hipError_t launch_bwd_kv_blocks(const void* q, const void* k, const void* v, const void* dout,
-                                void* dk, void* dv, int B, int H, int N, int d, float scale,
-                                bool causal, const float* lse2, const float* delta, float* dq_acc,
-                                hipStream_t stream) {
+hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, void* dk,
+                           void* dv, int B, int H, int N, int d, float scale, bool causal,
+                           const float* lse2, const float* delta, hipStream_t stream) {
     auto Qp = static_cast<const __bf16*>(q);
     auto Kp = static_cast<const __bf16*>(k);
     auto Vp = static_cast<const __bf16*>(v);
@@ -426,9 +535,9 @@ hipError_t launch_bwd_kv_blocks(const void* q, const void* k, const void* v, con
     const dim3 grid((unsigned)(B * H * nkb)), block(bwd::NT);
     const float sl2 = scale * kLog2e;
     const int delta_off = (int)((const char*)delta - (const char*)lse2);
-#define FA_BWD_LAUNCH(DD, CC)                                                                      \
-    hipLaunchKernelGGL((bwd_kv_kernel<DD, CC>), grid, block, 0, stream, Qp, Kp, Vp, dOp, lse2,    \
-                       delta_off, dq_acc, dKp, dVp, H, N, Npad, scale, sl2, nkb)
+#define FA_BWD_LAUNCH(DD, CC)                                                                        \
+    hipLaunchKernelGGL((bwd_dkdv_kernel<DD, CC>), grid, block, 0, stream, Qp, Kp, Vp, dOp, lse2,    \
+                       delta_off, dKp, dVp, H, N, Npad, scale, sl2, nkb)
     if (d == 128) {
         if (causal) FA_BWD_LAUNCH(128, true);
         else FA_BWD_LAUNCH(128, false);
@@ -440,11 +549,29 @@ hipError_t launch_bwd_kv_blocks(const void* q, const void* k, const void* v, con
     return hipGetLastError();
 }
 
-hipError_t launch_bwd_dq_convert(void* dq, int B, int H, int N, int d, const float* dq_acc,
-                                 hipStream_t stream) {
-    const long n8 = (long)B * N * H * d / 8;
-    hipLaunchKernelGGL(bwd_dq_convert_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream,
-                       dq_acc, static_cast<__bf16*>(dq), n8);
+hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dout, void* dq,
+                         int B, int H, int N, int d, float scale, bool causal, const float* lse2,
+                         const float* delta, hipStream_t stream) {
+    auto Qp = static_cast<const __bf16*>(q);
+    auto Kp = static_cast<const __bf16*>(k);
+    auto Vp = static_cast<const __bf16*>(v);
+    auto dOp = static_cast<const __bf16*>(dout);
+    auto dQp = static_cast<__bf16*>(dq);
+    const int Npad = bwd_rows_padded(N);
+    const int nqb = (N + bwdq::BR - 1) / bwdq::BR;
+    const dim3 grid((unsigned)(B * H * nqb)), block(bwdq::NT);
+    const float sl2 = scale * kLog2e;
+#define FA_BWDQ_LAUNCH(DD, CC)                                                                      \
+    hipLaunchKernelGGL((bwd_dq_kernel<DD, CC>), grid, block, 0, stream, Qp, Kp, Vp, dOp, lse2,     \
+                       delta, dQp, H, N, Npad, scale, sl2, nqb)
+    if (d == 128) {
+        if (causal) FA_BWDQ_LAUNCH(128, true);
+        else FA_BWDQ_LAUNCH(128, false);
+    } else {
+        if (causal) FA_BWDQ_LAUNCH(64, true);
+        else FA_BWDQ_LAUNCH(64, false);
+    }
+#undef FA_BWDQ_LAUNCH
     return hipGetLastError();
 }
 

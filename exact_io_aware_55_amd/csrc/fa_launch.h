@@ -13,19 +13,17 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B,
                           int H, int N, int d, float scale, bool causal, hipStream_t stream);
 
-// Backward steps: row statistics (padded D and LSE * log2 e) and the
-// dQ-accumulator zero fill; the key-block kernel (dK, dV, atomic dQ); the
-// dQ fp32 -> bf16 conversion.  Row statistics are padded per head to
-// bwd_rows_padded(N) rows.
+// Backward steps: row statistics (padded D and LSE * log2 e); the
+// key-block kernel (dK, dV); the query-block kernel (dQ).  Row statistics are
+// padded per head to bwd_rows_padded(N) rows.
 int bwd_rows_padded(int N);
 hipError_t launch_bwd_preprocess(const void* o, const void* dout, const float* lse, int B, int H,
-                                 int N, int d, float* lse2, float* delta, float* dq_acc,
-                                 hipStream_t stream);
-hipError_t launch_bwd_kv_blocks(const void* q, const void* k, const void* v, const void* dout,
-                                void* dk, void* dv, int B, int H, int N, int d, float scale,
-                                bool causal, const float* lse2, const float* delta, float* dq_acc,
-                                hipStream_t stream);
-hipError_t launch_bwd_dq_convert(void* dq, int B, int H, int N, int d, const float* dq_acc,
-                                 hipStream_t stream);
+                                 int N, int d, float* lse2, float* delta, hipStream_t stream);
+hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, void* dk,
+                           void* dv, int B, int H, int N, int d, float scale, bool causal,
+                           const float* lse2, const float* delta, hipStream_t stream);
+hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dout, void* dq,
+                         int B, int H, int N, int d, float scale, bool causal, const float* lse2,
+                         const float* delta, hipStream_t stream);
 
 }  // namespace fa

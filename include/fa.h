@@ -78,8 +78,8 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
 
 /* Bytes of device workspace fa_bwd needs for this shape (0 if the shape is
  * invalid).  It holds two fp32 row statistics per head, padded to a multiple
- * of 64 rows ([B,H,Npad]: LSE * log2(e) and D = rowsum(dO * O)), and an fp32
- * dQ accumulator [B,N,H,d], each 256-byte aligned. */
+ * of 64 rows ([B,H,Npad]: LSE * log2(e) and D = rowsum(dO * O)), each
+ * 256-byte aligned. */
 size_t fa_bwd_workspace_size(int B, int H, int N, int d);
 
 /* bf16 backward with recomputation.  q, k, v, o, dout: bf16 [B,N,H,d]
@@ -93,28 +93,29 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* The three steps fa_bwd runs, exported separately so a caller can schedule
- * or time them individually.  All share fa_bwd's workspace layout and must
- * run in this order on one stream for one backward:
+ * or time them individually.  They share fa_bwd's workspace; the first must
+ * complete (same stream) before either of the others:
  *   fa_bwd_preprocess: D_i = sum_k dO_ik O_ik and LSE_i * log2(e) into the
- *                      workspace, and zero the fp32 dQ accumulator.  D is the
- *                      softmax-Jacobian term of the backward (not on the
- *                      pages, which only require recomputation).
- *   fa_bwd_kv_blocks:  for each block of keys, walk the query blocks that can
- *                      see them, recompute P = exp(scale QK^T - LSE), and form
- *                      dV, dK (written as bf16) and the block's contribution to
- *                      dQ (added to the fp32 accumulator with float atomics,
- *                      so dQ is not bitwise repeatable; dK and dV are).
- *   fa_bwd_dq_convert: dQ = bf16(accumulator).
- * Arguments have the meaning and layout given for fa_bwd.  Backward calls
- * also require B * H * Npad < 2^28 (Npad = N rounded up to a multiple of 64),
- * else FA_ERR_UNSUPPORTED. */
+ *                      workspace.  D is the softmax-Jacobian term of the
+ *                      backward (not on the pages, which only require
+ *                      recomputation).
+ *   fa_bwd_dkdv:       for each block of 128 keys, walk the query blocks that
+ *                      can see them, recompute P = exp(scale QK^T - LSE) and
+ *                      dS, and write dK and dV (bf16).
+ *   fa_bwd_dq:         for each block of 256 queries, walk the key blocks it
+ *                      can see, recompute P and dS, and write dQ (bf16).
+ * Every output is written once by one workgroup (no atomics), so all three
+ * gradients are bitwise repeatable.  Arguments have the meaning and layout
+ * given for fa_bwd.  Backward calls also require B * H * Npad < 2^28
+ * (Npad = N rounded up to a multiple of 64), else FA_ERR_UNSUPPORTED. */
 int fa_bwd_preprocess(const void* o, const void* dout, const float* lse, int B, int H, int N,
                       int d, void* workspace, size_t workspace_bytes, hipStream_t stream);
-int fa_bwd_kv_blocks(const void* q, const void* k, const void* v, const void* dout,
-                     void* dk, void* dv, int B, int H, int N, int d, float scale, int causal,
-                     void* workspace, size_t workspace_bytes, hipStream_t stream);
-int fa_bwd_dq_convert(void* dq, int B, int H, int N, int d, void* workspace,
-                      size_t workspace_bytes, hipStream_t stream);
+int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
+                void* dk, void* dv, int B, int H, int N, int d, float scale, int causal,
+                void* workspace, size_t workspace_bytes, hipStream_t stream);
+int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, void* dq,
+              int B, int H, int N, int d, float scale, int causal,
+              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Human-readable text for a return code (static storage). */
 const char* fa_strerror(int code);

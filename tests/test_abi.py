@@ -70,9 +70,9 @@ def test_workspace_size(lib):
     def want(B, H, N, d):
         a256 = lambda x: (x + 255) // 256 * 256
         npad = (N + 63) // 64 * 64
-        return 2 * a256(B * H * npad * 4) + a256(B * N * H * d * 4)
+        return 2 * a256(B * H * npad * 4)
     assert lib.fa_bwd_workspace_size(4, 16, 4096, 64) == want(4, 16, 4096, 64)
-    assert lib.fa_bwd_workspace_size(1, 1, 7, 128) == want(1, 1, 7, 128) == 2 * 256 + 3584
+    assert lib.fa_bwd_workspace_size(1, 1, 7, 128) == want(1, 1, 7, 128) == 2 * 256
     assert lib.fa_bwd_workspace_size(0, 1, 8, 64) == 0
     assert lib.fa_bwd_workspace_size(1, 1, 8, 80) == 0
 
@@ -111,7 +111,7 @@ def test_backward_step_argument_errors(lib):
     assert f(*ok3, 1, 1, 8, 96, V(FAKE), 1 << 20, None) == binding.FA_ERR_UNSUPPORTED
     assert f(*ok3, 1, 1, 8, 64, V(FAKE), 16, None) == binding.FA_ERR_WORKSPACE
     assert f(*ok3, 1 << 12, 1 << 8, 1 << 9, 64, V(FAKE), 1 << 20, None) == binding.FA_ERR_UNSUPPORTED
-    g = lib.fa_bwd_kv_blocks
+    g = lib.fa_bwd_dkdv
     ok = [V(FAKE)] * 6
     assert g(*ok, 1, 1, 8, 64, float("inf"), 0, V(FAKE), 1 << 20, None) == binding.FA_ERR_INVALID_ARG
     assert g(*ok, 1, 0, 8, 64, 0.1, 0, V(FAKE), 1 << 20, None) == binding.FA_ERR_INVALID_ARG
@@ -119,9 +119,11 @@ def test_backward_step_argument_errors(lib):
     bad = list(ok)
     bad[4] = V(FAKE + 8)
     assert g(*bad, 1, 1, 8, 64, 0.1, 0, V(FAKE), 1 << 20, None) == binding.FA_ERR_MISALIGNED
-    h = lib.fa_bwd_dq_convert
-    assert h(None, 1, 1, 8, 64, V(FAKE), 1 << 20, None) == binding.FA_ERR_INVALID_ARG
-    assert h(V(FAKE), 1, 1, 8, 64, V(FAKE + 128), 1 << 20, None) == binding.FA_ERR_WORKSPACE
+    q = lib.fa_bwd_dq
+    ok5 = [V(FAKE)] * 5
+    assert q(None, *ok5[1:], 1, 1, 8, 64, 0.1, 0, V(FAKE), 1 << 20, None) == binding.FA_ERR_INVALID_ARG
+    assert q(*ok5, 1, 1, 8, 64, 0.1, 0, V(FAKE + 128), 1 << 20, None) == binding.FA_ERR_WORKSPACE
+    assert q(*ok5, 1, 1, 8, 32, 0.1, 0, V(FAKE), 1 << 20, None) == binding.FA_ERR_UNSUPPORTED
 
 
 def test_missing_library_fails_loudly(tmp_path):
