@@ -29,9 +29,17 @@ FLAGS = [
 ]
 
 
+# Per-source extra flags.  The backward kernels run one wave per SIMD (512
+# registers); for such kernels the compiler would otherwise put every MFMA
+# result in accumulation registers and copy the score tiles back for the
+# softmax, so the backward forces the VGPR form of MFMA.
+EXTRA = {"fa_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-c", src, "-o", obj]
+    extra = EXTRA.get(os.path.basename(src), [])
+    cmd = [HIPCC, *FLAGS, *extra, "-I", os.path.join(ROOT, "include"), "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{res.stdout}\n{res.stderr}")
