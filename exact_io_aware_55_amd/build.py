@@ -29,11 +29,9 @@ FLAGS = [
 ]
 
 
-# Per-source extra flags.  The backward kernels run one wave per SIMD (512
-# registers); for such kernels the compiler would otherwise put every MFMA
-# result in accumulation registers and copy the score tiles back for the
-# softmax, so the backward forces the VGPR form of MFMA.
-EXTRA = {"fa_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Per-source extra flags (none at present: each kernel's launch bounds decide
+# whether its MFMA results live in VGPRs or in accumulation registers).
+EXTRA = {}
 
 
 def _compile(src: str) -> str:

@@ -98,7 +98,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* __restrict__
 // 2. dK, dV: key-block kernel
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(bwd::NT, 1) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(bwd::NT, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const __bf16* __restrict__ dO, const float* __restrict__ stats, int delta_off,
     __bf16* __restrict__ dK, __bf16* __restrict__ dV, int H, int N, int Npad, float scale,
@@ -243,65 +243,115 @@ __global__ __launch_bounds__(bwd::NT, 1) void bwd_dkdv_kernel(
         const lds_char* sw = stage + 2 * QT + wave * 1024 + hl * 16;
         asm volatile("" : "+v"(qa0), "+v"(qa1), "+v"(t0), "+v"(t1), "+v"(sw));
 
-        u32x4 pb[BR / 16], dsb[BR / 16];
         const bool need_mask = (i0 + BR > N) || (k0 + KB > N) || (CAUSAL && k0 + KB - 1 > i0);
-#pragma unroll
-        for (int m = 0; m < BR / 32; ++m) {
-            // S = Q K_w^T, dP = dO V_w^T: 32 queries (registers) x 32 keys (lanes)
-            f32x16 sacc = f32x16{}, pacc = f32x16{};
-#pragma unroll
-            for (int c = 0; c < DC; ++c) {
-                const lds_char* a = ((c & 1) ? qa1 : qa0) + (c >> 1) * SUBQ + m * 32 * 64;
-                sacc = mfma32x32x16(lds_read_b128(a), kreg[c], sacc);
-                pacc = mfma32x32x16(lds_read_b128(a + QT), vreg[c], pacc);
-            }
-            // statistics of the lane's queries 32m + 8g + 4hl + (0..3)
-            f32x4 lse4[4], dl4[4];
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                lse4[g] = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(sw + (32 * m + 8 * g) * 4);
-                dl4[g] = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(sw + 256 + (32 * m + 8 * g) * 4);
-            }
-            float pv[16], dsv[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float p = fast_exp2(__builtin_fmaf(sacc[r], scale_log2, -lse4[r >> 2][r & 3]));
-                pv[r] = p;
-                dsv[r] = p * (pacc[r] - dl4[r >> 2][r & 3]);
-            }
-            if (need_mask) {
-                // query of register r = i0 + 4 hl + off, off = 32m + 8(r>>2) + (r&3)
-                const int lim_n = N - i0 - 4 * hl;            // q < N      <=> off < lim_n
-                const int lim_c = my_key - i0 - 4 * hl;       // key <= q   <=> off >= lim_c
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int off = 32 * m + 8 * (r >> 2) + (r & 3);
-                    const bool vis = key_ok && off < lim_n && (!CAUSAL || off >= lim_c);
-                    pv[r] = vis ? pv[r] : 0.f;
-                    dsv[r] = vis ? dsv[r] : 0.f;
+        // One step, software-pipelined by hand.  With one wave per SIMD
+        // nothing else hides LDS latency, so the step is cut into NU units of
+        // two MFMAs each; the operand reads of unit u + PF and the statistics
+        // of a later softmax chunk are issued in unit u, and the softmax of one
+        // 32-query half runs in pieces beside the products of the next units.
+        // Scheduling fences between units keep the compiler from sinking the
+        // reads back next to their MFMAs.
+        //   units 0 .. DC-1:        S/dP of queries 0..31   (one chunk c each)
+        //   units DC .. 2DC-1:      S/dP of queries 32..63
+        //   units 2DC .. NU-1:      dV^T/dK^T, query chunk cq major, feature tile dt
+        //   softmax of half 0 in units DC+1 .. 2DC, of half 1 in 2DC+1 .. 3DC,
+        //   DC chunks of RC = 16/DC registers each
+        // masking: the query of register r of half m is i0 + 4 hl + 32m + 8(r>>2) + (r&3);
+        // it must be < N, and >= the lane's key when causal; keys past N see nothing
+        const int lim_n = key_ok ? N - i0 - 4 * hl : 0;
+        const int lim_c = my_key - i0 - 4 * hl;
+        auto body = [&](auto masked) {
+            constexpr bool MASK = decltype(masked)::value;
+            constexpr int NS = 2 * DC;                 // S/dP units
+            constexpr int NU = NS + 4 * DT;            // all units
+            constexpr int PF = D == 64 ? 1 : 2;        // prefetch distance in units
+            constexpr int RC = 16 / DC;                // softmax registers per chunk
+            static_assert(3 * DC <= NU, "softmax chunks fit in the step");
+            bf16x8 opa[NU], opb[NU];                   // operands of each unit
+            f32x4 lse4[2][4], dl4[2][4];
+            f32x16 sacc[2], pacc[2];
+            u32x4 pb[BR / 16], dsb[BR / 16];
+            auto issue_reads = [&](auto ucon) {
+                constexpr int u = decltype(ucon)::value;
+                if constexpr (u < NS) {
+                    constexpr int m = u / DC, c = u % DC;
+                    const lds_char* a = ((c & 1) ? qa1 : qa0) + (c >> 1) * SUBQ + m * 32 * 64;
+                    opa[u] = lds_read_b128(a);
+                    opb[u] = lds_read_b128(a + QT);
+                } else if constexpr (u < NU) {
+                    constexpr int cq = (u - NS) / DT, dt = (u - NS) % DT;
+                    constexpr int off = dt * SUBQ + cq * 16 * 64;
+                    opa[u] = __builtin_shufflevector(lds_read_tr16(t0 + QT + off), lds_read_tr16(t1 + QT + off),
+                                                     0, 1, 2, 3, 4, 5, 6, 7);
+                    opb[u] = __builtin_shufflevector(lds_read_tr16(t0 + off), lds_read_tr16(t1 + off),
+                                                     0, 1, 2, 3, 4, 5, 6, 7);
                 }
-            }
+                // statistics of the softmax chunk that runs in unit u
+                constexpr int m = u <= 2 * DC ? 0 : 1;
+                constexpr int ch = u - (m == 0 ? DC + 1 : 2 * DC + 1);
+                if constexpr (ch >= 0 && ch < DC && (ch * RC) % 4 == 0) {
+                    constexpr int g = ch * RC / 4;
+                    lse4[m][g] = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(sw + (32 * m + 8 * g) * 4);
+                    dl4[m][g] = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(sw + 256 + (32 * m + 8 * g) * 4);
+                }
+            };
+            auto softmax_chunk = [&](auto ucon) {
+                constexpr int u = decltype(ucon)::value;
+                constexpr int m = u <= 2 * DC ? 0 : 1;
+                constexpr int ch = u - (m == 0 ? DC + 1 : 2 * DC + 1);
+                if constexpr (ch >= 0 && ch < DC) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                pb[2 * m + (g >> 1)][2 * (g & 1)] = pack_bf16x2(pv[4 * g], pv[4 * g + 1]);
-                pb[2 * m + (g >> 1)][2 * (g & 1) + 1] = pack_bf16x2(pv[4 * g + 2], pv[4 * g + 3]);
-                dsb[2 * m + (g >> 1)][2 * (g & 1)] = pack_bf16x2(dsv[4 * g], dsv[4 * g + 1]);
-                dsb[2 * m + (g >> 1)][2 * (g & 1) + 1] = pack_bf16x2(dsv[4 * g + 2], dsv[4 * g + 3]);
-            }
-        }
-        // dV^T += dO^T P and dK^T += Q^T dS over the step's queries
+                    for (int j = 0; j < RC; j += 2) {
+                        const int r = ch * RC + j;     // registers r, r + 1
+                        float pv[2], dsv[2];
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int cq = 0; cq < BR / 16; ++cq) {
-                const int off = dt * SUBQ + cq * 16 * 64;
-                const bf16x8 ot = __builtin_shufflevector(lds_read_tr16(t0 + QT + off), lds_read_tr16(t1 + QT + off),
-                                                          0, 1, 2, 3, 4, 5, 6, 7);
-                dvacc[dt] = mfma32x32x16(ot, __builtin_bit_cast(bf16x8, pb[cq]), dvacc[dt]);
-                const bf16x8 qt = __builtin_shufflevector(lds_read_tr16(t0 + off), lds_read_tr16(t1 + off),
-                                                          0, 1, 2, 3, 4, 5, 6, 7);
-                dkacc[dt] = mfma32x32x16(qt, __builtin_bit_cast(bf16x8, dsb[cq]), dkacc[dt]);
-            }
+                        for (int e = 0; e < 2; ++e) {
+                            const int rr = r + e;
+                            float x = __builtin_fmaf(sacc[m][rr], scale_log2, -lse4[m][rr >> 2][rr & 3]);
+                            if constexpr (MASK) {
+                                // hidden pairs get exp2(-inf) = 0, and so dS = 0 as dP is finite
+                                const int off = 32 * m + 8 * (rr >> 2) + (rr & 3);
+                                const bool vis = (off < lim_n) & (!CAUSAL | (off >= lim_c));
+                                x = vis ? x : -INFINITY;
+                            }
+                            const float p = fast_exp2(x);
+                            pv[e] = p;
+                            dsv[e] = p * (pacc[m][rr] - dl4[m][rr >> 2][rr & 3]);
+                        }
+                        const int g = r >> 2;
+                        pb[2 * m + (g >> 1)][2 * (g & 1) + ((r >> 1) & 1)] = pack_bf16x2(pv[0], pv[1]);
+                        dsb[2 * m + (g >> 1)][2 * (g & 1) + ((r >> 1) & 1)] = pack_bf16x2(dsv[0], dsv[1]);
+                    }
+                }
+            };
+            auto products = [&](auto ucon) {
+                constexpr int u = decltype(ucon)::value;
+                if constexpr (u < NS) {
+                    constexpr int m = u / DC, c = u % DC;
+                    if constexpr (c == 0) {
+                        sacc[m] = f32x16{};
+                        pacc[m] = f32x16{};
+                    }
+                    sacc[m] = mfma32x32x16(opa[u], kreg[c], sacc[m]);
+                    pacc[m] = mfma32x32x16(opb[u], vreg[c], pacc[m]);
+                } else {
+                    constexpr int cq = (u - NS) / DT, dt = (u - NS) % DT;
+                    dvacc[dt] = mfma32x32x16(opa[u], __builtin_bit_cast(bf16x8, pb[cq]), dvacc[dt]);
+                    dkacc[dt] = mfma32x32x16(opb[u], __builtin_bit_cast(bf16x8, dsb[cq]), dkacc[dt]);
+                }
+            };
+            static_for<PF>([&](auto u) { issue_reads(u); });
+            __builtin_amdgcn_sched_barrier(0);
+            static_for<NU>([&](auto u) {
+                constexpr int uu = decltype(u)::value;
+                issue_reads(flag_int<uu + PF>{});
+                softmax_chunk(u);
+                products(u);
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        };
+        if (need_mask) body(flag_t<true>{});
+        else body(flag_t<false>{});
     }
 
     // epilogue: dK = scale * (dK^T)^T, dV; C layout of dV^T / dK^T: lane = key
