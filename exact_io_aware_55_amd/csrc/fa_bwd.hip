@@ -243,7 +243,15 @@ __global__ __launch_bounds__(bwd::NT, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
         const lds_char* sw = stage + 2 * QT + wave * 1024 + hl * 16;
         asm volatile("" : "+v"(qa0), "+v"(qa1), "+v"(t0), "+v"(t1), "+v"(sw));
 
-        const bool need_mask = (i0 + BR > N) || (k0 + KB > N) || (CAUSAL && k0 + KB - 1 > i0);
+        // Masking.  Queries past N need none: their padded statistics
+        // (LSE = +inf, D = 0) give P = 0 and dS = 0.  Keys past N need none
+        // either: column j of dV^T and dK^T only depends on column j of P and
+        // dS, and those columns are never stored.  So only the causal mask
+        // remains: the query of register r of half m, i0 + 4 hl + 32m +
+        // 8(r>>2) + (r&3), must not precede the lane's key.  It is applied on
+        // every step, as a second copy of the step for the diagonal blocks
+        // would cost more in register moves than the compares.
+        const int lim_c = my_key - i0 - 4 * hl;
         // One step, software-pipelined by hand.  With one wave per SIMD
         // nothing else hides LDS latency, so the step is cut into NU units of
         // two MFMAs each; the operand reads of unit u + PF and the statistics
@@ -256,10 +264,6 @@ __global__ __launch_bounds__(bwd::NT, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
         //   units 2DC .. NU-1:      dV^T/dK^T, query chunk cq major, feature tile dt
         //   softmax of half 0 in units DC+1 .. 2DC, of half 1 in 2DC+1 .. 3DC,
         //   DC chunks of RC = 16/DC registers each
-        // masking: the query of register r of half m is i0 + 4 hl + 32m + 8(r>>2) + (r&3);
-        // it must be < N, and >= the lane's key when causal; keys past N see nothing
-        const int lim_n = key_ok ? N - i0 - 4 * hl : 0;
-        const int lim_c = my_key - i0 - 4 * hl;
         auto body = [&](auto masked) {
             constexpr bool MASK = decltype(masked)::value;
             constexpr int NS = 2 * DC;                 // S/dP units
@@ -311,7 +315,7 @@ __global__ __launch_bounds__(bwd::NT, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
                             if constexpr (MASK) {
                                 // hidden pairs get exp2(-inf) = 0, and so dS = 0 as dP is finite
                                 const int off = 32 * m + 8 * (rr >> 2) + (rr & 3);
-                                const bool vis = (off < lim_n) & (!CAUSAL | (off >= lim_c));
+                                const bool vis = off >= lim_c;
                                 x = vis ? x : -INFINITY;
                             }
                             const float p = fast_exp2(x);
@@ -350,8 +354,7 @@ __global__ __launch_bounds__(bwd::NT, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
                 __builtin_amdgcn_sched_barrier(0);
             });
         };
-        if (need_mask) body(flag_t<true>{});
-        else body(flag_t<false>{});
+        body(flag_t<CAUSAL>{});
     }
 
     // epilogue: dK = scale * (dK^T)^T, dV; C layout of dV^T / dK^T: lane = key

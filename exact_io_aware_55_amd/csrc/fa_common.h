@@ -30,14 +30,6 @@ __device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b,
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Scheduling groups: the machine scheduler emits the groups of one basic
-// block in the order of these calls (instruction classes of the AMDGPU
-// IGroupLP mutation).
-#define FA_SG_VALU 0x002
-#define FA_SG_MFMA 0x008
-#define FA_SG_DS_READ 0x100
-#define FA_SCHED_GROUP(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
-
 // compile-time constants for generic lambdas
 template <bool B>
 struct flag_t {
