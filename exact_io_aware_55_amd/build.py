@@ -29,9 +29,11 @@ FLAGS = [
 ]
 
 
-# Per-source extra flags (none at present: each kernel's launch bounds decide
-# whether its MFMA results live in VGPRs or in accumulation registers).
-EXTRA = {}
+# Per-source extra flags.  The backward kernels keep their score tiles in
+# VGPRs: without this flag the compiler would put every MFMA result of a
+# one-wave-per-SIMD kernel in AGPRs and copy the tiles back for the softmax.
+# (The d = 128 dK/dV accumulators are placed in AGPRs explicitly.)
+EXTRA = {"fa_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:

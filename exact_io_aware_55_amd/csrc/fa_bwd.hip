@@ -48,6 +48,17 @@ constexpr int NSTAGE = 3;    // query blocks resident in the LDS ring
 constexpr int ROWPAD = 64;   // row-statistic padding (= BR)
 }  // namespace bwd
 
+// acc += a * b on a 32x32x16 bf16 MFMA with the accumulator held in AGPRs.
+// The backward at d = 128 keeps dV^T and dK^T (128 registers) there so that
+// the VGPRs stay free for the score tiles; written as inline assembly because
+// the compiler otherwise picks one register form for all MFMAs of a kernel.
+// Callers must leave the MFMA result latency (the accumulators are only read
+// after the main loop) and must not feed it VGPRs written by the two preceding
+// VALU instructions.
+__device__ __forceinline__ void mfma_acc(f32x16& acc, const bf16x8& a, const u32x4& b) {
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
 __device__ __forceinline__ int xcd_remap_b(int bid, int nblocks) {
     const int per = nblocks >> 3, rem = nblocks & 7;
     const int x = bid & 7, i = bid >> 3;
@@ -117,9 +128,12 @@ __global__ __launch_bounds__(bwd::NT, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     constexpr int SEG_KV = KVB / 1024 / NW;    // K (and V) segments per wave at start
     static_assert(2 * KVB <= RING, "K/V staging fits in the ring");
     static_assert(DMA_W <= 15, "vmcnt immediate");
-    __shared__ __attribute__((aligned(1024))) char smem[RING];
+    // the ring, then 1 KB that absorbs the direct loads of the steps past the
+    // last one (every step issues the same loads, so no branch is needed)
+    __shared__ __attribute__((aligned(1024))) char smem[RING + 1024];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, hl = lane >> 5;
     const int tg = lane >> 4, tj = lane & 15;  // transposing-read group and lane
 
@@ -134,7 +148,7 @@ __global__ __launch_bounds__(bwd::NT, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     const char* Kh = reinterpret_cast<const char*>(K + head_off);
     const char* Vh = reinterpret_cast<const char*>(V + head_off);
     const char* dOh = reinterpret_cast<const char*>(dO + head_off);
-    const unsigned lds0 = lds_offset(smem);
+    const unsigned lds0 = __builtin_amdgcn_readfirstlane(lds_offset(smem));
     const lds_char* L = as_lds(smem);
 
     const int k0 = kb * KB;
@@ -199,19 +213,37 @@ __global__ __launch_bounds__(bwd::NT, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
         ld_c[i] = sub * 64 + (((lane & 3) ^ dual_swz(r)) << 4);
     }
     const unsigned st_lane = (unsigned)((bh * Npad + 4 * (lane & 15)) * 4 + ((lane & 16) ? delta_off : 0));
-    auto issue_step = [&](int it) {
-        const int i0 = step_of(it) * BR;
-        const unsigned base = lds0 + (it % NSTAGE) * STAGE;
-#pragma unroll
-        for (int i = 0; i < SEG_QO; ++i) {
-            const int seg = wave * SEG_QO + i;
-            const unsigned go = (unsigned)min(i0 + ld_r[i], N - 1) * row_bytes + ld_c[i];
-            dma16(seg < QT / 1024 ? Qh : dOh, go, __builtin_amdgcn_readfirstlane(base + seg * 1024));
-        }
-        dma16(stats, st_lane + i0 * 4, __builtin_amdgcn_readfirstlane(base + 2 * QT + wave * 1024));
+    // Direct loads of step `it`: where they go (uniform) and load i of them.  A
+    // step past the last one reloads step 0 into the spare kilobyte instead.
+    struct StepLoads {
+        unsigned lds;                          // LDS byte offset of segment 0
+        unsigned seg;                          // LDS stride per segment (0: spare)
+        int i0;                                // first query row
     };
-    if (nst > 0) issue_step(0);
-    if (nst > 1) issue_step(1);
+    auto step_loads = [&](int it) {
+        const bool real = it < nst;
+        StepLoads sl;
+        sl.lds = (unsigned)__builtin_amdgcn_readfirstlane(real ? lds0 + (it % NSTAGE) * STAGE : lds0 + RING);
+        sl.seg = real ? 1024u : 0u;
+        sl.i0 = __builtin_amdgcn_readfirstlane(step_of(real ? it : 0) * BR);
+        return sl;
+    };
+    auto issue_load = [&](const StepLoads& sl, int i) {
+        if (i < SEG_QO) {
+            const int seg = wave * SEG_QO + i;
+            const unsigned go = (unsigned)min(sl.i0 + ld_r[i], N - 1) * row_bytes + ld_c[i];
+            dma16(seg < QT / 1024 ? Qh : dOh, go, sl.lds + seg * sl.seg);
+        } else {
+            dma16(stats, st_lane + sl.i0 * 4, sl.lds + (2 * QT / 1024 + wave) * sl.seg);
+        }
+    };
+    {
+        const StepLoads s0 = step_loads(0), s1 = step_loads(1);
+#pragma unroll
+        for (int i = 0; i < DMA_W; ++i) issue_load(s0, i);
+#pragma unroll
+        for (int i = 0; i < DMA_W; ++i) issue_load(s1, i);
+    }
 
     f32x16 dvacc[DT], dkacc[DT];
 #pragma unroll
@@ -226,14 +258,14 @@ __global__ __launch_bounds__(bwd::NT, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
 
 #pragma clang loop unroll(disable)
     for (int it = 0; it < nst; ++it) {
-        if (it + 1 < nst) FA_WAIT_VMCNT(DMA_W);
-        else FA_WAIT_VMCNT(0);
+        // this step's loads are done once at most one step's loads are in
+        // flight; after the barrier nobody reads the stage of step it - 1,
+        // which the loads of step it + 2 (spread over the units below) refill
+        FA_WAIT_VMCNT(DMA_W);
         __builtin_amdgcn_s_barrier();
-        if (it + 2 < nst) issue_step(it + 2);
 
         const int i0 = step_of(it) * BR;
-        const bool wave_on = !CAUSAL || (k0 + wave * 32 <= i0 + BR - 1);
-        if (!wave_on) continue;                // keys all after the step's queries
+        const StepLoads next = step_loads(it + 2);
 
         const lds_char* stage = L + (it % NSTAGE) * STAGE;
         const lds_char* qa0 = stage + a_rd0;
@@ -268,7 +300,7 @@ __global__ __launch_bounds__(bwd::NT, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
             constexpr bool MASK = decltype(masked)::value;
             constexpr int NS = 2 * DC;                 // S/dP units
             constexpr int NU = NS + 4 * DT;            // all units
-            constexpr int PF = D == 64 ? 1 : 2;        // prefetch distance in units
+            constexpr int PF = D == 64 ? 1 : 3;        // prefetch distance in units
             constexpr int RC = 16 / DC;                // softmax registers per chunk
             static_assert(3 * DC <= NU, "softmax chunks fit in the step");
             bf16x8 opa[NU], opb[NU];                   // operands of each unit
@@ -340,8 +372,13 @@ __global__ __launch_bounds__(bwd::NT, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
                     pacc[m] = mfma32x32x16(opb[u], vreg[c], pacc[m]);
                 } else {
                     constexpr int cq = (u - NS) / DT, dt = (u - NS) % DT;
-                    dvacc[dt] = mfma32x32x16(opa[u], __builtin_bit_cast(bf16x8, pb[cq]), dvacc[dt]);
-                    dkacc[dt] = mfma32x32x16(opb[u], __builtin_bit_cast(bf16x8, dsb[cq]), dkacc[dt]);
+                    if constexpr (D == 128) {
+                        mfma_acc(dvacc[dt], opa[u], pb[cq]);
+                        mfma_acc(dkacc[dt], opb[u], dsb[cq]);
+                    } else {
+                        dvacc[dt] = mfma32x32x16(opa[u], __builtin_bit_cast(bf16x8, pb[cq]), dvacc[dt]);
+                        dkacc[dt] = mfma32x32x16(opb[u], __builtin_bit_cast(bf16x8, dsb[cq]), dkacc[dt]);
+                    }
                 }
             };
             static_for<PF>([&](auto u) { issue_reads(u); });
@@ -349,6 +386,8 @@ __global__ __launch_bounds__(bwd::NT, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
             static_for<NU>([&](auto u) {
                 constexpr int uu = decltype(u)::value;
                 issue_reads(flag_int<uu + PF>{});
+                // the direct loads of step it + 2, one every other unit
+                if constexpr (uu % 2 == 1 && uu / 2 < DMA_W) issue_load(next, uu / 2);
                 softmax_chunk(u);
                 products(u);
                 __builtin_amdgcn_sched_barrier(0);
@@ -356,6 +395,10 @@ __global__ __launch_bounds__(bwd::NT, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
         };
         body(flag_t<CAUSAL>{});
     }
+    FA_WAIT_VMCNT(0);                          // the loads past the last step
+    // the accumulators are read below by VALU after MFMAs the compiler does
+    // not see (inline assembly): wait out the MFMA result latency
+    asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
 
     // epilogue: dK = scale * (dK^T)^T, dV; C layout of dV^T / dK^T: lane = key
     // column, registers = feature rows 8g + 4h + t
