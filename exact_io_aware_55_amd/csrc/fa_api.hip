@@ -70,7 +70,7 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int d) {
 namespace {
 struct Workspace {
     float* lse2;     // LSE * log2(e), [B, H, Npad] (padding +inf)
-    float* delta;    // D = rowsum(dO * O), [B, H, Npad] (padding 0)
+    float* delta;    // -D, D = rowsum(dO * O), [B, H, Npad] (padding 0)
 };
 
 int check_workspace(void* workspace, size_t workspace_bytes, int B, int H, int N, int d, Workspace* ws) {
@@ -97,6 +97,9 @@ int check_bwd_shape(int B, int H, int N, int d, float scale) {
     const int rc = check_shape(B, H, N, d, scale);
     if (rc != FA_OK) return rc;
     if ((long long)B * H * fa::bwd_rows_padded(N) >= (1LL << 28)) return FA_ERR_UNSUPPORTED;
+    // byte offsets of rows up to N + 255 (tiles overhanging the last row,
+    // which read zeros through a range-checked load) must not wrap 32 bits
+    if ((long long)(N + 256) * H * d * 2 >= (1LL << 32)) return FA_ERR_UNSUPPORTED;
     return FA_OK;
 }
 }  // namespace

@@ -9,7 +9,7 @@
 //   dQ = scale dS K,  dK = scale dS^T Q.
 //
 // Three kernels run on the caller's stream:
-//   1. bwd_pre:  D_i = rowsum(dO * O) and LSE_i * log2(e) into per-head rows
+//   1. bwd_pre:  -D_i = -rowsum(dO * O) and LSE_i * log2(e) into per-head rows
 //      padded to a multiple of 64 (padding: D = 0, LSE = +inf, so padded
 //      queries get P = 0).
 //   2. bwd_dkdv: one workgroup per block of 128 keys of one head (4 waves, one
@@ -66,7 +66,7 @@ __device__ __forceinline__ int xcd_remap_b(int bid, int nblocks) {
 }
 
 // ---------------------------------------------------------------------------
-// 1. D_i = sum_k dO_ik O_ik and LSE_i * log2(e) (padded rows).
+// 1. -D_i = -sum_k dO_ik O_ik and LSE_i * log2(e) (padded rows).
 // Rows are enumerated in [B, H, Npad] order.
 // ---------------------------------------------------------------------------
 template <int D>
@@ -100,7 +100,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* __restrict__
 #pragma unroll
     for (int s = TPR / 2; s > 0; s >>= 1) acc += __shfl_xor(acc, s);
     if (row < rows && part == 0) {
-        delta[row] = live ? acc : 0.f;
+        delta[row] = live ? -acc : 0.f;       // stored negated: it seeds dP
         lse2[row] = live ? LSE[bh * N + i] * kLog2e : INFINITY;
     }
 }
@@ -150,6 +150,10 @@ __global__ __launch_bounds__(bwd::NT, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     const char* dOh = reinterpret_cast<const char*>(dO + head_off);
     const unsigned lds0 = __builtin_amdgcn_readfirstlane(lds_offset(smem));
     const lds_char* L = as_lds(smem);
+    // byte range of one head's rows: loads of rows past N read zeros
+    const unsigned head_bytes = (unsigned)(N - 1) * row_bytes + 2 * D;
+    const __amdgpu_buffer_rsrc_t rQ = byte_rsrc(Qh, head_bytes), rdO = byte_rsrc(dOh, head_bytes);
+    const __amdgpu_buffer_rsrc_t rK = byte_rsrc(Kh, head_bytes), rV = byte_rsrc(Vh, head_bytes);
 
     const int k0 = kb * KB;
     const int key_local = wave * 32 + l32;
@@ -169,9 +173,10 @@ __global__ __launch_bounds__(bwd::NT, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     for (int i = 0; i < SEG_KV; ++i) {
         const int seg = wave * SEG_KV + i;
         const int sub = seg / (SUBK / 1024), r = (seg % (SUBK / 1024)) * 16 + (lane >> 2);
-        const unsigned go = (unsigned)min(k0 + r, N - 1) * row_bytes + sub * 64 + (((lane & 3) ^ dual_swz(r)) << 4);
-        dma16(Kh, go, __builtin_amdgcn_readfirstlane(lds0 + seg * 1024));
-        dma16(Vh, go, __builtin_amdgcn_readfirstlane(lds0 + KVB + seg * 1024));
+        // keys past N load as zeros; their columns of dK and dV are never stored
+        const unsigned go = (unsigned)(k0 + r) * row_bytes + sub * 64 + (((lane & 3) ^ dual_swz(r)) << 4);
+        dma16_buf(rK, go, lds0 + seg * 1024);
+        dma16_buf(rV, go, lds0 + KVB + seg * 1024);
     }
     FA_WAIT_VMCNT(0);
     __builtin_amdgcn_s_barrier();
@@ -202,15 +207,15 @@ __global__ __launch_bounds__(bwd::NT, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
         return first + s;
     };
 
-    // direct loads of one step: SEG_QO segments of Q/dO per wave + the stats
-    int ld_r[SEG_QO], ld_c[SEG_QO];
+    // direct loads of one step: SEG_QO segments of Q/dO per wave + the stats;
+    // ld_off: byte offset of the lane's 16 bytes relative to the step's first row
+    unsigned ld_off[SEG_QO];
 #pragma unroll
     for (int i = 0; i < SEG_QO; ++i) {
         const int seg = wave * SEG_QO + i;
         const int sseg = seg % (QT / 1024);
         const int sub = sseg / (SUBQ / 1024), r = (sseg % (SUBQ / 1024)) * 16 + (lane >> 2);
-        ld_r[i] = r;
-        ld_c[i] = sub * 64 + (((lane & 3) ^ dual_swz(r)) << 4);
+        ld_off[i] = (unsigned)r * row_bytes + sub * 64 + (((lane & 3) ^ dual_swz(r)) << 4);
     }
     const unsigned st_lane = (unsigned)((bh * Npad + 4 * (lane & 15)) * 4 + ((lane & 16) ? delta_off : 0));
     // Direct loads of step `it`: where they go (uniform) and load i of them.  A
@@ -219,6 +224,7 @@ __global__ __launch_bounds__(bwd::NT, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
         unsigned lds;                          // LDS byte offset of segment 0
         unsigned seg;                          // LDS stride per segment (0: spare)
         int i0;                                // first query row
+        unsigned row0;                         // its byte offset in the head
     };
     auto step_loads = [&](int it) {
         const bool real = it < nst;
@@ -226,13 +232,13 @@ __global__ __launch_bounds__(bwd::NT, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
         sl.lds = (unsigned)__builtin_amdgcn_readfirstlane(real ? lds0 + (it % NSTAGE) * STAGE : lds0 + RING);
         sl.seg = real ? 1024u : 0u;
         sl.i0 = __builtin_amdgcn_readfirstlane(step_of(real ? it : 0) * BR);
+        sl.row0 = (unsigned)sl.i0 * row_bytes;
         return sl;
     };
     auto issue_load = [&](const StepLoads& sl, int i) {
         if (i < SEG_QO) {
             const int seg = wave * SEG_QO + i;
-            const unsigned go = (unsigned)min(sl.i0 + ld_r[i], N - 1) * row_bytes + ld_c[i];
-            dma16(seg < QT / 1024 ? Qh : dOh, go, sl.lds + seg * sl.seg);
+            dma16_buf(seg < QT / 1024 ? rQ : rdO, sl.row0 + ld_off[i], sl.lds + seg * sl.seg);
         } else {
             dma16(stats, st_lane + sl.i0 * 4, sl.lds + (2 * QT / 1024 + wave) * sl.seg);
         }
@@ -309,6 +315,13 @@ __global__ __launch_bounds__(bwd::NT, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
             u32x4 pb[BR / 16], dsb[BR / 16];
             auto issue_reads = [&](auto ucon) {
                 constexpr int u = decltype(ucon)::value;
+                if constexpr (u < NS && u % DC == 0) {
+                    // -D of half u / DC, in the C layout: it seeds dP's accumulator
+#pragma unroll
+                    for (int g = 0; g < 4; ++g)
+                        dl4[u / DC][g] = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
+                            sw + 256 + (32 * (u / DC) + 8 * g) * 4);
+                }
                 if constexpr (u < NS) {
                     constexpr int m = u / DC, c = u % DC;
                     const lds_char* a = ((c & 1) ? qa1 : qa0) + (c >> 1) * SUBQ + m * 32 * 64;
@@ -322,13 +335,12 @@ __global__ __launch_bounds__(bwd::NT, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
                     opb[u] = __builtin_shufflevector(lds_read_tr16(t0 + off), lds_read_tr16(t1 + off),
                                                      0, 1, 2, 3, 4, 5, 6, 7);
                 }
-                // statistics of the softmax chunk that runs in unit u
+                // LSE of the softmax chunk that runs in unit u
                 constexpr int m = u <= 2 * DC ? 0 : 1;
                 constexpr int ch = u - (m == 0 ? DC + 1 : 2 * DC + 1);
                 if constexpr (ch >= 0 && ch < DC && (ch * RC) % 4 == 0) {
                     constexpr int g = ch * RC / 4;
                     lse4[m][g] = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(sw + (32 * m + 8 * g) * 4);
-                    dl4[m][g] = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(sw + 256 + (32 * m + 8 * g) * 4);
                 }
             };
             auto softmax_chunk = [&](auto ucon) {
@@ -352,7 +364,7 @@ __global__ __launch_bounds__(bwd::NT, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
                             }
                             const float p = fast_exp2(x);
                             pv[e] = p;
-                            dsv[e] = p * (pacc[m][rr] - dl4[m][rr >> 2][rr & 3]);
+                            dsv[e] = p * pacc[m][rr];      // pacc = dP - D
                         }
                         const int g = r >> 2;
                         pb[2 * m + (g >> 1)][2 * (g & 1) + ((r >> 1) & 1)] = pack_bf16x2(pv[0], pv[1]);
@@ -366,7 +378,10 @@ __global__ __launch_bounds__(bwd::NT, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
                     constexpr int m = u / DC, c = u % DC;
                     if constexpr (c == 0) {
                         sacc[m] = f32x16{};
-                        pacc[m] = f32x16{};
+                        pacc[m] = __builtin_shufflevector(
+                            __builtin_shufflevector(dl4[m][0], dl4[m][1], 0, 1, 2, 3, 4, 5, 6, 7),
+                            __builtin_shufflevector(dl4[m][2], dl4[m][3], 0, 1, 2, 3, 4, 5, 6, 7),
+                            0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
                     }
                     sacc[m] = mfma32x32x16(opa[u], kreg[c], sacc[m]);
                     pacc[m] = mfma32x32x16(opb[u], vreg[c], pacc[m]);
@@ -508,7 +523,7 @@ __global__ __launch_bounds__(bwdq::NT, 1) void bwd_dq_kernel(
         }
     }
     float lq = lse2[(long)bh * Npad + q_rd];
-    float dq_row = delta[(long)bh * Npad + q_rd];
+    float dq_row = delta[(long)bh * Npad + q_rd];  // -D of this lane's query
     // consume the loads here so no wait for them lands inside the loop
 #pragma unroll
     for (int c = 0; c < DC; ++c) asm volatile("" : "+v"(qreg[c]), "+v"(oreg[c]));
@@ -563,8 +578,8 @@ __global__ __launch_bounds__(bwdq::NT, 1) void bwd_dq_kernel(
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
                 for (int r = 0; r < 16; r += 2) {
-                    float d0 = fast_exp2(__builtin_fmaf(s[kt][r], scale_log2, -lq)) * (dp[kt][r] - dq_row);
-                    float d1 = fast_exp2(__builtin_fmaf(s[kt][r + 1], scale_log2, -lq)) * (dp[kt][r + 1] - dq_row);
+                    float d0 = fast_exp2(__builtin_fmaf(s[kt][r], scale_log2, -lq)) * (dp[kt][r] + dq_row);
+                    float d1 = fast_exp2(__builtin_fmaf(s[kt][r + 1], scale_log2, -lq)) * (dp[kt][r + 1] + dq_row);
                     if (need_mask) {
                         const int o0 = kt * 32 + (r >> 2) * 8 + (r & 3);
                         d0 = (o0 < lim_n && (!CAUSAL || o0 <= lim_c)) ? d0 : 0.f;

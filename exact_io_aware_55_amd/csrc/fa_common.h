@@ -30,6 +30,20 @@ __device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b,
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// 16-byte direct load through a buffer resource (buffer_load_dwordx4 ... lds):
+// as dma16, but the offset is checked against the resource's byte range and
+// lanes outside it read zeros, so tiles past the last row need no clamping.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t byte_rsrc(const void* base, unsigned bytes) {
+    // raw buffer: stride 0, range in bytes, 32-bit data format
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t rsrc, unsigned offset, unsigned lds_base) {
+    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(offset), "s"(rsrc), "s"(lds_base)
+                 : "memory", "m0");
+}
+
 // compile-time constants for generic lambdas
 template <bool B>
 struct flag_t {

@@ -78,8 +78,8 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
 
 /* Bytes of device workspace fa_bwd needs for this shape (0 if the shape is
  * invalid).  It holds two fp32 row statistics per head, padded to a multiple
- * of 64 rows ([B,H,Npad]: LSE * log2(e) and D = rowsum(dO * O)), each
- * 256-byte aligned. */
+ * of 64 rows ([B,H,Npad]: LSE * log2(e) and -D with D = rowsum(dO * O)),
+ * each 256-byte aligned. */
 size_t fa_bwd_workspace_size(int B, int H, int N, int d);
 
 /* bf16 backward with recomputation.  q, k, v, o, dout: bf16 [B,N,H,d]
@@ -95,7 +95,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
 /* The three steps fa_bwd runs, exported separately so a caller can schedule
  * or time them individually.  They share fa_bwd's workspace; the first must
  * complete (same stream) before either of the others:
- *   fa_bwd_preprocess: D_i = sum_k dO_ik O_ik and LSE_i * log2(e) into the
+ *   fa_bwd_preprocess: -D_i = -sum_k dO_ik O_ik and LSE_i * log2(e) into the
  *                      workspace.  D is the softmax-Jacobian term of the
  *                      backward (not on the pages, which only require
  *                      recomputation).
@@ -107,7 +107,8 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
  * Every output is written once by one workgroup (no atomics), so all three
  * gradients are bitwise repeatable.  Arguments have the meaning and layout
  * given for fa_bwd.  Backward calls also require B * H * Npad < 2^28
- * (Npad = N rounded up to a multiple of 64), else FA_ERR_UNSUPPORTED. */
+ * (Npad = N rounded up to a multiple of 64) and (N + 256) * H * d * 2 < 2^32,
+ * else FA_ERR_UNSUPPORTED. */
 int fa_bwd_preprocess(const void* o, const void* dout, const float* lse, int B, int H, int N,
                       int d, void* workspace, size_t workspace_bytes, hipStream_t stream);
 int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,

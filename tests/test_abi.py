@@ -119,6 +119,8 @@ def test_backward_step_argument_errors(lib):
     bad = list(ok)
     bad[4] = V(FAKE + 8)
     assert g(*bad, 1, 1, 8, 64, 0.1, 0, V(FAKE), 1 << 20, None) == binding.FA_ERR_MISALIGNED
+    # row byte offsets up to N + 256 must fit 32 bits (here 257 rows of 2^24 bytes)
+    assert g(*ok, 1, 1 << 16, 1, 128, 0.1, 0, V(FAKE), 1 << 30, None) == binding.FA_ERR_UNSUPPORTED
     q = lib.fa_bwd_dq
     ok5 = [V(FAKE)] * 5
     assert q(None, *ok5[1:], 1, 1, 8, 64, 0.1, 0, V(FAKE), 1 << 20, None) == binding.FA_ERR_INVALID_ARG
