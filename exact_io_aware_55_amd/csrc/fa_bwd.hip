@@ -462,9 +462,13 @@ __global__ __launch_bounds__(bwdq::NT, 1) void bwd_dq_kernel(
     constexpr int SEG_W = SEGS / NW;           // segments per wave per tensor
     constexpr int SEG_SUB = SUB / 1024;
     static_assert(SEGS % NW == 0, "segments per wave");
-    __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * STAGE];
+    static_assert(2 * SEG_W <= 15, "vmcnt immediate");
+    // the ring, then 1 KB that absorbs the direct loads of tiles past the last
+    // one (every tile issues the same loads, so no branch is needed)
+    __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * STAGE + 1024];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, hl = lane >> 5;
     const int tg = lane >> 4, tj = lane & 15;
 
@@ -476,10 +480,13 @@ __global__ __launch_bounds__(bwdq::NT, 1) void bwd_dq_kernel(
     const int row_stride = H * D;
     const unsigned row_bytes = (unsigned)row_stride * 2u;
     const long head_off = ((long)b * N * H + h) * D;
-    const char* Kh = reinterpret_cast<const char*>(K + head_off);
-    const char* Vh = reinterpret_cast<const char*>(V + head_off);
-    const unsigned lds0 = lds_offset(smem);
+    const unsigned lds0 = __builtin_amdgcn_readfirstlane(lds_offset(smem));
     const lds_char* L = as_lds(smem);
+    // K and V rows past N load as zeros: such a key then adds dS * 0 to dQ,
+    // so ragged tails need no mask
+    const unsigned head_bytes = (unsigned)(N - 1) * row_bytes + 2 * D;
+    const __amdgpu_buffer_rsrc_t rK = byte_rsrc(K + head_off, head_bytes);
+    const __amdgpu_buffer_rsrc_t rV = byte_rsrc(V + head_off, head_bytes);
 
     const int q0 = qb * BR;
     const int qw = q0 + wave * 32;
@@ -488,28 +495,32 @@ __global__ __launch_bounds__(bwdq::NT, 1) void bwd_dq_kernel(
 
     const int kv_end = CAUSAL ? min(N, q0 + BR) : N;
     const int ntiles = (kv_end + BC - 1) / BC;
+    // tiles every query of the workgroup sees whole; causal tiles after them
+    // straddle some wave's diagonal and are masked
+    const int nfull = CAUSAL ? min(ntiles, (q0 + 1) / BC) : ntiles;
 
-    int ld_row[SEG_W], ld_col[SEG_W];
+    unsigned ld_off[SEG_W];                    // lane's bytes relative to the tile's first row
 #pragma unroll
     for (int i = 0; i < SEG_W; ++i) {
         const int seg = wave * SEG_W + i;
         const int sub = seg / SEG_SUB, r = (seg % SEG_SUB) * 16 + (lane >> 2);
-        ld_row[i] = r;
-        ld_col[i] = sub * 64 + (((lane & 3) ^ dual_swz(r)) << 4);
+        ld_off[i] = (unsigned)r * row_bytes + sub * 64 + (((lane & 3) ^ dual_swz(r)) << 4);
     }
+    // direct loads of tile t (a tile past the last one goes to the spare KB)
     auto issue_tile = [&](int t) {
-        const int j0 = t * BC;
-        const unsigned kb = lds0 + (t % NSTAGE) * STAGE;
+        const bool real = t < ntiles;
+        const unsigned kb = __builtin_amdgcn_readfirstlane(real ? lds0 + (t % NSTAGE) * STAGE : lds0 + NSTAGE * STAGE);
+        const unsigned segb = real ? 1024u : 0u;
+        const unsigned row0 = (unsigned)(real ? t * BC : 0) * row_bytes;
 #pragma unroll
         for (int i = 0; i < SEG_W; ++i) {
             const int seg = wave * SEG_W + i;
-            const unsigned go = (unsigned)min(j0 + ld_row[i], N - 1) * row_bytes + ld_col[i];
-            dma16(Kh, go, __builtin_amdgcn_readfirstlane(kb + seg * 1024));
-            dma16(Vh, go, __builtin_amdgcn_readfirstlane(kb + TILE + seg * 1024));
+            dma16_buf(rK, row0 + ld_off[i], kb + seg * segb);
+            dma16_buf(rV, row0 + ld_off[i], kb + (TILE / 1024 + seg) * segb);
         }
     };
     issue_tile(0);
-    if (ntiles > 1) issue_tile(1);
+    issue_tile(1);
 
     // this lane's query: Q and dO as B operands (features 16c + 8hl ..), LSE, D
     bf16x8 qreg[DC], oreg[DC];
@@ -540,65 +551,71 @@ __global__ __launch_bounds__(bwdq::NT, 1) void bwd_dq_kernel(
     const int tr0 = tr_r0 * 64 + ((tr_cl ^ dual_swz(tr_r0)) << 4) + ((tj & 1) << 3);
     const int tr1 = tr_r1 * 64 + ((tr_cl ^ dual_swz(tr_r1)) << 4) + ((tj & 1) << 3);
 
-#pragma clang loop unroll(disable)
-    for (int t = 0; t < ntiles; ++t) {
-        if (t + 1 < ntiles) FA_WAIT_VMCNT(2 * SEG_W);
-        else FA_WAIT_VMCNT(0);
+    // one K/V tile: wait for its loads, start those of tile t + 2, then
+    // S^T = K Q^T, dP^T = V dO^T (lane = query), dS^T, dQ^T += K^T dS^T
+    auto tile = [&](int t, auto masked) {
+        constexpr bool MASK = decltype(masked)::value;
+        FA_WAIT_VMCNT(2 * SEG_W);
         __builtin_amdgcn_s_barrier();
-        if (t + 2 < ntiles) issue_tile(t + 2);
+        issue_tile(t + 2);
 
         const int j0 = t * BC;
-        const bool wave_active = !CAUSAL || j0 <= qw + 31;
-        if (wave_active) {
-            const lds_char* stage = L + (t % NSTAGE) * STAGE;
-            const lds_char* ka0 = stage + a_rd0;
-            const lds_char* ka1 = stage + a_rd1;
-            const lds_char* kt0 = stage + tr0;
-            const lds_char* kt1 = stage + tr1;
-            asm volatile("" : "+v"(ka0), "+v"(ka1), "+v"(kt0), "+v"(kt1));
-            // S^T = K Q^T and dP^T = V dO^T for two 32-key tiles (lane = query)
-            f32x16 s[2], dp[2];
+        if (MASK && j0 > qw + 31) return;      // every key after this wave's queries
+        const lds_char* stage = L + (t % NSTAGE) * STAGE;
+        const lds_char* ka0 = stage + a_rd0;
+        const lds_char* ka1 = stage + a_rd1;
+        const lds_char* kt0 = stage + tr0;
+        const lds_char* kt1 = stage + tr1;
+        asm volatile("" : "+v"(ka0), "+v"(ka1), "+v"(kt0), "+v"(kt1));
+        f32x16 s[2], dp[2];
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
-                s[kt] = f32x16{};
-                dp[kt] = f32x16{};
+        for (int kt = 0; kt < 2; ++kt) {
+            s[kt] = f32x16{};
+            dp[kt] = f32x16{};
 #pragma unroll
-                for (int c = 0; c < DC; ++c) {
-                    const lds_char* a = ((c & 1) ? ka1 : ka0) + (c >> 1) * SUB + kt * 32 * 64;
-                    s[kt] = mfma32x32x16(lds_read_b128(a), qreg[c], s[kt]);
-                    dp[kt] = mfma32x32x16(lds_read_b128(a + TILE), oreg[c], dp[kt]);
-                }
+            for (int c = 0; c < DC; ++c) {
+                const lds_char* a = ((c & 1) ? ka1 : ka0) + (c >> 1) * SUB + kt * 32 * 64;
+                s[kt] = mfma32x32x16(lds_read_b128(a), qreg[c], s[kt]);
+                dp[kt] = mfma32x32x16(lds_read_b128(a + TILE), oreg[c], dp[kt]);
             }
-            // dS^T = P^T (dP^T - D), P^T = exp2(S^T scale log2e - LSE log2e)
-            u32x4 dsb[4];
-            const bool need_mask = (j0 + BC > N) || (CAUSAL && j0 + BC - 1 > qw);
-            const int lim_n = N - j0 - 4 * hl;        // key = j0 + 4hl + off: key < N <=> off < lim_n
-            const int lim_c = my_q - j0 - 4 * hl;     // causal: key <= q <=> off <= lim_c
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                for (int r = 0; r < 16; r += 2) {
-                    float d0 = fast_exp2(__builtin_fmaf(s[kt][r], scale_log2, -lq)) * (dp[kt][r] + dq_row);
-                    float d1 = fast_exp2(__builtin_fmaf(s[kt][r + 1], scale_log2, -lq)) * (dp[kt][r + 1] + dq_row);
-                    if (need_mask) {
-                        const int o0 = kt * 32 + (r >> 2) * 8 + (r & 3);
-                        d0 = (o0 < lim_n && (!CAUSAL || o0 <= lim_c)) ? d0 : 0.f;
-                        d1 = (o0 + 1 < lim_n && (!CAUSAL || o0 + 1 <= lim_c)) ? d1 : 0.f;
-                    }
-                    dsb[kt * 2 + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(d0, d1);
-                }
-            // dQ^T += K^T dS^T; A operand = K^T from the row-major K block
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-                for (int cc = 0; cc < 4; ++cc) {
-                    const int off = dt * SUB + cc * 16 * 64;
-                    const bf16x8 ka = __builtin_shufflevector(lds_read_tr16(kt0 + off), lds_read_tr16(kt1 + off),
-                                                              0, 1, 2, 3, 4, 5, 6, 7);
-                    dqacc[dt] = mfma32x32x16(ka, __builtin_bit_cast(bf16x8, dsb[cc]), dqacc[dt]);
-                }
         }
+        // dS^T = P^T (dP^T - D), P^T = exp2(S^T scale log2e - LSE log2e); on
+        // diagonal tiles keys after the lane's query get exp2(-inf) = 0
+        u32x4 dsb[4];
+        const int lim_c = my_q - j0 - 4 * hl;  // key = j0 + 4hl + off: key <= q <=> off <= lim_c
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                float x0 = __builtin_fmaf(s[kt][r], scale_log2, -lq);
+                float x1 = __builtin_fmaf(s[kt][r + 1], scale_log2, -lq);
+                if constexpr (MASK) {
+                    const int o0 = kt * 32 + (r >> 2) * 8 + (r & 3);
+                    x0 = o0 <= lim_c ? x0 : -INFINITY;
+                    x1 = o0 + 1 <= lim_c ? x1 : -INFINITY;
+                }
+                const float d0 = fast_exp2(x0) * (dp[kt][r] + dq_row);
+                const float d1 = fast_exp2(x1) * (dp[kt][r + 1] + dq_row);
+                dsb[kt * 2 + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(d0, d1);
+            }
+        // dQ^T += K^T dS^T; A operand = K^T from the row-major K block
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) {
+                const int off = dt * SUB + cc * 16 * 64;
+                const bf16x8 ka = __builtin_shufflevector(lds_read_tr16(kt0 + off), lds_read_tr16(kt1 + off),
+                                                          0, 1, 2, 3, 4, 5, 6, 7);
+                dqacc[dt] = mfma32x32x16(ka, __builtin_bit_cast(bf16x8, dsb[cc]), dqacc[dt]);
+            }
+    };
+#pragma clang loop unroll(disable)
+    for (int t = 0; t < nfull; ++t) tile(t, flag_t<false>{});
+    if constexpr (CAUSAL) {
+#pragma clang loop unroll(disable)
+        for (int t = nfull; t < ntiles; ++t) tile(t, flag_t<true>{});
     }
+    FA_WAIT_VMCNT(0);                          // the loads past the last tile
 
     // epilogue: dQ = scale * dQ^T^T -> bf16; lane = query, registers = features
     if (my_q < N) {
