@@ -17,8 +17,8 @@
 //  * K is staged row-major in LDS (rows padded by 16 B); V is staged
 //    transposed (V^T, one row per feature) with keys placed in the k-slot
 //    order of the P^T registers and 16-byte chunks XOR-swizzled per row.
-//  * K/V blocks are double-buffered in LDS and the next block is prefetched
-//    into registers while the current one is multiplied: one barrier per block.
+//  * K/V blocks stream through a 3-stage LDS ring by direct global -> LDS
+//    loads issued two blocks ahead: one barrier per block.
 //  * exponentials are v_exp_f32 (base 2) with scale * log2(e) folded into one
 //    FMA per score.
 #include <type_traits>
@@ -58,7 +58,9 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
 __device__ __forceinline__ int k_swz(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
 __device__ __forceinline__ int v_swz(int row) { return ((row >> 1) & 1) << 1; }
 
-template <int D, bool CAUSAL>
+// POS: scale >= 0 (row maxima of S); otherwise the maxima of scale * S are
+// the minima of S.  A template flag keeps the choice out of the loop.
+template <int D, bool CAUSAL, bool POS>
 __global__ __launch_bounds__(fwd::NT, 1) void fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     __bf16* __restrict__ O, float* __restrict__ LSE, int H, int N, float scale_log2, int nqb) {
@@ -73,9 +75,13 @@ __global__ __launch_bounds__(fwd::NT, 1) void fwd_bf16_kernel(
     constexpr int SEG_SUB = SUB / 1024;        // segments per sub-tile
     static_assert(SEGS % NW == 0, "segments per wave");
 
-    __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * STAGE];
+    static_assert(2 * SEG_W <= 15, "vmcnt immediate");
+    // the ring, then 1 KB that absorbs the direct loads of blocks past the
+    // last one (every block issues the same loads, so no branch is needed)
+    __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * STAGE + 1024];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, hl = lane >> 5;
 
     const int nblocks = gridDim.x;
@@ -86,8 +92,12 @@ __global__ __launch_bounds__(fwd::NT, 1) void fwd_bf16_kernel(
     const int b = bh / H, h = bh - b * H;
     const int row_stride = H * D;              // elements between sequence rows (N*H*D < 2^31)
     const long head_off = ((long)b * N * H + h) * D;
-    const char* Kh = reinterpret_cast<const char*>(K + head_off);
-    const char* Vh = reinterpret_cast<const char*>(V + head_off);
+    const unsigned row_bytes = (unsigned)row_stride * 2u;
+    // K and V rows past N read zeros (range-checked loads); their scores are
+    // masked, so they get weight exactly 0
+    const unsigned head_bytes = (unsigned)(N - 1) * row_bytes + 2 * D;
+    const __amdgpu_buffer_rsrc_t rK = byte_rsrc(K + head_off, head_bytes);
+    const __amdgpu_buffer_rsrc_t rV = byte_rsrc(V + head_off, head_bytes);
 
     const int q0 = qb * BR;
     const int qw = q0 + wave * 32;             // first query of this wave
@@ -95,38 +105,38 @@ __global__ __launch_bounds__(fwd::NT, 1) void fwd_bf16_kernel(
 
     const int kv_end = CAUSAL ? min(N, q0 + BR) : N;
     const int ntiles = (kv_end + BC - 1) / BC;
+    // blocks every query of the workgroup sees whole come first; the rest
+    // (a ragged last block, blocks on the causal diagonal) are masked
+    const int nfull = min(N / BC, CAUSAL ? (q0 + 1) / BC : ntiles);
 
     // Direct global -> LDS loads of one K/V block: each wave fills SEG_W 1 KB
     // segments of K and of V; lane i writes bytes [16 i, 16 i + 16) of its
     // segment (row 16 (seg % SEG_SUB) + i / 4 of sub-tile seg / SEG_SUB,
     // physical chunk i % 4), so it loads the global chunk that belongs there.
-    // Keys past N read row N - 1 (finite data; their scores are masked, so
-    // their V rows get weight exactly 0).
-    int ld_row[SEG_W], k_col[SEG_W], v_col[SEG_W];
+    unsigned k_off[SEG_W], v_off[SEG_W];       // relative to the block's first row
 #pragma unroll
     for (int i = 0; i < SEG_W; ++i) {
         const int seg = wave * SEG_W + i;
         const int sub = seg / SEG_SUB, r = (seg % SEG_SUB) * 16 + lane / 4;
-        ld_row[i] = r;
-        k_col[i] = sub * 64 + (((lane & 3) ^ k_swz(r)) << 4);   // bytes within the global row
-        v_col[i] = sub * 64 + (((lane & 3) ^ v_swz(r)) << 4);
+        k_off[i] = (unsigned)r * row_bytes + sub * 64 + (((lane & 3) ^ k_swz(r)) << 4);
+        v_off[i] = (unsigned)r * row_bytes + sub * 64 + (((lane & 3) ^ v_swz(r)) << 4);
     }
-    const unsigned row_bytes = (unsigned)row_stride * 2u;
-    const unsigned lds0 = lds_offset(smem);
+    const unsigned lds0 = __builtin_amdgcn_readfirstlane(lds_offset(smem));
     auto issue_tile = [&](int t) {
-        const int j0 = t * BC;
-        const unsigned kb = lds0 + (t % NSTAGE) * STAGE;
+        const bool real = t < ntiles;
+        const unsigned kb = __builtin_amdgcn_readfirstlane(real ? lds0 + (t % NSTAGE) * STAGE : lds0 + NSTAGE * STAGE);
+        const unsigned segb = real ? 1024u : 0u;
+        const unsigned row0 = (unsigned)(real ? t * BC : 0) * row_bytes;
 #pragma unroll
         for (int i = 0; i < SEG_W; ++i) {
             const int seg = wave * SEG_W + i;
-            const unsigned ro = (unsigned)min(j0 + ld_row[i], N - 1) * row_bytes;
-            dma16(Kh, ro + k_col[i], __builtin_amdgcn_readfirstlane(kb + seg * 1024));
-            dma16(Vh, ro + v_col[i], __builtin_amdgcn_readfirstlane(kb + TILE + seg * 1024));
+            dma16_buf(rK, row0 + k_off[i], kb + seg * segb);
+            dma16_buf(rV, row0 + v_off[i], kb + (TILE / 1024 + seg) * segb);
         }
     };
 
     issue_tile(0);
-    if (ntiles > 1) issue_tile(1);
+    issue_tile(1);
 
     // Queries of this lane, as B-operand chunks of S^T = K Q^T.  Rows past N
     // read row N-1 (finite data whose results are never stored).
@@ -152,8 +162,7 @@ __global__ __launch_bounds__(fwd::NT, 1) void fwd_bf16_kernel(
     constexpr float kLazy = 8.f;
     float m_run = -INFINITY;
     float l_run = 0.f;         // running sum over this lane's half of the keys
-    const bool pos_scale = scale_log2 >= 0.f;
-    const float masked = pos_scale ? -INFINITY : INFINITY;
+    constexpr float masked = POS ? -INFINITY : INFINITY;
 
     // per-lane LDS byte offsets of the operand reads (within a stage)
     const int k_rd0 = l32 * 64 + ((hl ^ k_swz(l32)) << 4);          // even k-chunks c
@@ -163,128 +172,119 @@ __global__ __launch_bounds__(fwd::NT, 1) void fwd_bf16_kernel(
     const int v_rd = TILE + tr_row * 64 + (((2 * (tr_g & 1) + ((tr_j & 3) >> 1)) ^ v_swz(tr_row)) << 4) +
                      ((tr_j & 1) << 3);
 
-#pragma clang loop unroll(disable)
-    for (int t = 0; t < ntiles; ++t) {
-        // block t landed (block t+1 may still be in flight), then make every
-        // wave's part visible; the barrier also retires all reads of block t-1
-        // (plain s_barrier, no fence: a fence would wait for block t+1 too)
-        if (t + 1 < ntiles) FA_WAIT_VMCNT(2 * SEG_W);
-        else FA_WAIT_VMCNT(0);
+    // One K/V block: wait for its loads (the next block may still be in
+    // flight), make every wave's part visible (the barrier also retires all
+    // reads of block t - 1, whose stage the loads of block t + 2 refill), then
+    // S^T = K Q^T, the online softmax and O^T += V^T P^T.
+    auto block = [&](int t, auto mask_tag) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        FA_WAIT_VMCNT(2 * SEG_W);
         __builtin_amdgcn_s_barrier();
-        if (t + 2 < ntiles) issue_tile(t + 2);
+        issue_tile(t + 2);
 
         const int j0 = t * BC;
-        const bool wave_active = !CAUSAL || j0 <= qw + 31;
-        if (wave_active) {
-            // per-iteration bases; the empty asm keeps the compiler from
-            // hoisting base + offset sums into separate registers, so the
-            // offsets fold into the LDS instructions
-            const lds_char* stage = as_lds(smem) + (t % NSTAGE) * STAGE;
-            const lds_char* kb0 = stage + k_rd0;
-            const lds_char* kb1 = stage + k_rd1;
-            const lds_char* vb = stage + v_rd;
-            asm volatile("" : "+v"(kb0), "+v"(kb1), "+v"(vb));
-            // S^T = K Q^T for two 32-key tiles
-            f32x16 s[2];
+        if (MASK && CAUSAL && j0 > qw + 31) return;   // every key after this wave's queries
+        // per-iteration bases; the empty asm keeps the compiler from
+        // hoisting base + offset sums into separate registers, so the
+        // offsets fold into the LDS instructions
+        const lds_char* stage = as_lds(smem) + (t % NSTAGE) * STAGE;
+        const lds_char* kb0 = stage + k_rd0;
+        const lds_char* kb1 = stage + k_rd1;
+        const lds_char* vb = stage + v_rd;
+        asm volatile("" : "+v"(kb0), "+v"(kb1), "+v"(vb));
+        // S^T = K Q^T for two 32-key tiles
+        f32x16 s[2];
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
-                s[kt] = f32x16{};
+        for (int kt = 0; kt < 2; ++kt) {
+            s[kt] = f32x16{};
 #pragma unroll
-                for (int c = 0; c < DC; ++c) {
-                    const lds_char* a = ((c & 1) ? kb1 : kb0) + (c >> 1) * SUB + kt * 32 * 64;
-                    s[kt] = mfma32x32x16(lds_read_b128(a), qreg[c], s[kt]);
-                }
+            for (int c = 0; c < DC; ++c) {
+                const lds_char* a = ((c & 1) ? kb1 : kb0) + (c >> 1) * SUB + kt * 32 * 64;
+                s[kt] = mfma32x32x16(lds_read_b128(a), qreg[c], s[kt]);
             }
-            // keep the V reads below the softmax (register pressure)
-            __builtin_amdgcn_sched_barrier(0);
-            u32x4 pw[4];
-            // MASK: keys past N and, for causal, keys after the query.  The two
-            // variants cover only the block max and the exponentials; the
-            // rescale of O sits between them, outside both, so the compiler
-            // keeps O in place across that (rarely taken) branch.
-            const bool need_mask = (j0 + BC > N) || (CAUSAL && j0 + BC - 1 > qw);
-            auto block_max = [&](auto mask_tag) {
-                constexpr bool MASK = decltype(mask_tag)::value;
+        }
+        // keep the V reads below the softmax (register pressure)
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (MASK) {
+            // keys past N and, for causal, keys after the query.  Key of
+            // register r = j0 + 4 hl + off(kt, r), off a constant: compare the
+            // constant with one per-lane limit
+            const int lim_n = N - j0 - 4 * hl;            // visible iff off < lim_n
+            const int lim_c = my_q - j0 - 4 * hl;         // causal: off <= lim_c
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int off = kt * 32 + (r >> 2) * 8 + (r & 3);
+                    const bool vis = off < lim_n && (!CAUSAL || off <= lim_c);
+                    s[kt][r] = vis ? s[kt][r] : masked;
+                }
+        }
+        float mx = s[0][0];
+        if constexpr (POS) {
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
+            mx = halves_max(mx);
+        } else {
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fminf(mx, s[kt][r]);
+            mx = halves_min(mx);
+        }
+        const float mt = mx * scale_log2;
+        if (__builtin_amdgcn_ballot_w64(mt > m_run + kLazy) != 0) {
+            const float m_new = fmaxf(m_run, mt);
+            const float alpha = fast_exp2(m_run - m_new);
+            m_run = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int i = 0; i < DT; ++i) oacc[i] *= alpha;
+        }
+        const float m_sub = m_run == -INFINITY ? 0.f : m_run;
+        // P = exp2(x - m): the row sum accumulates in fp32 (so LSE keeps
+        // fp32 accuracy); the PV product uses P rounded to bf16
+        u32x4 pw[4];
+        float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                float p0 = fast_exp2(__builtin_fmaf(s[kt][r], scale_log2, -m_sub));
+                float p1 = fast_exp2(__builtin_fmaf(s[kt][r + 1], scale_log2, -m_sub));
+                // a masked score must give exactly 0, also when scale == 0
                 if constexpr (MASK) {
-                    // key of register r = j0 + 4 hl + off(kt, r), off a constant:
-                    // compare the constant with one per-lane limit
-                    const int lim_n = N - j0 - 4 * hl;            // visible iff off < lim_n
-                    const int lim_c = my_q - j0 - 4 * hl;         // causal: off <= lim_c
-#pragma unroll
-                    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int off = kt * 32 + (r >> 2) * 8 + (r & 3);
-                            const bool vis = off < lim_n && (!CAUSAL || off <= lim_c);
-                            s[kt][r] = vis ? s[kt][r] : masked;
-                        }
+                    p0 = s[kt][r] == masked ? 0.f : p0;
+                    p1 = s[kt][r + 1] == masked ? 0.f : p1;
                 }
-                float mx = s[0][0];
-                if (pos_scale) {
-#pragma unroll
-                    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
-                    return halves_max(mx);
-                } else {
-#pragma unroll
-                    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) mx = fminf(mx, s[kt][r]);
-                    return halves_min(mx);
-                }
-            };
-            const float mt = (need_mask ? block_max(std::true_type{}) : block_max(std::false_type{})) * scale_log2;
-            if (__builtin_amdgcn_ballot_w64(mt > m_run + kLazy) != 0) {
-                const float m_new = fmaxf(m_run, mt);
-                const float alpha = fast_exp2(m_run - m_new);
-                m_run = m_new;
-                l_run *= alpha;
-#pragma unroll
-                for (int i = 0; i < DT; ++i) oacc[i] *= alpha;
+                ls0 += p0;
+                ls1 += p1;
+                pw[kt * 2 + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(p0, p1);
             }
-            const float m_sub = m_run == -INFINITY ? 0.f : m_run;
-            // P = exp2(x - m): the row sum accumulates in fp32 (so LSE keeps
-            // fp32 accuracy); the PV product uses P rounded to bf16
-            auto block_exp = [&](auto mask_tag) {
-                constexpr bool MASK = decltype(mask_tag)::value;
-                float ls0 = 0.f, ls1 = 0.f;
+        l_run += ls0 + ls1;
+        __builtin_amdgcn_sched_barrier(0);
+        // O^T += V^T P^T; the A operand (8 keys of one feature row) comes
+        // from two transposing reads: keys 16cc + 4h + 0..3 and +8.
 #pragma unroll
-                for (int kt = 0; kt < 2; ++kt)
+        for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
-                    for (int r = 0; r < 16; r += 2) {
-                        float p0 = fast_exp2(__builtin_fmaf(s[kt][r], scale_log2, -m_sub));
-                        float p1 = fast_exp2(__builtin_fmaf(s[kt][r + 1], scale_log2, -m_sub));
-                        // a masked score must give exactly 0, also when scale == 0
-                        if constexpr (MASK) {
-                            p0 = s[kt][r] == masked ? 0.f : p0;
-                            p1 = s[kt][r + 1] == masked ? 0.f : p1;
-                        }
-                        ls0 += p0;
-                        ls1 += p1;
-                        pw[kt * 2 + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(p0, p1);
-                    }
-                l_run += ls0 + ls1;
-            };
-            if (need_mask) block_exp(std::true_type{});
-            else block_exp(std::false_type{});
-            __builtin_amdgcn_sched_barrier(0);
-            // O^T += V^T P^T; the A operand (8 keys of one feature row) comes
-            // from two transposing reads: keys 16cc + 4h + 0..3 and +8.
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-                for (int cc = 0; cc < 4; ++cc) {
-                    const lds_char* a0 = vb + dt * SUB + cc * 16 * 64;
-                    const bf16x4 lo = lds_read_tr16(a0);
-                    const bf16x4 hi = lds_read_tr16(a0 + 8 * 64);
-                    const bf16x8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                    oacc[dt] = mfma32x32x16(va, __builtin_bit_cast(bf16x8, pw[cc]), oacc[dt]);
-                }
+            for (int cc = 0; cc < 4; ++cc) {
+                const lds_char* a0 = vb + dt * SUB + cc * 16 * 64;
+                const bf16x4 lo = lds_read_tr16(a0);
+                const bf16x4 hi = lds_read_tr16(a0 + 8 * 64);
+                const bf16x8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                oacc[dt] = mfma32x32x16(va, __builtin_bit_cast(bf16x8, pw[cc]), oacc[dt]);
             }
         }
         __builtin_amdgcn_sched_barrier(0);
-    }
+    };
+#pragma clang loop unroll(disable)
+    for (int t = 0; t < nfull; ++t) block(t, std::false_type{});
+#pragma clang loop unroll(disable)
+    for (int t = nfull; t < ntiles; ++t) block(t, std::true_type{});
+    FA_WAIT_VMCNT(0);                          // the loads past the last block
 
     // ---- epilogue: O = O / l, LSE = m ln2 + ln l ----
     const float l_tot = halves_sum(l_run);
@@ -411,16 +411,14 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
     auto Kp = static_cast<const __bf16*>(k);
     auto Vp = static_cast<const __bf16*>(v);
     auto Op = static_cast<__bf16*>(o);
+    auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, block, 0, stream, Qp, Kp, Vp, Op, lse, H, N, sl2, nqb); };
+    const bool pos = sl2 >= 0.f;
     if (d == 128) {
-        if (causal)
-            hipLaunchKernelGGL((fwd_bf16_kernel<128, true>), grid, block, 0, stream, Qp, Kp, Vp, Op, lse, H, N, sl2, nqb);
-        else
-            hipLaunchKernelGGL((fwd_bf16_kernel<128, false>), grid, block, 0, stream, Qp, Kp, Vp, Op, lse, H, N, sl2, nqb);
+        if (causal) pos ? go(fwd_bf16_kernel<128, true, true>) : go(fwd_bf16_kernel<128, true, false>);
+        else pos ? go(fwd_bf16_kernel<128, false, true>) : go(fwd_bf16_kernel<128, false, false>);
     } else {
-        if (causal)
-            hipLaunchKernelGGL((fwd_bf16_kernel<64, true>), grid, block, 0, stream, Qp, Kp, Vp, Op, lse, H, N, sl2, nqb);
-        else
-            hipLaunchKernelGGL((fwd_bf16_kernel<64, false>), grid, block, 0, stream, Qp, Kp, Vp, Op, lse, H, N, sl2, nqb);
+        if (causal) pos ? go(fwd_bf16_kernel<64, true, true>) : go(fwd_bf16_kernel<64, true, false>);
+        else pos ? go(fwd_bf16_kernel<64, false, true>) : go(fwd_bf16_kernel<64, false, false>);
     }
     return hipGetLastError();
 }
