@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the other workloads (causal, long causal, d=64 causal)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device-to-device copy of 1 GiB (3 times), the "
                          "reference for scaling HBM byte counters")
@@ -113,6 +115,53 @@ def naive_step(torch, q, k, v, do, scale, causal):
     dq = torch.bmm(ds, kh) * scale
     dk = torch.bmm(ds.transpose(1, 2).contiguous(), qh) * scale
     return o, dq, dk, dv
+
+
+# Workloads reported beside the headline one (parity-test shapes of the
+# same kernels): forward and backward timed separately, median of 5.
+EXTRA_WORKLOADS = [
+    ("b4_h32_n4096_d128_causal", 4, 32, 4096, 128, True),
+    ("b1_h32_n16384_d128_causal", 1, 32, 16384, 128, True),
+    ("b4_h16_n4096_d64_causal", 4, 16, 4096, 64, True),
+]
+
+
+def other_workloads(torch, binding, inputs, workloads, seed):
+    out = {}
+    dev = torch.device("cuda:0")
+    for name, B, H, N, d, causal in EXTRA_WORKLOADS:
+        x = inputs.make_qkv(B, N, H, d, torch.bfloat16, seed=seed, with_do=True)
+        q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "do"))
+        o, lse = binding.forward(q, k, v, causal=causal)
+        _, calls = binding.backward_steps(q, k, v, o, do, lse, causal=causal)
+
+        def fwd():
+            binding.forward(q, k, v, causal=causal, out=o, lse=lse)
+
+        def bwd():
+            for c in calls:
+                c()
+
+        res = {}
+        for tag, f, fl in (("fwd", fwd, workloads.fwd_flops(B, H, N, d, causal)),
+                           ("bwd", bwd, workloads.bwd_flops(B, H, N, d, causal))):
+            for _ in range(2):
+                f()
+            ms = []
+            for _ in range(5):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                f()
+                e1.record()
+                torch.cuda.synchronize()
+                ms.append(e0.elapsed_time(e1))
+            med = sorted(ms)[2]
+            res[f"{tag}_ms"] = round(med, 4)
+            res[f"{tag}_tflops"] = round(fl / (med * 1e-3) / 1e12, 1)
+        out[name] = res
+        del q, k, v, do, o, lse, calls
+        torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(x, args, flops_per_head):
@@ -270,6 +319,9 @@ def main():
         "kernels": kernels,
         "roofline": roofline,
     }
+
+    if not args.no_extra:
+        out["other_workloads"] = other_workloads(torch, binding, inputs, workloads, args.seed)
 
     if not args.no_naive:
         try:

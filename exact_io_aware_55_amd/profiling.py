@@ -1,0 +1,163 @@
+"""Turns rocprofv3 output of ``bench.py`` runs into the text summaries kept
+under ``profiles/`` (a kernel-trace table and an HBM-traffic table plus the
+``traffic.json`` that ``bench.py`` reads for its roofline ``traffic`` field).
+
+Usage, from the repository root, after the rocprofv3 runs listed in each
+summary::
+
+    python -m exact_io_aware_55_amd.profiling trace DIR OUT.md TITLE COMMAND
+    python -m exact_io_aware_55_amd.profiling traffic FETCH WRITE COPY_FETCH COPY_WRITE OUT.md WORKLOAD
+
+``DIR`` holds a ``--kernel-trace --stats`` run (``*_kernel_stats.csv``); the
+traffic arguments are the output folders of four ``--pmc`` runs: FETCH_SIZE
+and WRITE_SIZE of the bench workload, and the same two counters for the
+``bench.py --copy-calibration`` device copy of 1 GiB, whose known byte count
+scales the counters to bytes.
+"""
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# bench.py stage -> (kernel symbol prefix, sources that define it)
+STAGES = {
+    "fwd": ("fa::fwd_bf16_kernel", ("fa_fwd.hip", "fa_common.h")),
+    "bwd_preprocess": ("fa::bwd_pre_kernel", ("fa_bwd.hip", "fa_common.h")),
+    "bwd_dkdv": ("fa::bwd_dkdv_kernel", ("fa_bwd.hip", "fa_common.h")),
+    "bwd_dq": ("fa::bwd_dq_kernel", ("fa_bwd.hip", "fa_common.h")),
+}
+
+
+def source_digest(names):
+    """Same digest as bench.py: sha256 of the kernel's sources, 16 hex digits."""
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "exact_io_aware_55_amd", "csrc", n), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _one(pattern):
+    hits = sorted(glob.glob(pattern, recursive=True))
+    if not hits:
+        raise SystemExit(f"no file matches {pattern}")
+    return hits[0]
+
+
+def _short(name):
+    return name.split("(")[0].replace("void ", "").strip()
+
+
+def trace(folder, out, title, command):
+    rows = list(csv.DictReader(open(_one(os.path.join(folder, "**", "*kernel_stats.csv")))))
+    lines = [f"# {title}", "", "Command (from the repository root on one MI355X, after "
+             "`cd /tmp && export TMPDIR=/tmp`; `$REPO` is the repository root):", "",
+             "```", command, "```", "",
+             "| kernel | calls | average (us) | min (us) | max (us) | share |",
+             "|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                     f"{float(r['Percentage']):.1f}% |")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
+def _counter(folder):
+    """kernel name -> mean counter value per dispatch (KiB)."""
+    acc = {}
+    for f in glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            acc.setdefault(_short(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def traffic(fetch, write, copy_fetch, copy_write, out, workload, compulsory=None):
+    f, w = _counter(fetch), _counter(write)
+    cf, cw = _counter(copy_fetch), _counter(copy_write)
+    copy = [k for k in cf if "copy" in k.lower()][0]
+    gib_kib = (1 << 30) / 1024
+    fs, ws = gib_kib / cf[copy], gib_kib / cw[copy]
+    table_path = os.path.join(os.path.dirname(out), "traffic.json")
+    table = json.load(open(table_path)) if os.path.exists(table_path) else {}
+    lines = []
+    for stage, (prefix, srcs) in STAGES.items():
+        names = [k for k in f if k.startswith(prefix)]
+        if not names:
+            continue
+        k = names[0]
+        rd, wr = f[k] * fs * 1024, w.get(k, 0.0) * ws * 1024
+        table[f"{stage}@{workload}"] = {
+            "kernel": k, "bytes_per_launch": int(rd + wr), "read_bytes": int(rd),
+            "written_bytes": int(wr), "fetch_kib": f[k], "write_kib": w.get(k, 0.0),
+            "fetch_scale": round(fs, 4), "write_scale": round(ws, 4),
+            "source_sha": source_digest(srcs)}
+        comp = (compulsory or {}).get(stage)
+        ratio = f"{(rd + wr) / comp:.2f}" if comp else "-"
+        comp_mb = f"{comp / 1e6:.1f}" if comp else "-"
+        lines.append(f"| `{k}` | {f[k]:.0f} | {w.get(k, 0.0):.0f} | {rd / 1e6:.1f} | {wr / 1e6:.1f} | "
+                     f"{comp_mb} | {ratio} |")
+    with open(table_path, "w") as fh:
+        json.dump(table, fh, indent=1, sort_keys=True)
+    return fs, ws, lines
+
+
+def compulsory_bytes(B, H, N, d, causal):
+    """Bytes each kernel must move at least (bf16 tensors, fp32 statistics)."""
+    t = B * H * N * d * 2                       # one [B,N,H,d] bf16 tensor
+    rows = B * H * N
+    pad = B * H * ((N + 63) // 64 * 64) * 4     # one padded statistic
+    return {
+        "fwd": 4 * t + rows * 4,                # Q K V in, O and LSE out
+        "bwd_preprocess": 2 * t + rows * 4 + 2 * pad,
+        "bwd_dkdv": 6 * t + 2 * pad,            # Q K V dO + stats in, dK dV out
+        "bwd_dq": 5 * t + 2 * pad,              # Q K V dO + stats in, dQ out
+    }
+
+
+def main(argv):
+    if len(argv) >= 5 and argv[0] == "trace":
+        trace(argv[1], argv[2], argv[3], argv[4])
+    elif len(argv) >= 7 and argv[0] == "traffic":
+        workload = argv[6]
+        shape = {p[0]: p[1:] for p in workload.split("_") if p[:1] in "bhnd" and p[1:].isdigit()}
+        comp = compulsory_bytes(int(shape["b"]), int(shape["h"]), int(shape["n"]), int(shape["d"]),
+                                "causal" in workload)
+        fs, ws, lines = traffic(*argv[1:5], argv[5], workload, comp)
+        head = [f"# HBM traffic per launch: {workload}", "",
+                "Commands (from the repository root on one MI355X, after "
+                "`cd /tmp && export TMPDIR=/tmp`; `$REPO` is the repository root):", "", "```",
+                "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $REPO/gpurun_out/pmc_fetch -o bench -- "
+                "python3 $REPO/bench.py --steps 2 --warmup 1 --no-naive --no-cpu --no-extra",
+                "rocprofv3 --pmc WRITE_SIZE --output-format csv -d $REPO/gpurun_out/pmc_write -o bench -- "
+                "python3 $REPO/bench.py --steps 2 --warmup 1 --no-naive --no-cpu --no-extra",
+                "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $REPO/gpurun_out/pmc_copy_fetch -o copy -- "
+                "python3 $REPO/bench.py --copy-calibration",
+                "rocprofv3 --pmc WRITE_SIZE --output-format csv -d $REPO/gpurun_out/pmc_copy_write -o copy -- "
+                "python3 $REPO/bench.py --copy-calibration",
+                "python -m exact_io_aware_55_amd.profiling traffic gpurun_out/pmc_fetch gpurun_out/pmc_write "
+                f"gpurun_out/pmc_copy_fetch gpurun_out/pmc_copy_write profiles/<this file> {workload}",
+                "```", "",
+                f"Calibration: a plain 1 GiB device copy reads FETCH_SIZE and WRITE_SIZE that scale to its "
+                f"known bytes by x{fs:.4f} (fetch) and x{ws:.4f} (write); the same factors convert the "
+                "kernels' counters (KiB per dispatch) to bytes.", "",
+                "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | read MB (scaled) | written MB | compulsory MB | "
+                "measured / compulsory |", "|---|---|---|---|---|---|---|"]
+        tail = ["", "Compulsory bytes: the forward reads Q, K, V and writes O and LSE; the preprocess "
+                "reads O, dO and LSE and writes both padded row statistics; dK/dV reads Q, K, V, dO and "
+                "the statistics and writes dK, dV; dQ reads Q, K, V, dO and the statistics and writes "
+                "dQ.  The N x N score matrix never reaches HBM."]
+        with open(argv[5], "w") as fh:
+            fh.write("\n".join(head + lines + tail) + "\n")
+    else:
+        print(__doc__)
+        return 2
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main(sys.argv[1:]))
