@@ -557,7 +557,7 @@ __global__ __launch_bounds__(bwdq::NT, 1) void bwd_dq_kernel(
         constexpr bool MASK = decltype(masked)::value;
         FA_WAIT_VMCNT(2 * SEG_W);
         __builtin_amdgcn_s_barrier();
-        issue_tile(t + 2);
+        if constexpr (MASK) issue_tile(t + 2);
 
         const int j0 = t * BC;
         if (MASK && j0 > qw + 31) return;      // every key after this wave's queries
@@ -579,6 +579,10 @@ __global__ __launch_bounds__(bwdq::NT, 1) void bwd_dq_kernel(
                 dp[kt] = mfma32x32x16(lds_read_b128(a + TILE), oreg[c], dp[kt]);
             }
         }
+        // unmasked tiles start the loads of tile t + 2 here, behind the S^T and
+        // dP^T reads, rather than as a burst at the top (masked tiles may
+        // return early, so they issue first)
+        if constexpr (!MASK) issue_tile(t + 2);
         // dS^T = P^T (dP^T - D), P^T = exp2(S^T scale log2e - LSE log2e); on
         // diagonal tiles keys after the lane's query get exp2(-inf) = 0
         u32x4 dsb[4];

@@ -180,7 +180,7 @@ __global__ __launch_bounds__(fwd::NT, 1) void fwd_bf16_kernel(
         constexpr bool MASK = decltype(mask_tag)::value;
         FA_WAIT_VMCNT(2 * SEG_W);
         __builtin_amdgcn_s_barrier();
-        issue_tile(t + 2);
+        if constexpr (MASK) issue_tile(t + 2);  // masked blocks may return early
 
         const int j0 = t * BC;
         if (MASK && CAUSAL && j0 > qw + 31) return;   // every key after this wave's queries
@@ -203,6 +203,9 @@ __global__ __launch_bounds__(fwd::NT, 1) void fwd_bf16_kernel(
                 s[kt] = mfma32x32x16(lds_read_b128(a), qreg[c], s[kt]);
             }
         }
+        // unmasked blocks start the loads of block t + 2 here, behind the K
+        // reads, rather than as a burst at the top
+        if constexpr (!MASK) issue_tile(t + 2);
         // keep the V reads below the softmax (register pressure)
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (MASK) {
