@@ -119,21 +119,30 @@ def naive_step(torch, q, k, v, do, scale, causal):
 
 # Workloads reported beside the headline one (parity-test shapes of the
 # same kernels): forward and backward timed separately, median of 5.
+# (name, B, H, H_kv, N, d, causal); the last one is grouped-query attention
+# with the pages' Llama 2 70B head counts (64 query heads over 8 K/V heads).
 EXTRA_WORKLOADS = [
-    ("b4_h32_n4096_d128_causal", 4, 32, 4096, 128, True),
-    ("b1_h32_n16384_d128_causal", 1, 32, 16384, 128, True),
-    ("b4_h16_n4096_d64_causal", 4, 16, 4096, 64, True),
+    ("b4_h32_n4096_d128_causal", 4, 32, 32, 4096, 128, True),
+    ("b1_h32_n16384_d128_causal", 1, 32, 32, 16384, 128, True),
+    ("b4_h16_n4096_d64_causal", 4, 16, 16, 4096, 64, True),
+    ("b2_h64_hkv8_n4096_d128_causal_gqa", 2, 64, 8, 4096, 128, True),
 ]
 
 
 def other_workloads(torch, binding, inputs, workloads, seed):
     out = {}
     dev = torch.device("cuda:0")
-    for name, B, H, N, d, causal in EXTRA_WORKLOADS:
-        x = inputs.make_qkv(B, N, H, d, torch.bfloat16, seed=seed, with_do=True)
+    for name, B, H, Hkv, N, d, causal in EXTRA_WORKLOADS:
+        x = inputs.make_qkv(B, N, H, d, torch.bfloat16, seed=seed, with_do=True, H_kv=Hkv)
         q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "do"))
         o, lse = binding.forward(q, k, v, causal=causal)
-        _, calls = binding.backward_steps(q, k, v, o, do, lse, causal=causal)
+        if Hkv == H:
+            _, calls = binding.backward_steps(q, k, v, o, do, lse, causal=causal)
+        else:
+            ws = torch.empty(binding.bwd_workspace_size(B, H, N, d), device=dev, dtype=torch.uint8)
+            grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+            calls = [lambda: binding.backward(q, k, v, o, do, lse, causal=causal, workspace=ws,
+                                              out=grads)]
 
         def fwd():
             binding.forward(q, k, v, causal=causal, out=o, lse=lse)

@@ -18,7 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfa.so")
 
 EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_bwd_workspace_size", "fa_bwd", "fa_bwd_preprocess",
-           "fa_bwd_dkdv", "fa_bwd_dq", "fa_strerror")
+           "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_gqa", "fa_bwd_gqa", "fa_strerror")
 
 FA_OK = 0
 FA_ERR_INVALID_ARG = -1
@@ -55,6 +55,10 @@ def load(path: str = LIB_PATH):
     lib.fa_bwd_dkdv.restype = i
     lib.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, sz, vp]
     lib.fa_bwd_dq.restype = i
+    lib.fa_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+    lib.fa_fwd_gqa.restype = i
+    lib.fa_bwd_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
+    lib.fa_bwd_gqa.restype = i
     lib.fa_strerror.argtypes = [i]
     lib.fa_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -94,18 +98,35 @@ def _check_inputs(dtype, *ts):
     return shape
 
 
+def _check_gqa(dtype, q_like, kv_like):
+    """q-shaped tensors [B,N,H,d] and K/V-shaped tensors [B,N,H_kv,d], H a
+    multiple of H_kv.  Returns (B, N, H, H_kv, d)."""
+    B, N, H, d = _check_inputs(dtype, *q_like)
+    Bk, Nk, Hkv, dk = _check_inputs(dtype, *kv_like)
+    if (Bk, Nk, dk) != (B, N, d) or Hkv < 1 or H % Hkv != 0:
+        raise ValueError("k and v must be [B, N, H_kv, d] with H a multiple of H_kv")
+    return B, N, H, Hkv, d
+
+
 def _scale(scale, d):
     return float(d) ** -0.5 if scale is None else float(scale)
 
 
 def forward(q, k, v, causal=False, scale=None, out=None, lse=None):
-    """bf16 forward.  Returns (O [B,N,H,d] bf16, LSE [B,H,N] fp32)."""
+    """bf16 forward.  Returns (O [B,N,H,d] bf16, LSE [B,H,N] fp32).
+
+    k and v may have fewer heads than q (grouped-query attention: [B,N,H_kv,d]
+    with H a multiple of H_kv); that calls fa_fwd_gqa, else fa_fwd."""
     lib = load()
-    B, N, H, d = _check_inputs(torch.bfloat16, q, k, v)
+    B, N, H, Hkv, d = _check_gqa(torch.bfloat16, (q,), (k, v))
     o = torch.empty_like(q) if out is None else out
     lse_t = torch.empty((B, H, N), device=q.device, dtype=torch.float32) if lse is None else lse
-    _check(lib.fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), B, H, N, d,
-                      _scale(scale, d), int(bool(causal)), _stream()))
+    if Hkv == H:
+        _check(lib.fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), B, H, N, d,
+                          _scale(scale, d), int(bool(causal)), _stream()))
+    else:
+        _check(lib.fa_fwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), B, H, Hkv, N, d,
+                              _scale(scale, d), int(bool(causal)), _stream()))
     return o, lse_t
 
 
@@ -125,9 +146,11 @@ def bwd_workspace_size(B, H, N, d) -> int:
 
 
 def backward(q, k, v, o, do, lse, causal=False, scale=None, workspace=None, out=None):
-    """bf16 backward by recomputation.  Returns (dQ, dK, dV), bf16 [B,N,H,d]."""
+    """bf16 backward by recomputation.  Returns (dQ, dK, dV), bf16, shaped like
+    q, k and v (grouped-query attention when k and v have fewer heads: then
+    fa_bwd_gqa, else fa_bwd)."""
     lib = load()
-    B, N, H, d = _check_inputs(torch.bfloat16, q, k, v, o, do)
+    B, N, H, Hkv, d = _check_gqa(torch.bfloat16, (q, o, do), (k, v))
     if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
         raise ValueError("lse must be contiguous fp32 [B, H, N]")
     need = bwd_workspace_size(B, H, N, d)
@@ -136,9 +159,14 @@ def backward(q, k, v, o, do, lse, causal=False, scale=None, workspace=None, out=
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     else:
         dq, dk, dv = out
-    _check(lib.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk),
-                      _ptr(dv), B, H, N, d, _scale(scale, d), int(bool(causal)), _ptr(ws),
-                      ws.numel() * ws.element_size(), _stream()))
+    if Hkv == H:
+        _check(lib.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk),
+                          _ptr(dv), B, H, N, d, _scale(scale, d), int(bool(causal)), _ptr(ws),
+                          ws.numel() * ws.element_size(), _stream()))
+    else:
+        _check(lib.fa_bwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
+                              _ptr(dk), _ptr(dv), B, H, Hkv, N, d, _scale(scale, d), int(bool(causal)),
+                              _ptr(ws), ws.numel() * ws.element_size(), _stream()))
     return dq, dk, dv
 
 

@@ -29,6 +29,12 @@ int check_shape(int B, int H, int N, int d, float scale) {
     return FA_OK;
 }
 
+// grouped-query attention: H_kv K/V heads, each shared by H / H_kv query heads
+int check_groups(int H, int H_kv) {
+    if (H_kv < 1 || H_kv > H || H % H_kv != 0) return FA_ERR_INVALID_ARG;
+    return FA_OK;
+}
+
 int fwd_common(const void* q, const void* k, const void* v, const void* o, const void* lse, int B,
                int H, int N, int d, float scale) {
     if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
@@ -45,9 +51,15 @@ extern "C" {
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
            int d, float scale, int causal, hipStream_t stream) {
-    const int rc = fwd_common(q, k, v, o, lse, B, H, N, d, scale);
+    return fa_fwd_gqa(q, k, v, o, lse, B, H, H, N, d, scale, causal, stream);
+}
+
+int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int H_kv,
+               int N, int d, float scale, int causal, hipStream_t stream) {
+    int rc = fwd_common(q, k, v, o, lse, B, H, N, d, scale);
     if (rc != FA_OK) return rc;
-    if (fa::launch_fwd_bf16(q, k, v, o, lse, B, H, N, d, scale, causal != 0, stream) != hipSuccess)
+    if ((rc = check_groups(H, H_kv)) != FA_OK) return rc;
+    if (fa::launch_fwd_bf16(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal != 0, stream) != hipSuccess)
         return FA_ERR_LAUNCH;
     return FA_OK;
 }
@@ -116,55 +128,81 @@ int fa_bwd_preprocess(const void* o, const void* dout, const float* lse, int B, 
     return FA_OK;
 }
 
-int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, void* dk, void* dv, int B,
-                int H, int N, int d, float scale, int causal, void* workspace, size_t workspace_bytes,
-                hipStream_t stream) {
+namespace {
+int bwd_dkdv_impl(const void* q, const void* k, const void* v, const void* dout, void* dk, void* dv,
+                  int B, int H, int H_kv, int N, int d, float scale, int causal, void* workspace,
+                  size_t workspace_bytes, hipStream_t stream) {
     int rc = all_aligned({q, k, v, dout, dk, dv});
     if (rc != FA_OK) return rc;
     if ((rc = check_bwd_shape(B, H, N, d, scale)) != FA_OK) return rc;
+    if ((rc = check_groups(H, H_kv)) != FA_OK) return rc;
     Workspace ws;
     if ((rc = check_workspace(workspace, workspace_bytes, B, H, N, d, &ws)) != FA_OK) return rc;
-    if (fa::launch_bwd_dkdv(q, k, v, dout, dk, dv, B, H, N, d, scale, causal != 0, ws.lse2, ws.delta,
-                            stream) != hipSuccess)
+    if (fa::launch_bwd_dkdv(q, k, v, dout, dk, dv, B, H, H_kv, N, d, scale, causal != 0, ws.lse2,
+                            ws.delta, stream) != hipSuccess)
         return FA_ERR_LAUNCH;
     return FA_OK;
+}
+
+int bwd_dq_impl(const void* q, const void* k, const void* v, const void* dout, void* dq, int B, int H,
+                int H_kv, int N, int d, float scale, int causal, void* workspace, size_t workspace_bytes,
+                hipStream_t stream) {
+    int rc = all_aligned({q, k, v, dout, dq});
+    if (rc != FA_OK) return rc;
+    if ((rc = check_bwd_shape(B, H, N, d, scale)) != FA_OK) return rc;
+    if ((rc = check_groups(H, H_kv)) != FA_OK) return rc;
+    Workspace ws;
+    if ((rc = check_workspace(workspace, workspace_bytes, B, H, N, d, &ws)) != FA_OK) return rc;
+    if (fa::launch_bwd_dq(q, k, v, dout, dq, B, H, H_kv, N, d, scale, causal != 0, ws.lse2, ws.delta,
+                          stream) != hipSuccess)
+        return FA_ERR_LAUNCH;
+    return FA_OK;
+}
+}  // namespace
+
+int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, void* dk, void* dv, int B,
+                int H, int N, int d, float scale, int causal, void* workspace, size_t workspace_bytes,
+                hipStream_t stream) {
+    return bwd_dkdv_impl(q, k, v, dout, dk, dv, B, H, H, N, d, scale, causal, workspace, workspace_bytes,
+                         stream);
 }
 
 int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, void* dq, int B, int H,
               int N, int d, float scale, int causal, void* workspace, size_t workspace_bytes,
               hipStream_t stream) {
-    int rc = all_aligned({q, k, v, dout, dq});
+    return bwd_dq_impl(q, k, v, dout, dq, B, H, H, N, d, scale, causal, workspace, workspace_bytes, stream);
+}
+
+int fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const void* dout,
+               const float* lse, void* dq, void* dk, void* dv, int B, int H, int H_kv, int N, int d,
+               float scale, int causal, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    // validate everything before the first launch
+    int rc = all_aligned({q, k, v, o, dout, lse, dq, dk, dv});
     if (rc != FA_OK) return rc;
     if ((rc = check_bwd_shape(B, H, N, d, scale)) != FA_OK) return rc;
+    if ((rc = check_groups(H, H_kv)) != FA_OK) return rc;
     Workspace ws;
     if ((rc = check_workspace(workspace, workspace_bytes, B, H, N, d, &ws)) != FA_OK) return rc;
-    if (fa::launch_bwd_dq(q, k, v, dout, dq, B, H, N, d, scale, causal != 0, ws.lse2, ws.delta, stream) !=
-        hipSuccess)
-        return FA_ERR_LAUNCH;
-    return FA_OK;
+    if ((rc = fa_bwd_preprocess(o, dout, lse, B, H, N, d, workspace, workspace_bytes, stream)) != FA_OK)
+        return rc;
+    if ((rc = bwd_dkdv_impl(q, k, v, dout, dk, dv, B, H, H_kv, N, d, scale, causal, workspace,
+                            workspace_bytes, stream)) != FA_OK)
+        return rc;
+    return bwd_dq_impl(q, k, v, dout, dq, B, H, H_kv, N, d, scale, causal, workspace, workspace_bytes,
+                       stream);
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
            const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
            int causal, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-    // validate everything before the first launch
-    int rc = all_aligned({q, k, v, o, dout, lse, dq, dk, dv});
-    if (rc != FA_OK) return rc;
-    if ((rc = check_bwd_shape(B, H, N, d, scale)) != FA_OK) return rc;
-    Workspace ws;
-    if ((rc = check_workspace(workspace, workspace_bytes, B, H, N, d, &ws)) != FA_OK) return rc;
-    if ((rc = fa_bwd_preprocess(o, dout, lse, B, H, N, d, workspace, workspace_bytes, stream)) != FA_OK)
-        return rc;
-    if ((rc = fa_bwd_dkdv(q, k, v, dout, dk, dv, B, H, N, d, scale, causal, workspace, workspace_bytes,
-                          stream)) != FA_OK)
-        return rc;
-    return fa_bwd_dq(q, k, v, dout, dq, B, H, N, d, scale, causal, workspace, workspace_bytes, stream);
+    return fa_bwd_gqa(q, k, v, o, dout, lse, dq, dk, dv, B, H, H, N, d, scale, causal, workspace,
+                      workspace_bytes, stream);
 }
 
 const char* fa_strerror(int code) {
     switch (code) {
         case FA_OK: return "success";
-        case FA_ERR_INVALID_ARG: return "invalid argument (null pointer, B/H/N < 1 or non-finite scale)";
+        case FA_ERR_INVALID_ARG: return "invalid argument (null pointer, B/H/N < 1, non-finite scale, or H_kv not dividing H)";
         case FA_ERR_UNSUPPORTED: return "unsupported shape (d must be 64 or 128, N*H*d < 2^30)";
         case FA_ERR_MISALIGNED: return "pointer not 16-byte aligned";
         case FA_ERR_WORKSPACE: return "workspace null, not 256-byte aligned or smaller than fa_bwd_workspace_size()";

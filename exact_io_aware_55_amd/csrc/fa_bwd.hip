@@ -112,7 +112,7 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(bwd::NT, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const __bf16* __restrict__ dO, const float* __restrict__ stats, int delta_off,
-    __bf16* __restrict__ dK, __bf16* __restrict__ dV, int H, int N, int Npad, float scale,
+    __bf16* __restrict__ dK, __bf16* __restrict__ dV, int H, int G, int N, int Npad, float scale,
     float scale_log2, int nkb) {
     using namespace bwd;
     constexpr int DC = D / 16;                 // k-chunks over features
@@ -137,23 +137,28 @@ __global__ __launch_bounds__(bwd::NT, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     const int l32 = lane & 31, hl = lane >> 5;
     const int tg = lane >> 4, tj = lane & 15;  // transposing-read group and lane
 
+    // one workgroup per (batch, K/V head, key block); with grouped-query
+    // attention the G query heads hk G .. hk G + G - 1 share K/V head hk, and
+    // the workgroup walks the query blocks of all of them (G = 1: one head)
+    const int Hkv = H / G;
     const int logical = xcd_remap_b(blockIdx.x, gridDim.x);
-    const int bh = logical / nkb;
-    const int kb = logical - bh * nkb;
-    const int b = bh / H, h = bh - b * H;
+    const int bhk = logical / nkb;
+    const int kb = logical - bhk * nkb;
+    const int b = bhk / Hkv, hk = bhk - b * Hkv;
     const int row_stride = H * D;
     const unsigned row_bytes = (unsigned)row_stride * 2u;
-    const long head_off = ((long)b * N * H + h) * D;
-    const char* Qh = reinterpret_cast<const char*>(Q + head_off);
-    const char* Kh = reinterpret_cast<const char*>(K + head_off);
-    const char* Vh = reinterpret_cast<const char*>(V + head_off);
-    const char* dOh = reinterpret_cast<const char*>(dO + head_off);
+    const int kv_stride = Hkv * D;
+    const unsigned kv_row_bytes = (unsigned)kv_stride * 2u;
+    const long q_off = ((long)b * N * H + hk * G) * D;   // first query head of the group
+    const long kv_off = ((long)b * N * Hkv + hk) * D;
     const unsigned lds0 = __builtin_amdgcn_readfirstlane(lds_offset(smem));
     const lds_char* L = as_lds(smem);
-    // byte range of one head's rows: loads of rows past N read zeros
-    const unsigned head_bytes = (unsigned)(N - 1) * row_bytes + 2 * D;
-    const __amdgpu_buffer_rsrc_t rQ = byte_rsrc(Qh, head_bytes), rdO = byte_rsrc(dOh, head_bytes);
-    const __amdgpu_buffer_rsrc_t rK = byte_rsrc(Kh, head_bytes), rV = byte_rsrc(Vh, head_bytes);
+    // byte ranges: the group's query heads (adjacent within a row) and the K/V
+    // head; loads of rows past N read zeros
+    const unsigned q_bytes = (unsigned)(N - 1) * row_bytes + 2 * D * G;
+    const unsigned kv_bytes = (unsigned)(N - 1) * kv_row_bytes + 2 * D;
+    const __amdgpu_buffer_rsrc_t rQ = byte_rsrc(Q + q_off, q_bytes), rdO = byte_rsrc(dO + q_off, q_bytes);
+    const __amdgpu_buffer_rsrc_t rK = byte_rsrc(K + kv_off, kv_bytes), rV = byte_rsrc(V + kv_off, kv_bytes);
 
     const int k0 = kb * KB;
     const int key_local = wave * 32 + l32;
@@ -174,7 +179,7 @@ __global__ __launch_bounds__(bwd::NT, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
         const int seg = wave * SEG_KV + i;
         const int sub = seg / (SUBK / 1024), r = (seg % (SUBK / 1024)) * 16 + (lane >> 2);
         // keys past N load as zeros; their columns of dK and dV are never stored
-        const unsigned go = (unsigned)(k0 + r) * row_bytes + sub * 64 + (((lane & 3) ^ dual_swz(r)) << 4);
+        const unsigned go = (unsigned)(k0 + r) * kv_row_bytes + sub * 64 + (((lane & 3) ^ dual_swz(r)) << 4);
         dma16_buf(rK, go, lds0 + seg * 1024);
         dma16_buf(rV, go, lds0 + KVB + seg * 1024);
     }
@@ -196,13 +201,16 @@ __global__ __launch_bounds__(bwd::NT, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     __builtin_amdgcn_s_waitcnt(0xC07F);        // lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
 
-    // ---- query steps: first..nsteps-1, rotated per key block ----
+    // ---- query steps: for each query head g of the group, blocks
+    // first..nsteps-1, rotated per key block ----
     const int nsteps = (N + BR - 1) / BR;
     const int first = CAUSAL ? k0 / BR : 0;
-    const int nst = nsteps - first;
-    const int stagger = nst > 0 ? kb % nst : 0;
-    auto step_of = [&](int it) {
-        int s = it + stagger;
+    const int nst = nsteps - first;            // per query head
+    const int nst_all = G * nst;
+    const int stagger = kb % nst;
+    auto step_of = [&](int it, int& g) {       // query block of step it, and its head
+        g = it / nst;
+        int s = it - g * nst + stagger;
         s = s >= nst ? s - nst : s;
         return first + s;
     };
@@ -217,22 +225,24 @@ __global__ __launch_bounds__(bwd::NT, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
         const int sub = sseg / (SUBQ / 1024), r = (sseg % (SUBQ / 1024)) * 16 + (lane >> 2);
         ld_off[i] = (unsigned)r * row_bytes + sub * 64 + (((lane & 3) ^ dual_swz(r)) << 4);
     }
-    const unsigned st_lane = (unsigned)((bh * Npad + 4 * (lane & 15)) * 4 + ((lane & 16) ? delta_off : 0));
+    const unsigned st_lane = (unsigned)(((b * H + hk * G) * Npad + 4 * (lane & 15)) * 4 + ((lane & 16) ? delta_off : 0));
     // Direct loads of step `it`: where they go (uniform) and load i of them.  A
     // step past the last one reloads step 0 into the spare kilobyte instead.
     struct StepLoads {
         unsigned lds;                          // LDS byte offset of segment 0
         unsigned seg;                          // LDS stride per segment (0: spare)
-        int i0;                                // first query row
-        unsigned row0;                         // its byte offset in the head
+        unsigned row0;                         // byte offset of its first Q/dO row
+        unsigned st0;                          // byte offset of its statistics
     };
     auto step_loads = [&](int it) {
-        const bool real = it < nst;
+        const bool real = it < nst_all;
+        int g;
+        const int i0 = step_of(real ? it : 0, g) * BR;
         StepLoads sl;
         sl.lds = (unsigned)__builtin_amdgcn_readfirstlane(real ? lds0 + (it % NSTAGE) * STAGE : lds0 + RING);
         sl.seg = real ? 1024u : 0u;
-        sl.i0 = __builtin_amdgcn_readfirstlane(step_of(real ? it : 0) * BR);
-        sl.row0 = (unsigned)sl.i0 * row_bytes;
+        sl.row0 = (unsigned)__builtin_amdgcn_readfirstlane((int)((unsigned)i0 * row_bytes + (unsigned)g * 2 * D));
+        sl.st0 = (unsigned)__builtin_amdgcn_readfirstlane((g * Npad + i0) * 4);
         return sl;
     };
     auto issue_load = [&](const StepLoads& sl, int i) {
@@ -240,7 +250,7 @@ __global__ __launch_bounds__(bwd::NT, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
             const int seg = wave * SEG_QO + i;
             dma16_buf(seg < QT / 1024 ? rQ : rdO, sl.row0 + ld_off[i], sl.lds + seg * sl.seg);
         } else {
-            dma16(stats, st_lane + sl.i0 * 4, sl.lds + (2 * QT / 1024 + wave) * sl.seg);
+            dma16(stats, st_lane + sl.st0, sl.lds + (2 * QT / 1024 + wave) * sl.seg);
         }
     };
     {
@@ -263,14 +273,15 @@ __global__ __launch_bounds__(bwd::NT, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     const int a_rd1 = l32 * 64 + (((2 + hl) ^ dual_swz(l32)) << 4);  // odd c
 
 #pragma clang loop unroll(disable)
-    for (int it = 0; it < nst; ++it) {
+    for (int it = 0; it < nst_all; ++it) {
         // this step's loads are done once at most one step's loads are in
         // flight; after the barrier nobody reads the stage of step it - 1,
         // which the loads of step it + 2 (spread over the units below) refill
         FA_WAIT_VMCNT(DMA_W);
         __builtin_amdgcn_s_barrier();
 
-        const int i0 = step_of(it) * BR;
+        int g_unused;
+        const int i0 = step_of(it, g_unused) * BR;
         const StepLoads next = step_loads(it + 2);
 
         const lds_char* stage = L + (it % NSTAGE) * STAGE;
@@ -418,8 +429,8 @@ __global__ __launch_bounds__(bwd::NT, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     // epilogue: dK = scale * (dK^T)^T, dV; C layout of dV^T / dK^T: lane = key
     // column, registers = feature rows 8g + 4h + t
     if (key_ok) {
-        __bf16* dkr = dK + head_off + (long)my_key * row_stride;
-        __bf16* dvr = dV + head_off + (long)my_key * row_stride;
+        __bf16* dkr = dK + kv_off + (long)my_key * kv_stride;
+        __bf16* dvr = dV + kv_off + (long)my_key * kv_stride;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -451,7 +462,7 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(bwdq::NT, 1) void bwd_dq_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const __bf16* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ delta,
-    __bf16* __restrict__ dQ, int H, int N, int Npad, float scale, float scale_log2, int nqb) {
+    __bf16* __restrict__ dQ, int H, int G, int N, int Npad, float scale, float scale_log2, int nqb) {
     using namespace bwdq;
     constexpr int DC = D / 16;
     constexpr int DT = D / 32;
@@ -478,15 +489,18 @@ __global__ __launch_bounds__(bwdq::NT, 1) void bwd_dq_kernel(
     if (CAUSAL) qb = nqb - 1 - qb;             // longest rows first
     const int b = bh / H, h = bh - b * H;
     const int row_stride = H * D;
-    const unsigned row_bytes = (unsigned)row_stride * 2u;
     const long head_off = ((long)b * N * H + h) * D;
     const unsigned lds0 = __builtin_amdgcn_readfirstlane(lds_offset(smem));
     const lds_char* L = as_lds(smem);
+    // grouped-query attention: G query heads share one K/V head (G = 1: one each)
+    const int Hkv = H / G;
+    const unsigned kv_row_bytes = (unsigned)(Hkv * D) * 2u;
+    const long kv_off = ((long)b * N * Hkv + h / G) * D;
     // K and V rows past N load as zeros: such a key then adds dS * 0 to dQ,
     // so ragged tails need no mask
-    const unsigned head_bytes = (unsigned)(N - 1) * row_bytes + 2 * D;
-    const __amdgpu_buffer_rsrc_t rK = byte_rsrc(K + head_off, head_bytes);
-    const __amdgpu_buffer_rsrc_t rV = byte_rsrc(V + head_off, head_bytes);
+    const unsigned kv_bytes = (unsigned)(N - 1) * kv_row_bytes + 2 * D;
+    const __amdgpu_buffer_rsrc_t rK = byte_rsrc(K + kv_off, kv_bytes);
+    const __amdgpu_buffer_rsrc_t rV = byte_rsrc(V + kv_off, kv_bytes);
 
     const int q0 = qb * BR;
     const int qw = q0 + wave * 32;
@@ -504,14 +518,14 @@ __global__ __launch_bounds__(bwdq::NT, 1) void bwd_dq_kernel(
     for (int i = 0; i < SEG_W; ++i) {
         const int seg = wave * SEG_W + i;
         const int sub = seg / SEG_SUB, r = (seg % SEG_SUB) * 16 + (lane >> 2);
-        ld_off[i] = (unsigned)r * row_bytes + sub * 64 + (((lane & 3) ^ dual_swz(r)) << 4);
+        ld_off[i] = (unsigned)r * kv_row_bytes + sub * 64 + (((lane & 3) ^ dual_swz(r)) << 4);
     }
     // direct loads of tile t (a tile past the last one goes to the spare KB)
     auto issue_tile = [&](int t) {
         const bool real = t < ntiles;
         const unsigned kb = __builtin_amdgcn_readfirstlane(real ? lds0 + (t % NSTAGE) * STAGE : lds0 + NSTAGE * STAGE);
         const unsigned segb = real ? 1024u : 0u;
-        const unsigned row0 = (unsigned)(real ? t * BC : 0) * row_bytes;
+        const unsigned row0 = (unsigned)(real ? t * BC : 0) * kv_row_bytes;
 #pragma unroll
         for (int i = 0; i < SEG_W; ++i) {
             const int seg = wave * SEG_W + i;
@@ -654,8 +668,9 @@ hipError_t launch_bwd_preprocess(const void* o, const void* dout, const float* l
 }
 
 hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, void* dk,
-                           void* dv, int B, int H, int N, int d, float scale, bool causal,
+                           void* dv, int B, int H, int Hkv, int N, int d, float scale, bool causal,
                            const float* lse2, const float* delta, hipStream_t stream) {
+    const int G = H / Hkv;
     auto Qp = static_cast<const __bf16*>(q);
     auto Kp = static_cast<const __bf16*>(k);
     auto Vp = static_cast<const __bf16*>(v);
@@ -664,12 +679,12 @@ hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const vo
     auto dVp = static_cast<__bf16*>(dv);
     const int Npad = bwd_rows_padded(N);
     const int nkb = (N + bwd::KB - 1) / bwd::KB;
-    const dim3 grid((unsigned)(B * H * nkb)), block(bwd::NT);
+    const dim3 grid((unsigned)(B * Hkv * nkb)), block(bwd::NT);
     const float sl2 = scale * kLog2e;
     const int delta_off = (int)((const char*)delta - (const char*)lse2);
 #define FA_BWD_LAUNCH(DD, CC)                                                                        \
     hipLaunchKernelGGL((bwd_dkdv_kernel<DD, CC>), grid, block, 0, stream, Qp, Kp, Vp, dOp, lse2,    \
-                       delta_off, dKp, dVp, H, N, Npad, scale, sl2, nkb)
+                       delta_off, dKp, dVp, H, G, N, Npad, scale, sl2, nkb)
     if (d == 128) {
         if (causal) FA_BWD_LAUNCH(128, true);
         else FA_BWD_LAUNCH(128, false);
@@ -682,8 +697,9 @@ hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const vo
 }
 
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dout, void* dq,
-                         int B, int H, int N, int d, float scale, bool causal, const float* lse2,
+                         int B, int H, int Hkv, int N, int d, float scale, bool causal, const float* lse2,
                          const float* delta, hipStream_t stream) {
+    const int G = H / Hkv;
     auto Qp = static_cast<const __bf16*>(q);
     auto Kp = static_cast<const __bf16*>(k);
     auto Vp = static_cast<const __bf16*>(v);
@@ -695,7 +711,7 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void
     const float sl2 = scale * kLog2e;
 #define FA_BWDQ_LAUNCH(DD, CC)                                                                      \
     hipLaunchKernelGGL((bwd_dq_kernel<DD, CC>), grid, block, 0, stream, Qp, Kp, Vp, dOp, lse2,     \
-                       delta, dQp, H, N, Npad, scale, sl2, nqb)
+                       delta, dQp, H, G, N, Npad, scale, sl2, nqb)
     if (d == 128) {
         if (causal) FA_BWDQ_LAUNCH(128, true);
         else FA_BWDQ_LAUNCH(128, false);

@@ -63,7 +63,7 @@ __device__ __forceinline__ int v_swz(int row) { return ((row >> 1) & 1) << 1; }
 template <int D, bool CAUSAL, bool POS>
 __global__ __launch_bounds__(fwd::NT, 1) void fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-    __bf16* __restrict__ O, float* __restrict__ LSE, int H, int N, float scale_log2, int nqb) {
+    __bf16* __restrict__ O, float* __restrict__ LSE, int H, int G, int N, float scale_log2, int nqb) {
     using namespace fwd;
     constexpr int TILE = BC * D * 2;           // one K or V block
     constexpr int STAGE = 2 * TILE;            // K then V
@@ -92,12 +92,15 @@ __global__ __launch_bounds__(fwd::NT, 1) void fwd_bf16_kernel(
     const int b = bh / H, h = bh - b * H;
     const int row_stride = H * D;              // elements between sequence rows (N*H*D < 2^31)
     const long head_off = ((long)b * N * H + h) * D;
-    const unsigned row_bytes = (unsigned)row_stride * 2u;
+    // grouped-query attention: G query heads share one K/V head (G = 1: one each)
+    const int Hkv = H / G;
+    const unsigned kv_row_bytes = (unsigned)(Hkv * D) * 2u;
+    const long kv_off = ((long)b * N * Hkv + h / G) * D;
     // K and V rows past N read zeros (range-checked loads); their scores are
     // masked, so they get weight exactly 0
-    const unsigned head_bytes = (unsigned)(N - 1) * row_bytes + 2 * D;
-    const __amdgpu_buffer_rsrc_t rK = byte_rsrc(K + head_off, head_bytes);
-    const __amdgpu_buffer_rsrc_t rV = byte_rsrc(V + head_off, head_bytes);
+    const unsigned kv_bytes = (unsigned)(N - 1) * kv_row_bytes + 2 * D;
+    const __amdgpu_buffer_rsrc_t rK = byte_rsrc(K + kv_off, kv_bytes);
+    const __amdgpu_buffer_rsrc_t rV = byte_rsrc(V + kv_off, kv_bytes);
 
     const int q0 = qb * BR;
     const int qw = q0 + wave * 32;             // first query of this wave
@@ -118,15 +121,15 @@ __global__ __launch_bounds__(fwd::NT, 1) void fwd_bf16_kernel(
     for (int i = 0; i < SEG_W; ++i) {
         const int seg = wave * SEG_W + i;
         const int sub = seg / SEG_SUB, r = (seg % SEG_SUB) * 16 + lane / 4;
-        k_off[i] = (unsigned)r * row_bytes + sub * 64 + (((lane & 3) ^ k_swz(r)) << 4);
-        v_off[i] = (unsigned)r * row_bytes + sub * 64 + (((lane & 3) ^ v_swz(r)) << 4);
+        k_off[i] = (unsigned)r * kv_row_bytes + sub * 64 + (((lane & 3) ^ k_swz(r)) << 4);
+        v_off[i] = (unsigned)r * kv_row_bytes + sub * 64 + (((lane & 3) ^ v_swz(r)) << 4);
     }
     const unsigned lds0 = __builtin_amdgcn_readfirstlane(lds_offset(smem));
     auto issue_tile = [&](int t) {
         const bool real = t < ntiles;
         const unsigned kb = __builtin_amdgcn_readfirstlane(real ? lds0 + (t % NSTAGE) * STAGE : lds0 + NSTAGE * STAGE);
         const unsigned segb = real ? 1024u : 0u;
-        const unsigned row0 = (unsigned)(real ? t * BC : 0) * row_bytes;
+        const unsigned row0 = (unsigned)(real ? t * BC : 0) * kv_row_bytes;
 #pragma unroll
         for (int i = 0; i < SEG_W; ++i) {
             const int seg = wave * SEG_W + i;
@@ -406,7 +409,8 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(
 // launchers
 // ---------------------------------------------------------------------------
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                           int H, int N, int d, float scale, bool causal, hipStream_t stream) {
+                           int H, int Hkv, int N, int d, float scale, bool causal, hipStream_t stream) {
+    const int G = H / Hkv;
     const int nqb = (N + fwd::BR - 1) / fwd::BR;
     const dim3 grid((unsigned)(B * H * nqb)), block(fwd::NT);
     const float sl2 = scale * kLog2e;
@@ -414,7 +418,7 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
     auto Kp = static_cast<const __bf16*>(k);
     auto Vp = static_cast<const __bf16*>(v);
     auto Op = static_cast<__bf16*>(o);
-    auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, block, 0, stream, Qp, Kp, Vp, Op, lse, H, N, sl2, nqb); };
+    auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, block, 0, stream, Qp, Kp, Vp, Op, lse, H, G, N, sl2, nqb); };
     const bool pos = sl2 >= 0.f;
     if (d == 128) {
         if (causal) pos ? go(fwd_bf16_kernel<128, true, true>) : go(fwd_bf16_kernel<128, true, false>);

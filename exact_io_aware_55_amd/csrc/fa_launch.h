@@ -7,8 +7,10 @@
 
 namespace fa {
 
+// Hkv: K/V heads (H for multi-head attention; H a multiple of Hkv).  Query
+// head h uses K/V head h / (H / Hkv).
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                           int H, int N, int d, float scale, bool causal, hipStream_t stream);
+                           int H, int Hkv, int N, int d, float scale, bool causal, hipStream_t stream);
 
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B,
                           int H, int N, int d, float scale, bool causal, hipStream_t stream);
@@ -20,10 +22,10 @@ int bwd_rows_padded(int N);
 hipError_t launch_bwd_preprocess(const void* o, const void* dout, const float* lse, int B, int H,
                                  int N, int d, float* lse2, float* delta, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, void* dk,
-                           void* dv, int B, int H, int N, int d, float scale, bool causal,
+                           void* dv, int B, int H, int Hkv, int N, int d, float scale, bool causal,
                            const float* lse2, const float* delta, hipStream_t stream);
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dout, void* dq,
-                         int B, int H, int N, int d, float scale, bool causal, const float* lse2,
+                         int B, int H, int Hkv, int N, int d, float scale, bool causal, const float* lse2,
                          const float* delta, hipStream_t stream);
 
 }  // namespace fa

@@ -2,8 +2,9 @@
 
 This module holds no attention arithmetic: it only draws random tensors.
 Recipe: a CPU ``torch.Generator`` seeded with ``seed`` draws i.i.d. N(0, 1)
-fp32 tensors of shape [B, N, H, d] in the order Q, K, V, dO (dO only when
-asked), optionally multiplied by ``gain``, then cast to the requested dtype
+fp32 tensors of shape [B, N, H, d] (K and V: [B, N, H_kv, d] for grouped K/V
+heads) in the order Q, K, V, dO (dO only when asked), optionally multiplied
+by ``gain``, then cast to the requested dtype
 (bf16 casts round to nearest even).  The oracle is fed the cast values
 upcast to fp64, which is exact for both fp32 and bf16.
 """
@@ -16,13 +17,16 @@ import torch
 __all__ = ["make_qkv", "to_f64"]
 
 
-def make_qkv(B, N, H, d, dtype=torch.bfloat16, seed=0, with_do=False, gain=1.0):
-    """Return a dict with CPU tensors 'q', 'k', 'v' (and 'do') of shape [B,N,H,d]."""
+def make_qkv(B, N, H, d, dtype=torch.bfloat16, seed=0, with_do=False, gain=1.0, H_kv=None):
+    """Return a dict with CPU tensors 'q', 'k', 'v' (and 'do') of shape [B,N,H,d];
+    with ``H_kv`` (grouped K/V heads) 'k' and 'v' are [B,N,H_kv,d]."""
     g = torch.Generator().manual_seed(int(seed))
     names = ["q", "k", "v"] + (["do"] if with_do else [])
+    hkv = H if H_kv is None else H_kv
     out = {}
     for name in names:
-        t = torch.randn((B, N, H, d), generator=g, dtype=torch.float32)
+        heads = hkv if name in ("k", "v") else H
+        t = torch.randn((B, N, heads, d), generator=g, dtype=torch.float32)
         if gain != 1.0:
             t = t * gain
         out[name] = t.to(dtype).contiguous()

@@ -59,7 +59,8 @@ typedef struct ihipStream_t* hipStream_t;
 
 enum {
     FA_OK = 0,
-    FA_ERR_INVALID_ARG = -1, /* null pointer, B/H/N < 1, non-finite scale */
+    FA_ERR_INVALID_ARG = -1, /* null pointer, B/H/N < 1, non-finite scale,
+                                H_kv < 1 or not dividing H (GQA calls) */
     FA_ERR_UNSUPPORTED = -2, /* d not in {64, 128}, or N*H*d >= 2^30     */
     FA_ERR_MISALIGNED = -3,  /* a pointer not 16-byte aligned             */
     FA_ERR_WORKSPACE = -4,   /* workspace null, misaligned or too small   */
@@ -117,6 +118,25 @@ int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
 int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, void* dq,
               int B, int H, int N, int d, float scale, int causal,
               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Grouped-query attention (explainer page "Flash Attention", section
+ * "Varianten und Erweiterungen", subsection "Grouped Query Attention": several
+ * query heads share one K/V head).  q, o, dout, dq: [B,N,H,d]; k, v, dk, dv:
+ * [B,N,H_kv,d]; lse: [B,H,N]; H must be a multiple of H_kv, and query head h
+ * uses K/V head h / (H / H_kv) (contiguous groups).  H_kv = H is multi-head
+ * attention (fa_fwd / fa_bwd are exactly that call); H_kv = 1 is multi-query
+ * attention.  dk and dv sum over the query heads of a group; every gradient
+ * is still written once by one workgroup.  Workspace: fa_bwd_workspace_size(
+ * B, H, N, d) bytes (statistics are per query head).  Same errors, limits
+ * and stream semantics as fa_fwd / fa_bwd, plus FA_ERR_INVALID_ARG for an
+ * H_kv that does not divide H.  The dK/dV kernel runs one workgroup per
+ * (batch, K/V head, 128 keys), so small B * H_kv * N fill few compute units. */
+int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int H_kv, int N, int d, float scale, int causal, hipStream_t stream);
+int fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const void* dout,
+               const float* lse, void* dq, void* dk, void* dv,
+               int B, int H, int H_kv, int N, int d, float scale, int causal,
+               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Human-readable text for a return code (static storage). */
 const char* fa_strerror(int code);

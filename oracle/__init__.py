@@ -13,4 +13,5 @@ from .attention import (  # noqa: F401
     head_forward,
     head_forward_blockwise,
     head_probabilities,
+    kv_head,
 )

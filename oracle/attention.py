@@ -37,6 +37,15 @@ Delta is taken in its definition form (a row sum over the N x N product); the
 GPU path uses the equivalent row dot product of dO and O.
 
 Tensors use the [B, N, H, d] layout; LSE uses [B, H, N].
+
+Grouped-query attention (explainer page "Flash Attention", section "Varianten
+und Erweiterungen", subsection "Grouped Query Attention": several query heads
+share one K/V group): K and V may have H_kv heads with H a multiple of H_kv.
+The page does not say which query heads form a group; the reading taken is
+contiguous groups, query head h reading K/V head h // (H / H_kv).  Each query
+head is then ordinary attention against its group's K and V, and the gradient
+of a shared K/V head is the sum of its query heads' gradients (the chain rule
+over a tensor used G times).
 """
 
 from __future__ import annotations
@@ -44,6 +53,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
+    "kv_head",
     "head_forward",
     "head_backward",
     "head_forward_blockwise",
@@ -167,6 +177,13 @@ def head_forward_blockwise(q, k, v, scale, causal, block, dtype=np.float64):
     return o, lse, largest_tile
 
 
+def kv_head(h, H, H_kv):
+    """K/V head read by query head h (contiguous groups of H / H_kv)."""
+    if H_kv < 1 or H % H_kv:
+        raise ValueError("H must be a multiple of H_kv")
+    return h // (H // H_kv)
+
+
 def _heads_of(b, h, heads):
     if heads is None:
         return [(bi, hi) for bi in range(b) for hi in range(h)]
@@ -180,10 +197,12 @@ def forward(q, k, v, scale, causal, heads=None):
     other entries of the outputs are NaN.
     """
     B, N, H, d = q.shape
+    Hkv = k.shape[2]
     o = np.full((B, N, H, v.shape[3]), np.nan)
     lse = np.full((B, H, N), np.nan)
     for b, h in _heads_of(B, H, heads):
-        oh, lh = head_forward(q[b, :, h, :], k[b, :, h, :], v[b, :, h, :], scale, causal)
+        g = kv_head(h, H, Hkv)
+        oh, lh = head_forward(q[b, :, h, :], k[b, :, g, :], v[b, :, g, :], scale, causal)
         o[b, :, h, :] = oh
         lse[b, h, :] = lh
     return o, lse
@@ -199,8 +218,10 @@ def forward_rows(q, k, v, scale, causal, picks):
     """
     out_o = []
     out_l = []
+    H, Hkv = q.shape[2], k.shape[2]
     for b, h, i in picks:
-        oh, lh = head_forward(q[b, :, h, :], k[b, :, h, :], v[b, :, h, :], scale, causal,
+        g = kv_head(h, H, Hkv)
+        oh, lh = head_forward(q[b, :, h, :], k[b, :, g, :], v[b, :, g, :], scale, causal,
                               rows=[i])
         out_o.append(oh[0])
         out_l.append(lh[0])
@@ -208,19 +229,26 @@ def forward_rows(q, k, v, scale, causal, picks):
 
 
 def backward(q, k, v, do, scale, causal, heads=None):
-    """[B,N,H,d] backward.  Returns dQ, dK, dV in fp64 ([B,N,H,d]).
+    """Backward.  Returns dQ ([B,N,H,d]), dK and dV (shaped like k and v) in
+    fp64.  With grouped K/V heads a K/V head's gradient sums over its query
+    heads.
 
-    ``heads`` optionally restricts the work to a list of (b, h) pairs; the
-    other entries are NaN.
+    ``heads`` optionally restricts the work to a list of (b, h) pairs; entries
+    no listed head touches are NaN.
     """
     B, N, H, d = q.shape
+    Hkv = k.shape[2]
     dq = np.full(q.shape, np.nan)
     dk = np.full(k.shape, np.nan)
     dv = np.full(v.shape, np.nan)
     for b, h in _heads_of(B, H, heads):
-        a, bb, c = head_backward(q[b, :, h, :], k[b, :, h, :], v[b, :, h, :],
+        g = kv_head(h, H, Hkv)
+        a, bb, c = head_backward(q[b, :, h, :], k[b, :, g, :], v[b, :, g, :],
                                  do[b, :, h, :], scale, causal)
         dq[b, :, h, :] = a
-        dk[b, :, h, :] = bb
-        dv[b, :, h, :] = c
+        if np.isnan(dk[b, 0, g, 0]):
+            dk[b, :, g, :] = 0.0
+            dv[b, :, g, :] = 0.0
+        dk[b, :, g, :] += bb
+        dv[b, :, g, :] += c
     return dq, dk, dv

@@ -66,6 +66,24 @@ def test_forward_argument_errors(lib, fn):
         assert _fwd(lib, fn, ptrs) == binding.FA_ERR_MISALIGNED
 
 
+def test_gqa_argument_errors(lib):
+    """H_kv must divide H; otherwise the same checks as the multi-head calls."""
+    V = ctypes.c_void_p
+    f = lib.fa_fwd_gqa
+    p5 = [V(FAKE)] * 5
+    for hkv in (0, -1, 4, 7):                      # with H = 6
+        assert f(*p5, 1, 6, hkv, 8, 64, 0.1, 0, None) == binding.FA_ERR_INVALID_ARG
+    assert f(*p5, 1, 6, 3, 8, 96, 0.1, 0, None) == binding.FA_ERR_UNSUPPORTED
+    assert f(V(FAKE), V(FAKE + 4), *p5[2:], 1, 6, 3, 8, 64, 0.1, 0, None) == binding.FA_ERR_MISALIGNED
+    g = lib.fa_bwd_gqa
+    p9 = [V(FAKE)] * 9
+    need = lib.fa_bwd_workspace_size(1, 6, 8, 64)
+    assert g(*p9, 1, 6, 4, 8, 64, 0.1, 0, V(FAKE), need, None) == binding.FA_ERR_INVALID_ARG
+    assert g(*p9, 1, 6, 0, 8, 64, 0.1, 0, V(FAKE), need, None) == binding.FA_ERR_INVALID_ARG
+    assert g(*p9, 1, 6, 2, 8, 64, 0.1, 0, V(FAKE), need - 1, None) == binding.FA_ERR_WORKSPACE
+    assert g(*p9[:8], None, 1, 6, 2, 8, 64, 0.1, 0, V(FAKE), need, None) == binding.FA_ERR_INVALID_ARG
+
+
 def test_workspace_size(lib):
     def want(B, H, N, d):
         a256 = lambda x: (x + 255) // 256 * 256

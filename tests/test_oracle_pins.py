@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import (backward, forward, forward_rows, head_backward, head_forward,
+from oracle import (backward, forward, forward_rows, head_backward, head_forward, kv_head,
                     head_forward_blockwise, head_probabilities)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -366,3 +366,88 @@ def test_finite_differences_catch_backward_mistakes():
     assert np.abs(num - wrong_dk).max() > 1e-3
     wrong_dq = ds @ k                  # scale dropped
     assert np.abs(wrong_dq - dq).max() > 1e-3
+
+
+# --------------------------------------------------------------------------
+# Grouped-query attention (explainer page "Flash Attention", section
+# "Varianten und Erweiterungen", subsection "Grouped Query Attention")
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("H,Hkv", [(4, 2), (6, 3), (4, 1), (3, 3)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_forward_is_attention_on_repeated_kv(H, Hkv, causal):
+    """Explicit construction: each K/V head copied to its H / H_kv query heads
+    (contiguous groups, numpy's repeat) gives ordinary multi-head attention."""
+    B, N, d = 2, 7, 5
+    q = rnd(B, N, H, d, seed=60)
+    k, v = rnd(B, N, Hkv, d, seed=61), rnd(B, N, Hkv, d, seed=62)
+    o, lse = forward(q, k, v, 0.6, causal)
+    G = H // Hkv
+    o_ref, lse_ref = forward(q, np.repeat(k, G, axis=2), np.repeat(v, G, axis=2), 0.6, causal)
+    assert np.array_equal(o, o_ref) and np.array_equal(lse, lse_ref)
+    ro, rl = forward_rows(q, k, v, 0.6, causal, [(1, H - 1, N - 1), (0, 0, 3)])
+    assert np.allclose(ro[0], o[1, N - 1, H - 1], atol=1e-14) and np.isclose(rl[1], lse[0, 0, 3])
+
+
+@pytest.mark.parametrize("H,Hkv", [(4, 2), (4, 1)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_backward_torch_autograd(H, Hkv, causal):
+    """Independent library: torch.autograd in fp64 through repeat_interleave
+    of the K/V heads, so the shared heads' gradients are summed by autograd."""
+    B, N, d = 2, 9, 4
+    qn = rnd(B, N, H, d, seed=63)
+    kn, vn = rnd(B, N, Hkv, d, seed=64), rnd(B, N, Hkv, d, seed=65)
+    don = rnd(B, N, H, d, seed=66)
+    dq, dk, dv = backward(qn, kn, vn, don, 0.5, causal)
+    q, k, v = (torch.tensor(a, requires_grad=True) for a in (qn, kn, vn))
+    kr, vr = (t.repeat_interleave(H // Hkv, dim=2) for t in (k, v))
+    s = torch.einsum("bihd,bjhd->bhij", q, kr) * 0.5
+    if causal:
+        s = s.masked_fill(torch.triu(torch.ones(N, N, dtype=torch.bool), 1), float("-inf"))
+    o = torch.einsum("bhij,bjhd->bihd", torch.softmax(s, -1), vr)
+    (o * torch.from_numpy(don)).sum().backward()
+    for mine, ref in ((dq, q.grad), (dk, k.grad), (dv, v.grad)):
+        assert mine.shape == ref.shape
+        assert np.abs(mine - ref.numpy()).max() <= 1e-10
+
+
+def test_gqa_backward_finite_differences():
+    """Brute force on a shared K/V head: central differences of sum(O * dO)
+    over all query heads of the group."""
+    B, N, H, Hkv, d = 1, 4, 3, 1, 2
+    q, do = rnd(B, N, H, d, seed=67), rnd(B, N, H, d, seed=68)
+    k, v = rnd(B, N, Hkv, d, seed=69), rnd(B, N, Hkv, d, seed=70)
+    _, dk, dv = backward(q, k, v, do, 0.9, True)
+
+    def loss():
+        o, _ = forward(q, k, v, 0.9, True)
+        return float((o * do).sum())
+
+    h = 1e-6
+    for x, g in ((k, dk), (v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            keep = x[idx]
+            x[idx] = keep + h
+            lp = loss()
+            x[idx] = keep - h
+            lm = loss()
+            x[idx] = keep
+            num[idx] = (lp - lm) / (2 * h)
+        assert np.abs(num - g).max() / np.abs(g).max() <= 1e-6
+
+
+def test_gqa_group_mapping_mistake_is_caught():
+    """A plausible mistake (interleaved groups, h % H_kv) fails the repeat pin."""
+    B, N, H, Hkv, d = 1, 5, 4, 2, 3
+    q = rnd(B, N, H, d, seed=71)
+    k, v = rnd(B, N, Hkv, d, seed=72), rnd(B, N, Hkv, d, seed=73)
+    o_ref, _ = forward(q, np.repeat(k, 2, axis=2), np.repeat(v, 2, axis=2), 0.7, False)
+    wrong = np.stack([head_forward(q[0, :, h], k[0, :, h % Hkv], v[0, :, h % Hkv], 0.7, False)[0]
+                      for h in range(H)], axis=1)
+    assert np.abs(wrong - o_ref[0]).max() > 1e-3
+
+
+def test_gqa_rejects_non_dividing_heads():
+    with pytest.raises(ValueError):
+        kv_head(1, 4, 3)
