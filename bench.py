@@ -119,41 +119,44 @@ def naive_step(torch, q, k, v, do, scale, causal):
 
 # Workloads reported beside the headline one (parity-test shapes of the
 # same kernels): forward and backward timed separately, median of 5.
-# (name, B, H, H_kv, N, d, causal); the last one is grouped-query attention
-# with the pages' Llama 2 70B head counts (64 query heads over 8 K/V heads).
+# (name, B, H, H_kv, N, d, causal, window): grouped-query attention with the
+# pages' Llama 2 70B head counts (64 query heads over 8 K/V heads), and a
+# causal sliding window of 4096 over 32768 tokens (the pages' Mistral 7B
+# example; flops counted over the visible pairs only).
 EXTRA_WORKLOADS = [
-    ("b4_h32_n4096_d128_causal", 4, 32, 32, 4096, 128, True),
-    ("b1_h32_n16384_d128_causal", 1, 32, 32, 16384, 128, True),
-    ("b4_h16_n4096_d64_causal", 4, 16, 16, 4096, 64, True),
-    ("b2_h64_hkv8_n4096_d128_causal_gqa", 2, 64, 8, 4096, 128, True),
+    ("b4_h32_n4096_d128_causal", 4, 32, 32, 4096, 128, True, None),
+    ("b1_h32_n16384_d128_causal", 1, 32, 32, 16384, 128, True, None),
+    ("b4_h16_n4096_d64_causal", 4, 16, 16, 4096, 64, True, None),
+    ("b2_h64_hkv8_n4096_d128_causal_gqa", 2, 64, 8, 4096, 128, True, None),
+    ("b1_h32_n32768_d128_window4096", 1, 32, 32, 32768, 128, True, 4096),
 ]
 
 
 def other_workloads(torch, binding, inputs, workloads, seed):
     out = {}
     dev = torch.device("cuda:0")
-    for name, B, H, Hkv, N, d, causal in EXTRA_WORKLOADS:
+    for name, B, H, Hkv, N, d, causal, window in EXTRA_WORKLOADS:
         x = inputs.make_qkv(B, N, H, d, torch.bfloat16, seed=seed, with_do=True, H_kv=Hkv)
         q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "do"))
-        o, lse = binding.forward(q, k, v, causal=causal)
-        if Hkv == H:
+        o, lse = binding.forward(q, k, v, causal=causal, window=window)
+        if Hkv == H and window is None:
             _, calls = binding.backward_steps(q, k, v, o, do, lse, causal=causal)
         else:
             ws = torch.empty(binding.bwd_workspace_size(B, H, N, d), device=dev, dtype=torch.uint8)
             grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
             calls = [lambda: binding.backward(q, k, v, o, do, lse, causal=causal, workspace=ws,
-                                              out=grads)]
+                                              out=grads, window=window)]
 
         def fwd():
-            binding.forward(q, k, v, causal=causal, out=o, lse=lse)
+            binding.forward(q, k, v, causal=causal, out=o, lse=lse, window=window)
 
         def bwd():
             for c in calls:
                 c()
 
         res = {}
-        for tag, f, fl in (("fwd", fwd, workloads.fwd_flops(B, H, N, d, causal)),
-                           ("bwd", bwd, workloads.bwd_flops(B, H, N, d, causal))):
+        for tag, f, fl in (("fwd", fwd, workloads.fwd_flops(B, H, N, d, causal, window)),
+                           ("bwd", bwd, workloads.bwd_flops(B, H, N, d, causal, window))):
             for _ in range(2):
                 f()
             ms = []
@@ -167,6 +170,8 @@ def other_workloads(torch, binding, inputs, workloads, seed):
             med = sorted(ms)[2]
             res[f"{tag}_ms"] = round(med, 4)
             res[f"{tag}_tflops"] = round(fl / (med * 1e-3) / 1e12, 1)
+        if window is not None:
+            res["pairs_skipped_frac"] = round(1 - workloads.window_pairs(N, window) / N ** 2, 4)
         out[name] = res
         del q, k, v, do, o, lse, calls
         torch.cuda.empty_cache()

@@ -18,7 +18,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfa.so")
 
 EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_bwd_workspace_size", "fa_bwd", "fa_bwd_preprocess",
-           "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_gqa", "fa_bwd_gqa", "fa_strerror")
+           "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_gqa", "fa_bwd_gqa", "fa_fwd_window", "fa_bwd_window",
+           "fa_strerror")
 
 FA_OK = 0
 FA_ERR_INVALID_ARG = -1
@@ -59,6 +60,10 @@ def load(path: str = LIB_PATH):
     lib.fa_fwd_gqa.restype = i
     lib.fa_bwd_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
     lib.fa_bwd_gqa.restype = i
+    lib.fa_fwd_window.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+    lib.fa_fwd_window.restype = i
+    lib.fa_bwd_window.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
+    lib.fa_bwd_window.restype = i
     lib.fa_strerror.argtypes = [i]
     lib.fa_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -112,16 +117,21 @@ def _scale(scale, d):
     return float(d) ** -0.5 if scale is None else float(scale)
 
 
-def forward(q, k, v, causal=False, scale=None, out=None, lse=None):
+def forward(q, k, v, causal=False, scale=None, out=None, lse=None, window=None):
     """bf16 forward.  Returns (O [B,N,H,d] bf16, LSE [B,H,N] fp32).
 
     k and v may have fewer heads than q (grouped-query attention: [B,N,H_kv,d]
-    with H a multiple of H_kv); that calls fa_fwd_gqa, else fa_fwd."""
+    with H a multiple of H_kv); that calls fa_fwd_gqa, else fa_fwd.  ``window``
+    (causal sliding window: query i sees keys i - window < j <= i) calls
+    fa_fwd_window and implies causal."""
     lib = load()
     B, N, H, Hkv, d = _check_gqa(torch.bfloat16, (q,), (k, v))
     o = torch.empty_like(q) if out is None else out
     lse_t = torch.empty((B, H, N), device=q.device, dtype=torch.float32) if lse is None else lse
-    if Hkv == H:
+    if window is not None:
+        _check(lib.fa_fwd_window(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), B, H, Hkv, N, d,
+                                 _scale(scale, d), int(window), _stream()))
+    elif Hkv == H:
         _check(lib.fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), B, H, N, d,
                           _scale(scale, d), int(bool(causal)), _stream()))
     else:
@@ -145,10 +155,10 @@ def bwd_workspace_size(B, H, N, d) -> int:
     return int(load().fa_bwd_workspace_size(B, H, N, d))
 
 
-def backward(q, k, v, o, do, lse, causal=False, scale=None, workspace=None, out=None):
+def backward(q, k, v, o, do, lse, causal=False, scale=None, workspace=None, out=None, window=None):
     """bf16 backward by recomputation.  Returns (dQ, dK, dV), bf16, shaped like
     q, k and v (grouped-query attention when k and v have fewer heads: then
-    fa_bwd_gqa, else fa_bwd)."""
+    fa_bwd_gqa, else fa_bwd; ``window`` as in :func:`forward`: fa_bwd_window)."""
     lib = load()
     B, N, H, Hkv, d = _check_gqa(torch.bfloat16, (q, o, do), (k, v))
     if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
@@ -159,7 +169,11 @@ def backward(q, k, v, o, do, lse, causal=False, scale=None, workspace=None, out=
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     else:
         dq, dk, dv = out
-    if Hkv == H:
+    if window is not None:
+        _check(lib.fa_bwd_window(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
+                                 _ptr(dk), _ptr(dv), B, H, Hkv, N, d, _scale(scale, d), int(window),
+                                 _ptr(ws), ws.numel() * ws.element_size(), _stream()))
+    elif Hkv == H:
         _check(lib.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk),
                           _ptr(dv), B, H, N, d, _scale(scale, d), int(bool(causal)), _ptr(ws),
                           ws.numel() * ws.element_size(), _stream()))

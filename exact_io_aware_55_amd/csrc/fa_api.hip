@@ -54,14 +54,29 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
     return fa_fwd_gqa(q, k, v, o, lse, B, H, H, N, d, scale, causal, stream);
 }
 
-int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int H_kv,
-               int N, int d, float scale, int causal, hipStream_t stream) {
+namespace {
+// window > 0: causal sliding window; 0: none
+int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int H_kv,
+             int N, int d, float scale, int causal, int window, hipStream_t stream) {
     int rc = fwd_common(q, k, v, o, lse, B, H, N, d, scale);
     if (rc != FA_OK) return rc;
     if ((rc = check_groups(H, H_kv)) != FA_OK) return rc;
-    if (fa::launch_fwd_bf16(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal != 0, stream) != hipSuccess)
+    if (fa::launch_fwd_bf16(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal != 0, window, stream) !=
+        hipSuccess)
         return FA_ERR_LAUNCH;
     return FA_OK;
+}
+}  // namespace
+
+int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int H_kv,
+               int N, int d, float scale, int causal, hipStream_t stream) {
+    return fwd_impl(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal, 0, stream);
+}
+
+int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                  int H_kv, int N, int d, float scale, int window, hipStream_t stream) {
+    if (window < 1) return FA_ERR_INVALID_ARG;
+    return fwd_impl(q, k, v, o, lse, B, H, H_kv, N, d, scale, 1, window, stream);
 }
 
 int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H,
@@ -130,30 +145,30 @@ int fa_bwd_preprocess(const void* o, const void* dout, const float* lse, int B, 
 
 namespace {
 int bwd_dkdv_impl(const void* q, const void* k, const void* v, const void* dout, void* dk, void* dv,
-                  int B, int H, int H_kv, int N, int d, float scale, int causal, void* workspace,
-                  size_t workspace_bytes, hipStream_t stream) {
+                  int B, int H, int H_kv, int N, int d, float scale, int causal, int window,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
     int rc = all_aligned({q, k, v, dout, dk, dv});
     if (rc != FA_OK) return rc;
     if ((rc = check_bwd_shape(B, H, N, d, scale)) != FA_OK) return rc;
     if ((rc = check_groups(H, H_kv)) != FA_OK) return rc;
     Workspace ws;
     if ((rc = check_workspace(workspace, workspace_bytes, B, H, N, d, &ws)) != FA_OK) return rc;
-    if (fa::launch_bwd_dkdv(q, k, v, dout, dk, dv, B, H, H_kv, N, d, scale, causal != 0, ws.lse2,
+    if (fa::launch_bwd_dkdv(q, k, v, dout, dk, dv, B, H, H_kv, N, d, scale, causal != 0, window, ws.lse2,
                             ws.delta, stream) != hipSuccess)
         return FA_ERR_LAUNCH;
     return FA_OK;
 }
 
 int bwd_dq_impl(const void* q, const void* k, const void* v, const void* dout, void* dq, int B, int H,
-                int H_kv, int N, int d, float scale, int causal, void* workspace, size_t workspace_bytes,
-                hipStream_t stream) {
+                int H_kv, int N, int d, float scale, int causal, int window, void* workspace,
+                size_t workspace_bytes, hipStream_t stream) {
     int rc = all_aligned({q, k, v, dout, dq});
     if (rc != FA_OK) return rc;
     if ((rc = check_bwd_shape(B, H, N, d, scale)) != FA_OK) return rc;
     if ((rc = check_groups(H, H_kv)) != FA_OK) return rc;
     Workspace ws;
     if ((rc = check_workspace(workspace, workspace_bytes, B, H, N, d, &ws)) != FA_OK) return rc;
-    if (fa::launch_bwd_dq(q, k, v, dout, dq, B, H, H_kv, N, d, scale, causal != 0, ws.lse2, ws.delta,
+    if (fa::launch_bwd_dq(q, k, v, dout, dq, B, H, H_kv, N, d, scale, causal != 0, window, ws.lse2, ws.delta,
                           stream) != hipSuccess)
         return FA_ERR_LAUNCH;
     return FA_OK;
@@ -163,19 +178,22 @@ int bwd_dq_impl(const void* q, const void* k, const void* v, const void* dout, v
 int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, void* dk, void* dv, int B,
                 int H, int N, int d, float scale, int causal, void* workspace, size_t workspace_bytes,
                 hipStream_t stream) {
-    return bwd_dkdv_impl(q, k, v, dout, dk, dv, B, H, H, N, d, scale, causal, workspace, workspace_bytes,
-                         stream);
+    return bwd_dkdv_impl(q, k, v, dout, dk, dv, B, H, H, N, d, scale, causal, 0, workspace,
+                         workspace_bytes, stream);
 }
 
 int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, void* dq, int B, int H,
               int N, int d, float scale, int causal, void* workspace, size_t workspace_bytes,
               hipStream_t stream) {
-    return bwd_dq_impl(q, k, v, dout, dq, B, H, H, N, d, scale, causal, workspace, workspace_bytes, stream);
+    return bwd_dq_impl(q, k, v, dout, dq, B, H, H, N, d, scale, causal, 0, workspace, workspace_bytes,
+                       stream);
 }
 
-int fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const void* dout,
-               const float* lse, void* dq, void* dk, void* dv, int B, int H, int H_kv, int N, int d,
-               float scale, int causal, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+namespace {
+int bwd_impl(const void* q, const void* k, const void* v, const void* o, const void* dout,
+             const float* lse, void* dq, void* dk, void* dv, int B, int H, int H_kv, int N, int d,
+             float scale, int causal, int window, void* workspace, size_t workspace_bytes,
+             hipStream_t stream) {
     // validate everything before the first launch
     int rc = all_aligned({q, k, v, o, dout, lse, dq, dk, dv});
     if (rc != FA_OK) return rc;
@@ -185,11 +203,27 @@ int fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const
     if ((rc = check_workspace(workspace, workspace_bytes, B, H, N, d, &ws)) != FA_OK) return rc;
     if ((rc = fa_bwd_preprocess(o, dout, lse, B, H, N, d, workspace, workspace_bytes, stream)) != FA_OK)
         return rc;
-    if ((rc = bwd_dkdv_impl(q, k, v, dout, dk, dv, B, H, H_kv, N, d, scale, causal, workspace,
+    if ((rc = bwd_dkdv_impl(q, k, v, dout, dk, dv, B, H, H_kv, N, d, scale, causal, window, workspace,
                             workspace_bytes, stream)) != FA_OK)
         return rc;
-    return bwd_dq_impl(q, k, v, dout, dq, B, H, H_kv, N, d, scale, causal, workspace, workspace_bytes,
-                       stream);
+    return bwd_dq_impl(q, k, v, dout, dq, B, H, H_kv, N, d, scale, causal, window, workspace,
+                       workspace_bytes, stream);
+}
+}  // namespace
+
+int fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const void* dout,
+               const float* lse, void* dq, void* dk, void* dv, int B, int H, int H_kv, int N, int d,
+               float scale, int causal, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, B, H, H_kv, N, d, scale, causal, 0, workspace,
+                    workspace_bytes, stream);
+}
+
+int fa_bwd_window(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                  const float* lse, void* dq, void* dk, void* dv, int B, int H, int H_kv, int N, int d,
+                  float scale, int window, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (window < 1) return FA_ERR_INVALID_ARG;
+    return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, B, H, H_kv, N, d, scale, 1, window, workspace,
+                    workspace_bytes, stream);
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,

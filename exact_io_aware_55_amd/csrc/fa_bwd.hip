@@ -112,8 +112,8 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(bwd::NT, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const __bf16* __restrict__ dO, const float* __restrict__ stats, int delta_off,
-    __bf16* __restrict__ dK, __bf16* __restrict__ dV, int H, int G, int N, int Npad, float scale,
-    float scale_log2, int nkb) {
+    __bf16* __restrict__ dK, __bf16* __restrict__ dV, int H, int G, int N, int window, int Npad,
+    float scale, float scale_log2, int nkb) {
     using namespace bwd;
     constexpr int DC = D / 16;                 // k-chunks over features
     constexpr int DT = D / 32;                 // 32-feature sub-tiles
@@ -203,9 +203,12 @@ __global__ __launch_bounds__(bwd::NT, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
 
     // ---- query steps: for each query head g of the group, blocks
     // first..nsteps-1, rotated per key block ----
+    // causal: queries k0 .. k0 + KB - 1 + window - 1 can see these keys
+    // (query i sees keys j with i - window < j <= i; window >= N: plain causal)
     const int nsteps = (N + BR - 1) / BR;
     const int first = CAUSAL ? k0 / BR : 0;
-    const int nst = nsteps - first;            // per query head
+    const int last = CAUSAL ? min(nsteps - 1, (k0 + KB - 2 + window) / BR) : nsteps - 1;
+    const int nst = last - first + 1;          // per query head
     const int nst_all = G * nst;
     const int stagger = kb % nst;
     auto step_of = [&](int it, int& g) {       // query block of step it, and its head
@@ -297,10 +300,12 @@ __global__ __launch_bounds__(bwd::NT, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
         // either: column j of dV^T and dK^T only depends on column j of P and
         // dS, and those columns are never stored.  So only the causal mask
         // remains: the query of register r of half m, i0 + 4 hl + 32m +
-        // 8(r>>2) + (r&3), must not precede the lane's key.  It is applied on
-        // every step, as a second copy of the step for the diagonal blocks
-        // would cost more in register moves than the compares.
+        // 8(r>>2) + (r&3), must not precede the lane's key (nor, with a
+        // sliding window, reach window rows past it).  It is applied on every
+        // step, as a second copy of the step for the diagonal blocks would
+        // cost more in register moves than the compares.
         const int lim_c = my_key - i0 - 4 * hl;
+        const int lim_w = lim_c + window - 1;      // window: query < key + window
         // One step, software-pipelined by hand.  With one wave per SIMD
         // nothing else hides LDS latency, so the step is cut into NU units of
         // two MFMAs each; the operand reads of unit u + PF and the statistics
@@ -370,7 +375,7 @@ __global__ __launch_bounds__(bwd::NT, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
                             if constexpr (MASK) {
                                 // hidden pairs get exp2(-inf) = 0, and so dS = 0 as dP is finite
                                 const int off = 32 * m + 8 * (rr >> 2) + (rr & 3);
-                                const bool vis = off >= lim_c;
+                                const bool vis = (off >= lim_c) & (off <= lim_w);
                                 x = vis ? x : -INFINITY;
                             }
                             const float p = fast_exp2(x);
@@ -462,7 +467,8 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(bwdq::NT, 1) void bwd_dq_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const __bf16* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ delta,
-    __bf16* __restrict__ dQ, int H, int G, int N, int Npad, float scale, float scale_log2, int nqb) {
+    __bf16* __restrict__ dQ, int H, int G, int N, int window, int Npad, float scale, float scale_log2,
+    int nqb) {
     using namespace bwdq;
     constexpr int DC = D / 16;
     constexpr int DT = D / 32;
@@ -507,11 +513,15 @@ __global__ __launch_bounds__(bwdq::NT, 1) void bwd_dq_kernel(
     const int my_q = qw + l32;
     const int q_rd = min(my_q, N - 1);         // rows past N: finite data, never stored
 
+    // Key tiles t_lo .. ntiles-1 (causal: query i sees keys j with
+    // i - window < j <= i; window >= N is plain causal).  Tiles every query of
+    // the workgroup sees whole, [t_ulo, t_uhi), run unmasked; those on the
+    // window edge or the diagonal are masked.  Keys past N need no mask.
     const int kv_end = CAUSAL ? min(N, q0 + BR) : N;
     const int ntiles = (kv_end + BC - 1) / BC;
-    // tiles every query of the workgroup sees whole; causal tiles after them
-    // straddle some wave's diagonal and are masked
-    const int nfull = CAUSAL ? min(ntiles, (q0 + 1) / BC) : ntiles;
+    const int t_lo = CAUSAL ? max(0, q0 - window + 1) / BC : 0;
+    const int t_uhi = CAUSAL ? max(t_lo, min(ntiles, (q0 + 1) / BC)) : ntiles;
+    const int t_ulo = CAUSAL ? min(t_uhi, max(t_lo, (max(0, q0 + BR - window) + BC - 1) / BC)) : 0;
 
     unsigned ld_off[SEG_W];                    // lane's bytes relative to the tile's first row
 #pragma unroll
@@ -523,7 +533,8 @@ __global__ __launch_bounds__(bwdq::NT, 1) void bwd_dq_kernel(
     // direct loads of tile t (a tile past the last one goes to the spare KB)
     auto issue_tile = [&](int t) {
         const bool real = t < ntiles;
-        const unsigned kb = __builtin_amdgcn_readfirstlane(real ? lds0 + (t % NSTAGE) * STAGE : lds0 + NSTAGE * STAGE);
+        const unsigned kb = __builtin_amdgcn_readfirstlane(real ? lds0 + ((t - t_lo) % NSTAGE) * STAGE
+                                                                : lds0 + NSTAGE * STAGE);
         const unsigned segb = real ? 1024u : 0u;
         const unsigned row0 = (unsigned)(real ? t * BC : 0) * kv_row_bytes;
 #pragma unroll
@@ -533,8 +544,8 @@ __global__ __launch_bounds__(bwdq::NT, 1) void bwd_dq_kernel(
             dma16_buf(rV, row0 + ld_off[i], kb + (TILE / 1024 + seg) * segb);
         }
     };
-    issue_tile(0);
-    issue_tile(1);
+    issue_tile(t_lo);
+    issue_tile(t_lo + 1);
 
     // this lane's query: Q and dO as B operands (features 16c + 8hl ..), LSE, D
     bf16x8 qreg[DC], oreg[DC];
@@ -574,8 +585,9 @@ __global__ __launch_bounds__(bwdq::NT, 1) void bwd_dq_kernel(
         if constexpr (MASK) issue_tile(t + 2);
 
         const int j0 = t * BC;
-        if (MASK && j0 > qw + 31) return;      // every key after this wave's queries
-        const lds_char* stage = L + (t % NSTAGE) * STAGE;
+        // every key after this wave's queries, or before all of their windows
+        if (MASK && (j0 > qw + 31 || j0 + BC - 1 < qw - window + 1)) return;
+        const lds_char* stage = L + ((t - t_lo) % NSTAGE) * STAGE;
         const lds_char* ka0 = stage + a_rd0;
         const lds_char* ka1 = stage + a_rd1;
         const lds_char* kt0 = stage + tr0;
@@ -601,6 +613,7 @@ __global__ __launch_bounds__(bwdq::NT, 1) void bwd_dq_kernel(
         // diagonal tiles keys after the lane's query get exp2(-inf) = 0
         u32x4 dsb[4];
         const int lim_c = my_q - j0 - 4 * hl;  // key = j0 + 4hl + off: key <= q <=> off <= lim_c
+        const int lim_w = lim_c - window + 1;  // window: key > q - window <=> off >= lim_w
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -609,8 +622,8 @@ __global__ __launch_bounds__(bwdq::NT, 1) void bwd_dq_kernel(
                 float x1 = __builtin_fmaf(s[kt][r + 1], scale_log2, -lq);
                 if constexpr (MASK) {
                     const int o0 = kt * 32 + (r >> 2) * 8 + (r & 3);
-                    x0 = o0 <= lim_c ? x0 : -INFINITY;
-                    x1 = o0 + 1 <= lim_c ? x1 : -INFINITY;
+                    x0 = (o0 <= lim_c && o0 >= lim_w) ? x0 : -INFINITY;
+                    x1 = (o0 + 1 <= lim_c && o0 + 1 >= lim_w) ? x1 : -INFINITY;
                 }
                 const float d0 = fast_exp2(x0) * (dp[kt][r] + dq_row);
                 const float d1 = fast_exp2(x1) * (dp[kt][r + 1] + dq_row);
@@ -628,10 +641,12 @@ __global__ __launch_bounds__(bwdq::NT, 1) void bwd_dq_kernel(
             }
     };
 #pragma clang loop unroll(disable)
-    for (int t = 0; t < nfull; ++t) tile(t, flag_t<false>{});
+    for (int t = t_lo; t < t_ulo; ++t) tile(t, flag_t<CAUSAL>{});
+#pragma clang loop unroll(disable)
+    for (int t = t_ulo; t < t_uhi; ++t) tile(t, flag_t<false>{});
     if constexpr (CAUSAL) {
 #pragma clang loop unroll(disable)
-        for (int t = nfull; t < ntiles; ++t) tile(t, flag_t<true>{});
+        for (int t = t_uhi; t < ntiles; ++t) tile(t, flag_t<true>{});
     }
     FA_WAIT_VMCNT(0);                          // the loads past the last tile
 
@@ -669,8 +684,9 @@ hipError_t launch_bwd_preprocess(const void* o, const void* dout, const float* l
 
 hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, void* dk,
                            void* dv, int B, int H, int Hkv, int N, int d, float scale, bool causal,
-                           const float* lse2, const float* delta, hipStream_t stream) {
+                           int window, const float* lse2, const float* delta, hipStream_t stream) {
     const int G = H / Hkv;
+    const int win = window > 0 ? window : kNoWindow;
     auto Qp = static_cast<const __bf16*>(q);
     auto Kp = static_cast<const __bf16*>(k);
     auto Vp = static_cast<const __bf16*>(v);
@@ -684,7 +700,7 @@ hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const vo
     const int delta_off = (int)((const char*)delta - (const char*)lse2);
 #define FA_BWD_LAUNCH(DD, CC)                                                                        \
     hipLaunchKernelGGL((bwd_dkdv_kernel<DD, CC>), grid, block, 0, stream, Qp, Kp, Vp, dOp, lse2,    \
-                       delta_off, dKp, dVp, H, G, N, Npad, scale, sl2, nkb)
+                       delta_off, dKp, dVp, H, G, N, win, Npad, scale, sl2, nkb)
     if (d == 128) {
         if (causal) FA_BWD_LAUNCH(128, true);
         else FA_BWD_LAUNCH(128, false);
@@ -697,9 +713,10 @@ hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const vo
 }
 
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dout, void* dq,
-                         int B, int H, int Hkv, int N, int d, float scale, bool causal, const float* lse2,
-                         const float* delta, hipStream_t stream) {
+                         int B, int H, int Hkv, int N, int d, float scale, bool causal, int window,
+                         const float* lse2, const float* delta, hipStream_t stream) {
     const int G = H / Hkv;
+    const int win = window > 0 ? window : kNoWindow;
     auto Qp = static_cast<const __bf16*>(q);
     auto Kp = static_cast<const __bf16*>(k);
     auto Vp = static_cast<const __bf16*>(v);
@@ -711,7 +728,7 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void
     const float sl2 = scale * kLog2e;
 #define FA_BWDQ_LAUNCH(DD, CC)                                                                      \
     hipLaunchKernelGGL((bwd_dq_kernel<DD, CC>), grid, block, 0, stream, Qp, Kp, Vp, dOp, lse2,     \
-                       delta, dQp, H, G, N, Npad, scale, sl2, nqb)
+                       delta, dQp, H, G, N, win, Npad, scale, sl2, nqb)
     if (d == 128) {
         if (causal) FA_BWDQ_LAUNCH(128, true);
         else FA_BWDQ_LAUNCH(128, false);

@@ -63,7 +63,8 @@ __device__ __forceinline__ int v_swz(int row) { return ((row >> 1) & 1) << 1; }
 template <int D, bool CAUSAL, bool POS>
 __global__ __launch_bounds__(fwd::NT, 1) void fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-    __bf16* __restrict__ O, float* __restrict__ LSE, int H, int G, int N, float scale_log2, int nqb) {
+    __bf16* __restrict__ O, float* __restrict__ LSE, int H, int G, int N, int window, float scale_log2,
+    int nqb) {
     using namespace fwd;
     constexpr int TILE = BC * D * 2;           // one K or V block
     constexpr int STAGE = 2 * TILE;            // K then V
@@ -106,11 +107,16 @@ __global__ __launch_bounds__(fwd::NT, 1) void fwd_bf16_kernel(
     const int qw = q0 + wave * 32;             // first query of this wave
     const int my_q = qw + l32;
 
+    // Key blocks t_lo .. ntiles-1.  Causal: query i sees keys j with
+    // i - window < j <= i (window >= N: plain causal), so blocks wholly before
+    // the block's first window are skipped.  Blocks every query of the
+    // workgroup sees whole, [t_ulo, t_uhi), run unmasked; the others (window
+    // edge, causal diagonal, a ragged last block) are masked.
     const int kv_end = CAUSAL ? min(N, q0 + BR) : N;
     const int ntiles = (kv_end + BC - 1) / BC;
-    // blocks every query of the workgroup sees whole come first; the rest
-    // (a ragged last block, blocks on the causal diagonal) are masked
-    const int nfull = min(N / BC, CAUSAL ? (q0 + 1) / BC : ntiles);
+    const int t_lo = CAUSAL ? max(0, q0 - window + 1) / BC : 0;
+    const int t_uhi = max(t_lo, min(N / BC, CAUSAL ? (q0 + 1) / BC : ntiles));
+    const int t_ulo = CAUSAL ? min(t_uhi, max(t_lo, (max(0, q0 + BR - window) + BC - 1) / BC)) : 0;
 
     // Direct global -> LDS loads of one K/V block: each wave fills SEG_W 1 KB
     // segments of K and of V; lane i writes bytes [16 i, 16 i + 16) of its
@@ -127,7 +133,8 @@ __global__ __launch_bounds__(fwd::NT, 1) void fwd_bf16_kernel(
     const unsigned lds0 = __builtin_amdgcn_readfirstlane(lds_offset(smem));
     auto issue_tile = [&](int t) {
         const bool real = t < ntiles;
-        const unsigned kb = __builtin_amdgcn_readfirstlane(real ? lds0 + (t % NSTAGE) * STAGE : lds0 + NSTAGE * STAGE);
+        const unsigned kb = __builtin_amdgcn_readfirstlane(real ? lds0 + ((t - t_lo) % NSTAGE) * STAGE
+                                                                : lds0 + NSTAGE * STAGE);
         const unsigned segb = real ? 1024u : 0u;
         const unsigned row0 = (unsigned)(real ? t * BC : 0) * kv_row_bytes;
 #pragma unroll
@@ -138,8 +145,8 @@ __global__ __launch_bounds__(fwd::NT, 1) void fwd_bf16_kernel(
         }
     };
 
-    issue_tile(0);
-    issue_tile(1);
+    issue_tile(t_lo);
+    issue_tile(t_lo + 1);
 
     // Queries of this lane, as B-operand chunks of S^T = K Q^T.  Rows past N
     // read row N-1 (finite data whose results are never stored).
@@ -186,11 +193,12 @@ __global__ __launch_bounds__(fwd::NT, 1) void fwd_bf16_kernel(
         if constexpr (MASK) issue_tile(t + 2);  // masked blocks may return early
 
         const int j0 = t * BC;
-        if (MASK && CAUSAL && j0 > qw + 31) return;   // every key after this wave's queries
+        // every key after this wave's queries, or before all of their windows
+        if (MASK && CAUSAL && (j0 > qw + 31 || j0 + BC - 1 < qw - window + 1)) return;
         // per-iteration bases; the empty asm keeps the compiler from
         // hoisting base + offset sums into separate registers, so the
         // offsets fold into the LDS instructions
-        const lds_char* stage = as_lds(smem) + (t % NSTAGE) * STAGE;
+        const lds_char* stage = as_lds(smem) + ((t - t_lo) % NSTAGE) * STAGE;
         const lds_char* kb0 = stage + k_rd0;
         const lds_char* kb1 = stage + k_rd1;
         const lds_char* vb = stage + v_rd;
@@ -217,12 +225,13 @@ __global__ __launch_bounds__(fwd::NT, 1) void fwd_bf16_kernel(
             // constant with one per-lane limit
             const int lim_n = N - j0 - 4 * hl;            // visible iff off < lim_n
             const int lim_c = my_q - j0 - 4 * hl;         // causal: off <= lim_c
+            const int lim_w = lim_c - window + 1;         // window: off >= lim_w
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int off = kt * 32 + (r >> 2) * 8 + (r & 3);
-                    const bool vis = off < lim_n && (!CAUSAL || off <= lim_c);
+                    const bool vis = off < lim_n && (!CAUSAL || (off <= lim_c && off >= lim_w));
                     s[kt][r] = vis ? s[kt][r] : masked;
                 }
         }
@@ -243,7 +252,10 @@ __global__ __launch_bounds__(fwd::NT, 1) void fwd_bf16_kernel(
         const float mt = mx * scale_log2;
         if (__builtin_amdgcn_ballot_w64(mt > m_run + kLazy) != 0) {
             const float m_new = fmaxf(m_run, mt);
-            const float alpha = fast_exp2(m_run - m_new);
+            // a row that has seen no visible key yet (possible at a sliding
+            // window's edge while other rows of the wave rescale) has l = 0
+            // and O = 0: any finite alpha will do, and -inf - -inf is NaN
+            const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
             m_run = m_new;
             l_run *= alpha;
 #pragma unroll
@@ -287,9 +299,11 @@ __global__ __launch_bounds__(fwd::NT, 1) void fwd_bf16_kernel(
         __builtin_amdgcn_sched_barrier(0);
     };
 #pragma clang loop unroll(disable)
-    for (int t = 0; t < nfull; ++t) block(t, std::false_type{});
+    for (int t = t_lo; t < t_ulo; ++t) block(t, std::true_type{});
 #pragma clang loop unroll(disable)
-    for (int t = nfull; t < ntiles; ++t) block(t, std::true_type{});
+    for (int t = t_ulo; t < t_uhi; ++t) block(t, std::false_type{});
+#pragma clang loop unroll(disable)
+    for (int t = t_uhi; t < ntiles; ++t) block(t, std::true_type{});
     FA_WAIT_VMCNT(0);                          // the loads past the last block
 
     // ---- epilogue: O = O / l, LSE = m ln2 + ln l ----
@@ -409,7 +423,8 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(
 // launchers
 // ---------------------------------------------------------------------------
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                           int H, int Hkv, int N, int d, float scale, bool causal, hipStream_t stream) {
+                           int H, int Hkv, int N, int d, float scale, bool causal, int window,
+                           hipStream_t stream) {
     const int G = H / Hkv;
     const int nqb = (N + fwd::BR - 1) / fwd::BR;
     const dim3 grid((unsigned)(B * H * nqb)), block(fwd::NT);
@@ -418,7 +433,10 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
     auto Kp = static_cast<const __bf16*>(k);
     auto Vp = static_cast<const __bf16*>(v);
     auto Op = static_cast<__bf16*>(o);
-    auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, block, 0, stream, Qp, Kp, Vp, Op, lse, H, G, N, sl2, nqb); };
+    const int win = window > 0 ? window : kNoWindow;
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, grid, block, 0, stream, Qp, Kp, Vp, Op, lse, H, G, N, win, sl2, nqb);
+    };
     const bool pos = sl2 >= 0.f;
     if (d == 128) {
         if (causal) pos ? go(fwd_bf16_kernel<128, true, true>) : go(fwd_bf16_kernel<128, true, false>);

@@ -8,9 +8,12 @@
 namespace fa {
 
 // Hkv: K/V heads (H for multi-head attention; H a multiple of Hkv).  Query
-// head h uses K/V head h / (H / Hkv).
+// head h uses K/V head h / (H / Hkv).  window (causal only): query i sees keys
+// j with i - window < j <= i; window <= 0 means no window.
+constexpr int kNoWindow = 1 << 30;
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                           int H, int Hkv, int N, int d, float scale, bool causal, hipStream_t stream);
+                           int H, int Hkv, int N, int d, float scale, bool causal, int window,
+                           hipStream_t stream);
 
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B,
                           int H, int N, int d, float scale, bool causal, hipStream_t stream);
@@ -23,9 +26,9 @@ hipError_t launch_bwd_preprocess(const void* o, const void* dout, const float* l
                                  int N, int d, float* lse2, float* delta, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, void* dk,
                            void* dv, int B, int H, int Hkv, int N, int d, float scale, bool causal,
-                           const float* lse2, const float* delta, hipStream_t stream);
+                           int window, const float* lse2, const float* delta, hipStream_t stream);
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dout, void* dq,
-                         int B, int H, int Hkv, int N, int d, float scale, bool causal, const float* lse2,
-                         const float* delta, hipStream_t stream);
+                         int B, int H, int Hkv, int N, int d, float scale, bool causal, int window,
+                         const float* lse2, const float* delta, hipStream_t stream);
 
 }  // namespace fa

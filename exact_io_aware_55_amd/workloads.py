@@ -32,13 +32,24 @@ def tile_bytes(rows: int, cols: int, elem_bytes: int = 2) -> int:
     return rows * cols * elem_bytes
 
 
-def fwd_flops(B, H, N, d, causal):
+def window_pairs(N: int, window: int) -> int:
+    """Visible (query, key) pairs of one head under a causal sliding window:
+    query i sees min(i + 1, window) keys."""
+    w = min(window, N)
+    return w * (w + 1) // 2 + (N - w) * w
+
+
+def fwd_flops(B, H, N, d, causal, window=None):
+    """Counted forward flops: 4 N^2 d per head, halved for causal (N^2 / 2
+    pairs); with a sliding window, 4 d per visible pair."""
     f = 4.0 * N * N * d * B * H
+    if window is not None:
+        return 4.0 * d * window_pairs(N, window) * B * H
     return f / 2 if causal else f
 
 
-def bwd_flops(B, H, N, d, causal):
-    return 2.5 * fwd_flops(B, H, N, d, causal)
+def bwd_flops(B, H, N, d, causal, window=None):
+    return 2.5 * fwd_flops(B, H, N, d, causal, window)
 
 
 def fwd_bytes(B, H, N, d, elem=2):

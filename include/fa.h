@@ -60,7 +60,8 @@ typedef struct ihipStream_t* hipStream_t;
 enum {
     FA_OK = 0,
     FA_ERR_INVALID_ARG = -1, /* null pointer, B/H/N < 1, non-finite scale,
-                                H_kv < 1 or not dividing H (GQA calls) */
+                                H_kv < 1 or not dividing H (GQA calls),
+                                window < 1 (sliding-window calls) */
     FA_ERR_UNSUPPORTED = -2, /* d not in {64, 128}, or N*H*d >= 2^30     */
     FA_ERR_MISALIGNED = -3,  /* a pointer not 16-byte aligned             */
     FA_ERR_WORKSPACE = -4,   /* workspace null, misaligned or too small   */
@@ -137,6 +138,23 @@ int fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const
                const float* lse, void* dq, void* dk, void* dv,
                int B, int H, int H_kv, int N, int d, float scale, int causal,
                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Causal sliding-window attention (explainer page "Flash Attention", section
+ * "Varianten und Erweiterungen", subsection "Sliding Window Attention": each
+ * position attends to a fixed neighbourhood, and key blocks wholly outside
+ * it are neither loaded nor computed).  Query i sees keys j with
+ * i - window < j <= i (the window counts the query's own key); window >= N
+ * is plain causal attention.  Grouped K/V heads as in fa_fwd_gqa (H_kv = H
+ * for multi-head attention).  lse holds the log-sum-exp over the window;
+ * fa_bwd_window takes the O and LSE of fa_fwd_window with the same window.
+ * window < 1 returns FA_ERR_INVALID_ARG; otherwise as fa_fwd_gqa /
+ * fa_bwd_gqa. */
+int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int B, int H, int H_kv, int N, int d, float scale, int window, hipStream_t stream);
+int fa_bwd_window(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                  const float* lse, void* dq, void* dk, void* dv,
+                  int B, int H, int H_kv, int N, int d, float scale, int window,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Human-readable text for a return code (static storage). */
 const char* fa_strerror(int code);

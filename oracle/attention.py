@@ -38,6 +38,13 @@ GPU path uses the equivalent row dot product of dO and O.
 
 Tensors use the [B, N, H, d] layout; LSE uses [B, H, N].
 
+Sliding-window attention (same page and section, subsection "Sliding Window
+Attention": each position attends to a fixed neighbourhood).  The page gives
+a window size of 4096 tokens for its causal language-model example without
+saying whether the window counts the query itself; the reading taken is
+causal with the window counting it: query i sees keys j with
+i - window < j <= i.
+
 Grouped-query attention (explainer page "Flash Attention", section "Varianten
 und Erweiterungen", subsection "Grouped Query Attention": several query heads
 share one K/V group): K and V may have H_kv heads with H a multiple of H_kv.
@@ -69,18 +76,28 @@ def _f64(x):
     return np.asarray(x, dtype=np.float64)
 
 
-def _visible(nq: int, nk: int, causal: bool, rows=None):
+def _visible(nq: int, nk: int, causal: bool, rows=None, window=None):
     """Boolean mask [len(rows), nk]: True where query row i may see key j.
 
     Causal means key j is visible to query i when j <= i (square N x N case).
+    A sliding window (causal only) further requires j > i - window: each
+    query sees its own key and the window - 1 keys before it.
     """
     r = np.arange(nq) if rows is None else np.asarray(rows)
     if not causal:
+        if window is not None:
+            raise ValueError("a sliding window is defined for causal attention only")
         return np.ones((r.shape[0], nk), dtype=bool)
-    return np.arange(nk)[None, :] <= r[:, None]
+    j = np.arange(nk)[None, :]
+    vis = j <= r[:, None]
+    if window is not None:
+        if window < 1:
+            raise ValueError("window must be >= 1")
+        vis &= j > r[:, None] - window
+    return vis
 
 
-def head_probabilities(q, k, scale, causal, rows=None):
+def head_probabilities(q, k, scale, causal, rows=None, window=None):
     """Return (P, m, l) for one head by the two-pass softmax of the definition.
 
     q: [Nq, d], k: [Nk, d].  ``rows`` optionally selects query rows (absolute
@@ -93,7 +110,7 @@ def head_probabilities(q, k, scale, causal, rows=None):
     if rows is not None:
         q = q[np.asarray(rows)]
     s = scale * (q @ k.T)
-    s = np.where(_visible(nq, k.shape[0], causal, rows), s, -np.inf)
+    s = np.where(_visible(nq, k.shape[0], causal, rows, window), s, -np.inf)
     # pass 1: row maximum
     m = s.max(axis=1)
     # pass 2: exponentials relative to the maximum, and their sum
@@ -102,18 +119,18 @@ def head_probabilities(q, k, scale, causal, rows=None):
     return e / l[:, None], m, l
 
 
-def head_forward(q, k, v, scale, causal, rows=None):
+def head_forward(q, k, v, scale, causal, rows=None, window=None):
     """One head: O = softmax(scale Q K^T [masked]) V and LSE = m + ln l.
 
     Returns (O [len(rows) or N, d], LSE [len(rows) or N]) in fp64.
     """
-    p, m, l = head_probabilities(q, k, scale, causal, rows)
+    p, m, l = head_probabilities(q, k, scale, causal, rows, window)
     o = p @ _f64(v)
     lse = m + np.log(l)
     return o, lse
 
 
-def head_backward(q, k, v, do, scale, causal):
+def head_backward(q, k, v, do, scale, causal, window=None):
     """One head: (dQ, dK, dV) of L = sum(O * dO) by the softmax Jacobian.
 
     P is recomputed from the definition (no stored N x N from a forward).
@@ -122,7 +139,7 @@ def head_backward(q, k, v, do, scale, causal):
     k = _f64(k)
     v = _f64(v)
     do = _f64(do)
-    p, _, _ = head_probabilities(q, k, scale, causal)
+    p, _, _ = head_probabilities(q, k, scale, causal, window=window)
     dv = p.T @ do
     dp = do @ v.T
     delta = (p * dp).sum(axis=1)          # definition form of Delta_i
@@ -132,7 +149,7 @@ def head_backward(q, k, v, do, scale, causal):
     return dq, dk, dv
 
 
-def head_forward_blockwise(q, k, v, scale, causal, block, dtype=np.float64):
+def head_forward_blockwise(q, k, v, scale, causal, block, dtype=np.float64, window=None):
     """The tiled online-softmax forward over key/value blocks, for self-tests.
 
     This follows the streaming description on the glossary page ("How it
@@ -142,7 +159,10 @@ def head_forward_blockwise(q, k, v, scale, causal, block, dtype=np.float64):
     with V, and divide by the running sum once at the end.  ``dtype`` selects
     the arithmetic precision (fp64 by default, fp32 to reproduce the page's
     worked example).  It is never used to check the GPU; it pins the claim
-    that the blockwise result equals the full softmax.
+    that the blockwise result equals the full softmax.  With a sliding
+    ``window`` a block no row can see is skipped without being read, as the
+    page describes ("Sliding Window Attention"); the number of skipped blocks
+    is stored in the function attribute ``skipped``.
     """
     q = np.asarray(q, dtype=dtype)
     k = np.asarray(k, dtype=dtype)
@@ -150,30 +170,43 @@ def head_forward_blockwise(q, k, v, scale, causal, block, dtype=np.float64):
     n, d = q.shape
     nk = k.shape[0]
     sc = dtype(scale)
-    run_max = np.full((n, 1), -np.inf, dtype=dtype)
-    run_sum = np.zeros((n, 1), dtype=dtype)
-    acc = np.zeros((n, v.shape[1]), dtype=dtype)
-    qi = np.arange(n)[:, None]
+    vis_all = _visible(n, nk, causal, window=window)
+    o = np.zeros((n, v.shape[1]), dtype=dtype)
+    lse = np.zeros(n, dtype=dtype)
     largest_tile = (0, 0)
-    for start in range(0, nk, block):
-        kb = k[start:start + block]
-        vb = v[start:start + block]
-        s = (q @ kb.T) * sc
-        largest_tile = max(largest_tile, s.shape)
-        if causal:
-            kj = np.arange(start, start + kb.shape[0])[None, :]
-            s = np.where(kj <= qi, s, dtype(-np.inf))
-        blk_max = s.max(axis=1, keepdims=True)
-        new_max = np.maximum(run_max, blk_max)
-        # a row that has seen no visible key yet keeps max -inf; subtract 0
-        safe = np.where(np.isfinite(new_max), new_max, dtype(0))
-        alpha = np.exp(run_max - safe)
-        p = np.exp(s - safe)
-        run_sum = run_sum * alpha + p.sum(axis=1, keepdims=True)
-        acc = acc * alpha + p @ vb
-        run_max = new_max
-    o = acc / run_sum
-    lse = (run_max + np.log(run_sum))[:, 0]
+    skipped = 0
+    # the page's sketch streams K/V blocks past all queries at once; with a
+    # window the queries go in blocks of the same size too, so that whole
+    # (query block, key block) tiles outside every window can be skipped
+    qblock = block if window is not None else n
+    for qs in range(0, n, qblock):
+        qb = q[qs:qs + qblock]
+        run_max = np.full((qb.shape[0], 1), -np.inf, dtype=dtype)
+        run_sum = np.zeros((qb.shape[0], 1), dtype=dtype)
+        acc = np.zeros((qb.shape[0], v.shape[1]), dtype=dtype)
+        for start in range(0, nk, block):
+            vis = vis_all[qs:qs + qblock, start:start + block]
+            if window is not None and not vis.any():
+                skipped += 1          # a block outside every row's window: never read
+                continue
+            kb = k[start:start + block]
+            vb = v[start:start + block]
+            s = (qb @ kb.T) * sc
+            largest_tile = max(largest_tile, s.shape)
+            if causal:
+                s = np.where(vis, s, dtype(-np.inf))
+            blk_max = s.max(axis=1, keepdims=True)
+            new_max = np.maximum(run_max, blk_max)
+            # a row that has seen no visible key yet keeps max -inf; subtract 0
+            safe = np.where(np.isfinite(new_max), new_max, dtype(0))
+            alpha = np.exp(run_max - safe)
+            p = np.exp(s - safe)
+            run_sum = run_sum * alpha + p.sum(axis=1, keepdims=True)
+            acc = acc * alpha + p @ vb
+            run_max = new_max
+        o[qs:qs + qblock] = acc / run_sum
+        lse[qs:qs + qblock] = (run_max + np.log(run_sum))[:, 0]
+    head_forward_blockwise.skipped = skipped
     return o, lse, largest_tile
 
 
@@ -190,7 +223,7 @@ def _heads_of(b, h, heads):
     return [tuple(x) for x in heads]
 
 
-def forward(q, k, v, scale, causal, heads=None):
+def forward(q, k, v, scale, causal, heads=None, window=None):
     """[B,N,H,d] forward.  Returns O [B,N,H,d] and LSE [B,H,N] in fp64.
 
     ``heads`` optionally restricts the work to a list of (b, h) pairs; the
@@ -202,13 +235,14 @@ def forward(q, k, v, scale, causal, heads=None):
     lse = np.full((B, H, N), np.nan)
     for b, h in _heads_of(B, H, heads):
         g = kv_head(h, H, Hkv)
-        oh, lh = head_forward(q[b, :, h, :], k[b, :, g, :], v[b, :, g, :], scale, causal)
+        oh, lh = head_forward(q[b, :, h, :], k[b, :, g, :], v[b, :, g, :], scale, causal,
+                              window=window)
         o[b, :, h, :] = oh
         lse[b, h, :] = lh
     return o, lse
 
 
-def forward_rows(q, k, v, scale, causal, picks):
+def forward_rows(q, k, v, scale, causal, picks, window=None):
     """Forward for selected query rows only.
 
     ``picks`` is a list of (b, h, i).  Returns (O rows [len, d], LSE [len]).
@@ -222,13 +256,13 @@ def forward_rows(q, k, v, scale, causal, picks):
     for b, h, i in picks:
         g = kv_head(h, H, Hkv)
         oh, lh = head_forward(q[b, :, h, :], k[b, :, g, :], v[b, :, g, :], scale, causal,
-                              rows=[i])
+                              rows=[i], window=window)
         out_o.append(oh[0])
         out_l.append(lh[0])
     return np.array(out_o), np.array(out_l)
 
 
-def backward(q, k, v, do, scale, causal, heads=None):
+def backward(q, k, v, do, scale, causal, heads=None, window=None):
     """Backward.  Returns dQ ([B,N,H,d]), dK and dV (shaped like k and v) in
     fp64.  With grouped K/V heads a K/V head's gradient sums over its query
     heads.
@@ -244,7 +278,7 @@ def backward(q, k, v, do, scale, causal, heads=None):
     for b, h in _heads_of(B, H, heads):
         g = kv_head(h, H, Hkv)
         a, bb, c = head_backward(q[b, :, h, :], k[b, :, g, :], v[b, :, g, :],
-                                 do[b, :, h, :], scale, causal)
+                                 do[b, :, h, :], scale, causal, window)
         dq[b, :, h, :] = a
         if np.isnan(dk[b, 0, g, 0]):
             dk[b, :, g, :] = 0.0

@@ -63,16 +63,16 @@ U_BF16 = 2.0 ** -8
 F32_ALLOW = 1e-5
 
 
-def bwd_error_bounds(q, k, v, do, scale, causal):
+def bwd_error_bounds(q, k, v, do, scale, causal, window=None):
     """Return (bound_dQ, bound_dK, bound_dV) for one head (fp64 inputs)."""
     import oracle
 
-    p, _, _ = oracle.head_probabilities(q, k, scale, causal)
+    p, _, _ = oracle.head_probabilities(q, k, scale, causal, window=window)
     o = p @ v
     dp = do @ v.T
     delta = (p * dp).sum(1)
     ds = p * (dp - delta[:, None])
-    dq, dk, dv = oracle.head_backward(q, k, v, do, scale, causal)
+    dq, dk, dv = oracle.head_backward(q, k, v, do, scale, causal, window)
     u = U_BF16
     o_err = u * np.abs(o) + u * (p @ np.abs(v))
     d_err = (np.abs(do) * o_err).sum(1)

@@ -84,6 +84,19 @@ def test_gqa_argument_errors(lib):
     assert g(*p9[:8], None, 1, 6, 2, 8, 64, 0.1, 0, V(FAKE), need, None) == binding.FA_ERR_INVALID_ARG
 
 
+def test_window_argument_errors(lib):
+    V = ctypes.c_void_p
+    p5 = [V(FAKE)] * 5
+    for w in (0, -3):
+        assert lib.fa_fwd_window(*p5, 1, 4, 2, 8, 64, 0.1, w, None) == binding.FA_ERR_INVALID_ARG
+    assert lib.fa_fwd_window(*p5, 1, 4, 3, 8, 64, 0.1, 4, None) == binding.FA_ERR_INVALID_ARG
+    assert lib.fa_fwd_window(*p5, 1, 4, 2, 8, 80, 0.1, 4, None) == binding.FA_ERR_UNSUPPORTED
+    p9 = [V(FAKE)] * 9
+    need = lib.fa_bwd_workspace_size(1, 4, 8, 64)
+    assert lib.fa_bwd_window(*p9, 1, 4, 2, 8, 64, 0.1, 0, V(FAKE), need, None) == binding.FA_ERR_INVALID_ARG
+    assert lib.fa_bwd_window(*p9, 1, 4, 2, 8, 64, 0.1, 3, V(FAKE), need - 1, None) == binding.FA_ERR_WORKSPACE
+
+
 def test_workspace_size(lib):
     def want(B, H, N, d):
         a256 = lambda x: (x + 255) // 256 * 256

@@ -14,6 +14,8 @@ import numpy as np
 import pytest
 import torch
 
+from exact_io_aware_55_amd import workloads
+
 from oracle import (backward, forward, forward_rows, head_backward, head_forward, kv_head,
                     head_forward_blockwise, head_probabilities)
 
@@ -451,3 +453,73 @@ def test_gqa_group_mapping_mistake_is_caught():
 def test_gqa_rejects_non_dividing_heads():
     with pytest.raises(ValueError):
         kv_head(1, 4, 3)
+
+
+# --------------------------------------------------------------------------
+# Sliding-window attention (explainer page "Flash Attention", section
+# "Varianten und Erweiterungen", subsection "Sliding Window Attention")
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("window", [1, 3, 8, 100])
+def test_window_closed_forms(window):
+    """window = 1: each query sees only its own key, so O = V and
+    LSE = scale q_i . k_i; a window at least N long is plain causal."""
+    n, d = 9, 4
+    q, k, v = rnd(n, d, seed=80), rnd(n, d, seed=81), rnd(n, d, seed=82)
+    o, lse = head_forward(q, k, v, 0.6, True, window=window)
+    if window == 1:
+        assert np.allclose(o, v, atol=1e-14)
+        assert np.allclose(lse, 0.6 * (q * k).sum(1), atol=1e-14)
+    if window >= n:
+        oc, lc = head_forward(q, k, v, 0.6, True)
+        assert np.array_equal(o, oc) and np.array_equal(lse, lc)
+    # row i equals full attention over exactly the keys max(0, i-window+1) .. i
+    for i in range(n):
+        lo = max(0, i - window + 1)
+        s = 0.6 * k[lo:i + 1] @ q[i]
+        e = np.exp(s - s.max())
+        assert np.allclose(o[i], e @ v[lo:i + 1] / e.sum(), atol=1e-13)
+        assert np.isclose(lse[i], s.max() + np.log(e.sum()), atol=1e-13)
+
+
+@pytest.mark.parametrize("window", [2, 5])
+def test_window_backward_torch_autograd(window):
+    """Independent library: torch.autograd through an explicit band mask."""
+    n, d = 17, 6
+    arrs = [rnd(n, d, seed=s) for s in (83, 84, 85, 86)]
+    dq, dk, dv = head_backward(*arrs, 0.4, True, window)
+    q, k, v = (torch.tensor(a, requires_grad=True) for a in arrs[:3])
+    i = torch.arange(n)[:, None]
+    j = torch.arange(n)[None, :]
+    s = (q @ k.T * 0.4).masked_fill((j > i) | (j <= i - window), float("-inf"))
+    (torch.softmax(s, -1) @ v * torch.from_numpy(arrs[3])).sum().backward()
+    for mine, ref in ((dq, q.grad), (dk, k.grad), (dv, v.grad)):
+        assert np.abs(mine - ref.numpy()).max() <= 1e-10
+
+
+@pytest.mark.parametrize("window,block", [(3, 2), (7, 4), (16, 5)])
+def test_window_block_skipping_is_exact(window, block):
+    """Skipping the blocks no row of the window can see leaves the result
+    equal to the two-pass softmax, and some blocks are skipped."""
+    n, d = 40, 5
+    q, k, v = rnd(n, d, seed=87), rnd(n, d, seed=88), rnd(n, d, seed=89)
+    o, lse = head_forward(q, k, v, 0.5, True, window=window)
+    ob, lb, _ = head_forward_blockwise(q, k, v, 0.5, True, block, window=window)
+    assert np.abs(ob - o).max() <= 1e-12 and np.abs(lb - lse).max() <= 1e-12
+    assert head_forward_blockwise.skipped >= 1
+
+
+def test_window_pairs_and_page_skip_fraction():
+    """The visible-pair count equals the oracle's mask; at the page's example
+    (32 768 tokens, window 4 096) 88.3 % of the N x N pairs are skipped, the
+    page's "up to 87 %" of the blocks (a magnitude pin)."""
+    from oracle.attention import _visible
+    for n, w in ((10, 3), (33, 33), (50, 1), (64, 17)):
+        assert workloads.window_pairs(n, w) == int(_visible(n, n, True, window=w).sum())
+    frac = 1 - workloads.window_pairs(32768, 4096) / 32768 ** 2
+    assert abs(frac - 0.883) < 1e-3 and frac >= 0.87
+
+
+def test_window_requires_causal():
+    with pytest.raises(ValueError):
+        head_forward(rnd(4, 2), rnd(4, 2), rnd(4, 2), 1.0, False, window=2)
