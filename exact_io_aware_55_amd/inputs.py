@@ -7,6 +7,12 @@ heads) in the order Q, K, V, dO (dO only when asked), optionally multiplied
 by ``gain``, then cast to the requested dtype
 (bf16 casts round to nearest even).  The oracle is fed the cast values
 upcast to fp64, which is exact for both fp32 and bf16.
+
+FP8 inputs (``make_qkv_fp8``) are the same N(0, 1) draws, quantised per
+(batch, head): descale = max|x| / 448 over that head's [N, d] values, and the
+code is x / descale cast to OCP E4M3 (torch ``float8_e4m3fn``, round to
+nearest even), so each head spans the format's whole range.  The codes (as
+bytes) and the fp32 descale factors are the inputs of both sides.
 """
 
 from __future__ import annotations
@@ -14,7 +20,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-__all__ = ["make_qkv", "to_f64"]
+__all__ = ["make_qkv", "make_qkv_fp8", "to_f64"]
 
 
 def make_qkv(B, N, H, d, dtype=torch.bfloat16, seed=0, with_do=False, gain=1.0, H_kv=None):
@@ -30,6 +36,22 @@ def make_qkv(B, N, H, d, dtype=torch.bfloat16, seed=0, with_do=False, gain=1.0, 
         if gain != 1.0:
             t = t * gain
         out[name] = t.to(dtype).contiguous()
+    return out
+
+
+def make_qkv_fp8(B, N, H, d, seed=0, gain=1.0, H_kv=None):
+    """Return a dict with uint8 CPU tensors 'q8', 'k8', 'v8' (E4M3 codes,
+    [B,N,H,d]; K and V [B,N,H_kv,d]) and fp32 'q_descale' [B,H],
+    'k_descale' and 'v_descale' [B,H_kv]."""
+    x = make_qkv(B, N, H, d, torch.float32, seed=seed, gain=gain, H_kv=H_kv)
+    out = {}
+    for name in ("q", "k", "v"):
+        t = x[name]
+        amax = t.abs().amax(dim=(1, 3))                       # [B, heads]
+        descale = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+        codes = (t / descale[:, None, :, None]).to(torch.float8_e4m3fn)
+        out[name + "8"] = codes.view(torch.uint8).contiguous()
+        out[name + "_descale"] = descale.to(torch.float32).contiguous()
     return out
 
 

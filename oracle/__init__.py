@@ -2,7 +2,8 @@
 
 TEST INFRASTRUCTURE ONLY: imported by the test suite, ``__graft_entry__.smoke()``
 and ``bench.py``'s ``cpu_baseline`` leg, never by the product path.  Parity of
-every function here is pinned by ``tests/test_oracle_pins.py``.
+every function here is pinned by ``tests/test_oracle_pins.py`` (the FP8
+decoding by ``tests/test_oracle_fp8.py``).
 """
 
 from .attention import (  # noqa: F401
@@ -15,3 +16,4 @@ from .attention import (  # noqa: F401
     head_probabilities,
     kv_head,
 )
+from .fp8 import decode_e4m3, dequantize, forward_fp8, forward_rows_fp8  # noqa: F401

@@ -90,3 +90,53 @@ def assert_within_bound(got, ref, bound, what="", slack=1.25):
     bad = err > lim
     assert not bad.any(), (f"{what}: {int(bad.sum())} elements outside the bf16 rounding bound; "
                            f"worst excess {float((err - lim).max()):.3e}")
+
+
+# --------------------------------------------------------------------------
+# Element-wise a-priori error bound of the FP8 forward.
+#
+# The oracle is attention of the decoded E4M3 inputs, so the inputs carry no
+# error.  The kernel then rounds each probability p (in its own units, where
+# p <= 2^8 because the running maximum lags the true one by at most 8 in
+# log2 units) to E4M3 for the P V product: |p~ - p| <= 2^-4 p in the normal
+# range and <= 2^-10 (half the subnormal spacing) below 2^-6.  The row sum l
+# adds the unrounded fp32 p, and l >= L_i = sum_j exp(s_ij - max_j s_ij)
+# whatever maximum was used.  So, per output element,
+#   |O_err| <= 2^-4 (P|V|) + 2^-10 (sum_vis |V|) / L_i
+# plus the score error of the fp8 matrix core (its accumulation was measured
+# at about 2^-15 of sum |a b|; allowed here as 2^-12, which perturbs each p by
+# a relative eta_i <= 2^-11 |scale| max_j (|q_i| . |k_j|)), the same allowance
+# on the P V accumulation, the bf16 rounding of O (2^-8 |O|) and fp32 terms.
+# --------------------------------------------------------------------------
+U_E4M3 = 2.0 ** -4
+SUB_E4M3 = 2.0 ** -10
+FP8_MFMA_ACC = 2.0 ** -12
+
+
+def fp8_fwd_error_bound(q, k, v, scale, causal, window=None):
+    """Element-wise bound on |O_gpu - O_oracle| for one head (fp64 decoded inputs)."""
+    import oracle
+
+    p, m, _ = oracle.head_probabilities(q, k, scale, causal, window=window)
+    vis = p > 0
+    s = scale * (q @ k.T)
+    # L_i = sum_j exp(s_ij - max_j s_ij) over visible keys
+    big_l = np.where(vis, np.exp(np.where(vis, s, 0.0) - m[:, None]), 0.0).sum(1)
+    pv = p @ np.abs(v)
+    o = np.abs(p @ v)
+    eta = 2.0 ** -11 * abs(scale) * (np.abs(q) @ np.abs(k).T).max(1)
+    return ((U_E4M3 + FP8_MFMA_ACC + 2.0 ** -16) * pv + SUB_E4M3 * (vis @ np.abs(v)) / big_l[:, None]
+            + (U_BF16 + 2.0 ** -16) * o + eta[:, None] * (pv + o) + 1e-7)
+
+
+def fp8_fwd_rel_l2_limit(q, k, v, scale, causal, window=None, factor=2.0):
+    """Relative-L2 limit for the FP8 forward of one head: ``factor`` times the
+    root-mean-square error expected from independent E4M3 roundings of P
+    (relative error spread evenly over +-2^-4: standard deviation
+    2^-4 / sqrt(3)), i.e. sqrt(sum_ij sigma^2 P_ij^2 |V_j|^2) / ||P V||."""
+    import oracle
+
+    p, _, _ = oracle.head_probabilities(q, k, scale, causal, window=window)
+    sigma = U_E4M3 / np.sqrt(3.0)
+    expected = sigma * np.sqrt(((p ** 2) @ (v ** 2)).sum())
+    return factor * float(expected / np.linalg.norm(p @ v))
