@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libfa.so")
 
 EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_bwd_workspace_size", "fa_bwd", "fa_bwd_preprocess",
            "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_gqa", "fa_bwd_gqa", "fa_fwd_window", "fa_bwd_window",
-           "fa_strerror")
+           "fa_fwd_fp8", "fa_strerror")
 
 FA_OK = 0
 FA_ERR_INVALID_ARG = -1
@@ -64,6 +64,8 @@ def load(path: str = LIB_PATH):
     lib.fa_fwd_window.restype = i
     lib.fa_bwd_window.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
     lib.fa_bwd_window.restype = i
+    lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp]
+    lib.fa_fwd_fp8.restype = i
     lib.fa_strerror.argtypes = [i]
     lib.fa_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -137,6 +139,28 @@ def forward(q, k, v, causal=False, scale=None, out=None, lse=None, window=None):
     else:
         _check(lib.fa_fwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), B, H, Hkv, N, d,
                               _scale(scale, d), int(bool(causal)), _stream()))
+    return o, lse_t
+
+
+def forward_fp8(q8, k8, v8, q_descale, k_descale, v_descale, causal=False, scale=None, window=None,
+                out=None, lse=None):
+    """FP8 forward (fa_fwd_fp8).  q8 [B,N,H,d] and k8, v8 [B,N,H_kv,d] are
+    uint8 tensors of OCP E4M3 codes; the descales are fp32 [B,H] (Q) and
+    [B,H_kv] (K, V).  ``scale`` multiplies the decoded scores (default
+    1/sqrt(d)).  Returns (O [B,N,H,d] bf16, LSE [B,H,N] fp32)."""
+    lib = load()
+    B, N, H, Hkv, d = _check_gqa(torch.uint8, (q8,), (k8, v8))
+    for t, heads in ((q_descale, H), (k_descale, Hkv), (v_descale, Hkv)):
+        if (not t.is_cuda or t.dtype != torch.float32 or tuple(t.shape) != (B, heads)
+                or not t.is_contiguous()):
+            raise ValueError("descales must be contiguous fp32 GPU tensors [B, H] (q) and [B, H_kv] (k, v)")
+    if window is not None:
+        causal = True
+    o = torch.empty((B, N, H, d), device=q8.device, dtype=torch.bfloat16) if out is None else out
+    lse_t = torch.empty((B, H, N), device=q8.device, dtype=torch.float32) if lse is None else lse
+    _check(lib.fa_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(q_descale), _ptr(k_descale), _ptr(v_descale),
+                          _ptr(o), _ptr(lse_t), B, H, Hkv, N, d, _scale(scale, d), int(bool(causal)),
+                          0 if window is None else int(window), _stream()))
     return o, lse_t
 
 

@@ -79,6 +79,23 @@ int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* l
     return fwd_impl(q, k, v, o, lse, B, H, H_kv, N, d, scale, 1, window, stream);
 }
 
+int fa_fwd_fp8(const void* q, const void* k, const void* v, const float* q_descale,
+               const float* k_descale, const float* v_descale, void* o, float* lse, int B, int H,
+               int H_kv, int N, int d, float scale, int causal, int window, hipStream_t stream) {
+    int rc = fwd_common(q, k, v, o, lse, B, H, N, d, scale);
+    if (rc != FA_OK) return rc;
+    if ((rc = check_groups(H, H_kv)) != FA_OK) return rc;
+    if (!q_descale || !k_descale || !v_descale) return FA_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(q_descale) | reinterpret_cast<uintptr_t>(k_descale) |
+         reinterpret_cast<uintptr_t>(v_descale)) & 3u)
+        return FA_ERR_MISALIGNED;
+    if (window < 0 || (window > 0 && !causal)) return FA_ERR_INVALID_ARG;
+    if (fa::launch_fwd_fp8(q, k, v, q_descale, k_descale, v_descale, o, lse, B, H, H_kv, N, d, scale,
+                           causal != 0, window, stream) != hipSuccess)
+        return FA_ERR_LAUNCH;
+    return FA_OK;
+}
+
 int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H,
                int N, int d, float scale, int causal, hipStream_t stream) {
     const int rc = fwd_common(q, k, v, o, lse, B, H, N, d, scale);

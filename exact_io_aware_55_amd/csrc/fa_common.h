@@ -66,6 +66,15 @@ __device__ __forceinline__ void static_for(F&& f) {
     static_for_from<0, N>(f);
 }
 
+// Maps a linear workgroup id to (head, query block) so that the workgroups the
+// hardware places on one XCD (ids congruent mod 8) take a contiguous range of
+// query blocks: those share K/V of the same heads and hit the same L2.
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
+    const int per = nblocks >> 3, rem = nblocks & 7;
+    const int x = bid & 7, i = bid >> 3;
+    return x * per + (x < rem ? x : rem) + i;
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ u32x4 ld_global16(const void* p) {

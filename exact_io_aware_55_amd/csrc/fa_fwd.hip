@@ -36,15 +36,6 @@ constexpr int NW = NT / 64; // waves
 constexpr int NSTAGE = 3;   // K/V blocks resident in the LDS ring
 }  // namespace fwd
 
-// Maps a linear workgroup id to (head, query block) so that the workgroups the
-// hardware places on one XCD (ids congruent mod 8) take a contiguous range of
-// query blocks: those share K/V of the same heads and hit the same L2.
-__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
-    const int per = nblocks >> 3, rem = nblocks & 7;
-    const int x = bid & 7, i = bid >> 3;
-    return x * per + (x < rem ? x : rem) + i;
-}
-
 // LDS layout of one K or V block (BC keys): D/32 sub-tiles [BC keys][32
 // features] with 64-byte rows (4 chunks of 16 bytes), chunk c of row R stored
 // at chunk c ^ swizzle(R).

@@ -15,6 +15,13 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
                            int H, int Hkv, int N, int d, float scale, bool causal, int window,
                            hipStream_t stream);
 
+// FP8 forward: Q, K, V are OCP E4M3 codes; q_descale [B*H], k_descale and
+// v_descale [B*Hkv] are device fp32 arrays (value = code * descale).
+hipError_t launch_fwd_fp8(const void* q, const void* k, const void* v, const float* q_descale,
+                          const float* k_descale, const float* v_descale, void* o, float* lse, int B,
+                          int H, int Hkv, int N, int d, float scale, bool causal, int window,
+                          hipStream_t stream);
+
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B,
                           int H, int N, int d, float scale, bool causal, hipStream_t stream);
 

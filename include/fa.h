@@ -156,6 +156,32 @@ int fa_bwd_window(const void* q, const void* k, const void* v, const void* o, co
                   int B, int H, int H_kv, int N, int d, float scale, int window,
                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* FP8 forward (explainer page "Flash Attention", section "Versionen: Flash
+ * Attention 2 und Flash Attention 3", and glossary page "Flash Attention",
+ * section "FlashAttention-2, -3 and -4": FlashAttention-3 runs attention in
+ * FP8).  The pages fix no format; here:
+ *   q        device, OCP E4M3 byte codes [B, N, H, d], 16-byte aligned
+ *   k, v     device, E4M3 codes [B, N, H_kv, d] (H a multiple of H_kv, query
+ *            head h reads K/V head h / (H / H_kv); H_kv = H: multi-head)
+ *   q_descale  device fp32 [B, H]; k_descale, v_descale: device fp32
+ *            [B, H_kv]; 4-byte aligned.  The real value of a code c is
+ *            decode(c) * descale of its (batch, head).
+ *   o        device bf16 [B, N, H, d]: attention of the decoded values
+ *   lse      device fp32 [B, H, N], natural-log log-sum-exp of the scaled
+ *            scores of the decoded values
+ *   causal   0 / 1; window: 0 = none, >= 1 = causal sliding window as in
+ *            fa_fwd_window (window > 0 with causal = 0 is INVALID_ARG)
+ * Both products run on the fp8 matrix cores; the probabilities are rounded
+ * to E4M3 before the product with V, so O carries a relative error of up to
+ * about 2^-4 per probability (the row sum and LSE use the unrounded values).
+ * A descale factor that is not positive and finite makes the rows of its
+ * heads NaN (checked on the device).  Errors as fa_fwd_gqa; null or
+ * misaligned descale pointers return INVALID_ARG / MISALIGNED. */
+int fa_fwd_fp8(const void* q, const void* k, const void* v,
+               const float* q_descale, const float* k_descale, const float* v_descale,
+               void* o, float* lse, int B, int H, int H_kv, int N, int d, float scale,
+               int causal, int window, hipStream_t stream);
+
 /* Human-readable text for a return code (static storage). */
 const char* fa_strerror(int code);
 

@@ -113,11 +113,14 @@ SUB_E4M3 = 2.0 ** -10
 FP8_MFMA_ACC = 2.0 ** -12
 
 
-def fp8_fwd_error_bound(q, k, v, scale, causal, window=None):
-    """Element-wise bound on |O_gpu - O_oracle| for one head (fp64 decoded inputs)."""
+def fp8_fwd_error_bound(q, k, v, scale, causal, window=None, rows=None):
+    """Element-wise bound on |O_gpu - O_oracle| for one head (fp64 decoded
+    inputs); ``rows`` restricts it to those query rows."""
     import oracle
 
-    p, m, _ = oracle.head_probabilities(q, k, scale, causal, window=window)
+    p, m, _ = oracle.head_probabilities(q, k, scale, causal, rows=rows, window=window)
+    if rows is not None:
+        q = q[np.asarray(rows)]
     vis = p > 0
     s = scale * (q @ k.T)
     # L_i = sum_j exp(s_ij - max_j s_ij) over visible keys

@@ -97,6 +97,33 @@ def test_window_argument_errors(lib):
     assert lib.fa_bwd_window(*p9, 1, 4, 2, 8, 64, 0.1, 3, V(FAKE), need - 1, None) == binding.FA_ERR_WORKSPACE
 
 
+def test_fp8_argument_errors(lib):
+    """fa_fwd_fp8: null or misaligned pointers (descales need 4 bytes), H_kv
+    not dividing H, a window without causal or below 0, unsupported d."""
+    V = ctypes.c_void_p
+    def call(ptrs=None, H=4, Hkv=2, d=64, causal=0, window=0, scale=0.1):
+        ptrs = [FAKE] * 8 if ptrs is None else ptrs
+        return lib.fa_fwd_fp8(*[V(p) if p else None for p in ptrs], 1, H, Hkv, 8, d, scale, causal,
+                              window, None)
+    for i in range(8):
+        ptrs = [FAKE] * 8
+        ptrs[i] = 0
+        assert call(ptrs) == binding.FA_ERR_INVALID_ARG
+    for i in (0, 1, 2, 6, 7):                      # q, k, v, o, lse: 16 bytes
+        ptrs = [FAKE] * 8
+        ptrs[i] = FAKE + 8
+        assert call(ptrs) == binding.FA_ERR_MISALIGNED
+    for i in (3, 4, 5):                            # descales: 4 bytes
+        ptrs = [FAKE] * 8
+        ptrs[i] = FAKE + 2
+        assert call(ptrs) == binding.FA_ERR_MISALIGNED
+    assert call(Hkv=3) == binding.FA_ERR_INVALID_ARG
+    assert call(window=4, causal=0) == binding.FA_ERR_INVALID_ARG
+    assert call(window=-1, causal=1) == binding.FA_ERR_INVALID_ARG
+    assert call(d=96) == binding.FA_ERR_UNSUPPORTED
+    assert call(scale=float("nan")) == binding.FA_ERR_INVALID_ARG
+
+
 def test_workspace_size(lib):
     def want(B, H, N, d):
         a256 = lambda x: (x + 255) // 256 * 256
