@@ -27,6 +27,7 @@ import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 PEAK_BF16_TFLOPS = 2516.6
+PEAK_FP8_TFLOPS = 5033.2     # dense fp8 MFMA: 256 CU x 8192 flop/clk x 2.4 GHz
 PEAK_HBM_GBS = 8000.0
 
 
@@ -118,7 +119,8 @@ def naive_step(torch, q, k, v, do, scale, causal):
 
 
 # Workloads reported beside the headline one (parity-test shapes of the
-# same kernels): forward and backward timed separately, median of 5.
+# same kernels): forward and backward timed separately, median of 5 samples
+# of 5 back-to-back calls.
 # (name, B, H, H_kv, N, d, causal, window): grouped-query attention with the
 # pages' Llama 2 70B head counts (64 query heads over 8 K/V heads), and a
 # causal sliding window of 4096 over 32768 tokens (the pages' Mistral 7B
@@ -130,6 +132,23 @@ EXTRA_WORKLOADS = [
     ("b2_h64_hkv8_n4096_d128_causal_gqa", 2, 64, 8, 4096, 128, True, None),
     ("b1_h32_n32768_d128_window4096", 1, 32, 32, 32768, 128, True, 4096),
 ]
+
+
+def median_ms(torch, f, reps=5, samples=5):
+    """Median over ``samples`` of the per-call time of ``reps`` back-to-back
+    calls of f (events on the current stream), after two warm-up calls."""
+    for _ in range(2):
+        f()
+    ms = []
+    for _ in range(samples):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1) / reps)
+    return sorted(ms)[samples // 2]
 
 
 def other_workloads(torch, binding, inputs, workloads, seed):
@@ -157,23 +176,39 @@ def other_workloads(torch, binding, inputs, workloads, seed):
         res = {}
         for tag, f, fl in (("fwd", fwd, workloads.fwd_flops(B, H, N, d, causal, window)),
                            ("bwd", bwd, workloads.bwd_flops(B, H, N, d, causal, window))):
-            for _ in range(2):
-                f()
-            ms = []
-            for _ in range(5):
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record()
-                f()
-                e1.record()
-                torch.cuda.synchronize()
-                ms.append(e0.elapsed_time(e1))
-            med = sorted(ms)[2]
+            med = median_ms(torch, f)
             res[f"{tag}_ms"] = round(med, 4)
             res[f"{tag}_tflops"] = round(fl / (med * 1e-3) / 1e12, 1)
         if window is not None:
             res["pairs_skipped_frac"] = round(1 - workloads.window_pairs(N, window) / N ** 2, 4)
         out[name] = res
         del q, k, v, do, o, lse, calls
+        torch.cuda.empty_cache()
+    return out
+
+
+# FP8 forward (fa_fwd_fp8, E4M3 inputs with per-head descales, bf16 O):
+# forward only, timed like the other workloads, against the dense fp8 MFMA
+# peak.
+FP8_WORKLOADS = [
+    ("b4_h32_n4096_d128_fp8", 4, 32, 32, 4096, 128, False, None),
+    ("b1_h32_n16384_d128_causal_fp8", 1, 32, 32, 16384, 128, True, None),
+]
+
+
+def fp8_workloads(torch, binding, inputs, workloads, seed):
+    out = {}
+    dev = torch.device("cuda:0")
+    for name, B, H, Hkv, N, d, causal, window in FP8_WORKLOADS:
+        x = inputs.make_qkv_fp8(B, N, H, d, seed=seed, H_kv=Hkv)
+        args = [x[n].to(dev) for n in ("q8", "k8", "v8", "q_descale", "k_descale", "v_descale")]
+        o, lse = binding.forward_fp8(*args, causal=causal, window=window)
+        med = median_ms(torch, lambda: binding.forward_fp8(*args, causal=causal, window=window,
+                                                           out=o, lse=lse))
+        tf = workloads.fwd_flops(B, H, N, d, causal, window) / (med * 1e-3) / 1e12
+        out[name] = {"fwd_ms": round(med, 4), "fwd_tflops": round(tf, 1),
+                     "frac_of_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4)}
+        del args, o, lse
         torch.cuda.empty_cache()
     return out
 
@@ -336,6 +371,7 @@ def main():
 
     if not args.no_extra:
         out["other_workloads"] = other_workloads(torch, binding, inputs, workloads, args.seed)
+        out["fp8_forward"] = fp8_workloads(torch, binding, inputs, workloads, args.seed)
 
     if not args.no_naive:
         try:
