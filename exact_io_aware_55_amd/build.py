@@ -29,11 +29,12 @@ FLAGS = [
 ]
 
 
-# Per-source extra flags.  The backward kernels keep their score tiles in
-# VGPRs: without this flag the compiler would put every MFMA result of a
-# one-wave-per-SIMD kernel in AGPRs and copy the tiles back for the softmax.
-# (The d = 128 dK/dV accumulators are placed in AGPRs explicitly.)
-EXTRA = {"fa_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Per-source extra flags.  The kernels keep their score tiles in VGPRs:
+# without this flag the compiler would put every MFMA result in AGPRs once
+# any accumulator lives there, and copy the tiles back for the softmax.  The
+# long-lived d = 128 dK/dV accumulators are placed in AGPRs explicitly.
+_VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+EXTRA = {"fa_bwd.hip": _VGPR_FORM}
 
 
 def _compile(src: str) -> str:

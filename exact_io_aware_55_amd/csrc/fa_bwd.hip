@@ -48,17 +48,6 @@ constexpr int NSTAGE = 3;    // query blocks resident in the LDS ring
 constexpr int ROWPAD = 64;   // row-statistic padding (= BR)
 }  // namespace bwd
 
-// acc += a * b on a 32x32x16 bf16 MFMA with the accumulator held in AGPRs.
-// The backward at d = 128 keeps dV^T and dK^T (128 registers) there so that
-// the VGPRs stay free for the score tiles; written as inline assembly because
-// the compiler otherwise picks one register form for all MFMAs of a kernel.
-// Callers must leave the MFMA result latency (the accumulators are only read
-// after the main loop) and must not feed it VGPRs written by the two preceding
-// VALU instructions.
-__device__ __forceinline__ void mfma_acc(f32x16& acc, const bf16x8& a, const u32x4& b) {
-    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
-
 __device__ __forceinline__ int xcd_remap_b(int bid, int nblocks) {
     const int per = nblocks >> 3, rem = nblocks & 7;
     const int x = bid & 7, i = bid >> 3;
@@ -429,7 +418,7 @@ __global__ __launch_bounds__(bwd::NT, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     FA_WAIT_VMCNT(0);                          // the loads past the last step
     // the accumulators are read below by VALU after MFMAs the compiler does
     // not see (inline assembly): wait out the MFMA result latency
-    asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
+    FA_MFMA_DRAIN();
 
     // epilogue: dK = scale * (dK^T)^T, dV; C layout of dV^T / dK^T: lane = key
     // column, registers = feature rows 8g + 4h + t

@@ -30,6 +30,20 @@ __device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b,
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// acc += a * b on a 32x32x16 bf16 MFMA with the accumulator held in AGPRs.
+// The d = 128 backward keeps dV^T and dK^T (128 registers) there so that the
+// VGPRs stay free for the score tiles (and vector instructions issued beside
+// an MFMA cost less with its accumulator in AGPRs).  Written as inline assembly because the compiler picks one register
+// form for all MFMAs of a kernel.  The compiler cannot see the hazards of an
+// MFMA inside assembly, so callers must (a) leave the MFMA result latency
+// before any vector instruction reads the accumulator (explicit s_nop), and
+// (b) not feed it VGPRs written by the two preceding vector instructions.
+__device__ __forceinline__ void mfma_acc(f32x16& acc, const bf16x8& a, const u32x4& b) {
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// wait states after inline-assembly MFMAs before their accumulators are read
+#define FA_MFMA_DRAIN() asm volatile("s_nop 15\n\ts_nop 15" ::: "memory")
+
 // 16-byte direct load through a buffer resource (buffer_load_dwordx4 ... lds):
 // as dma16, but the offset is checked against the resource's byte range and
 // lanes outside it read zeros, so tiles past the last row need no clamping.

@@ -7,16 +7,16 @@
 // exp(m_old - m_new) whenever the maximum grows, divides by l once at the end
 // and writes only O and one statistic per row (LSE = m + ln l).
 //
-// bf16 kernel layout (per workgroup: 4 waves, 128 queries, K/V blocks of 64):
+// bf16 kernel layout (per workgroup: 8 waves, 256 queries, K/V blocks of 64):
 //  * each wave owns 32 queries and keeps them in registers as the B operand of
 //    S^T = K Q^T, so a lane holds the scores of ONE query against 16 keys of
 //    each 32-key MFMA tile.  The row max/sum are in-lane reductions plus one
 //    exchange between the two lane halves.
 //  * P^T stays in registers: after exp and the bf16 conversion, registers of
 //    the S^T accumulator are directly the B operand of O^T += V^T P^T.
-//  * K is staged row-major in LDS (rows padded by 16 B); V is staged
-//    transposed (V^T, one row per feature) with keys placed in the k-slot
-//    order of the P^T registers and 16-byte chunks XOR-swizzled per row.
+//  * K and V are staged row-major in LDS (64-byte rows of 32 features, 16-byte
+//    chunks XOR-swizzled per row); V^T comes from transposing LDS reads
+//    (ds_read_b64_tr_b16) with keys in the k-slot order of the P^T registers.
 //  * K/V blocks stream through a 3-stage LDS ring by direct global -> LDS
 //    loads issued two blocks ahead: one barrier per block.
 //  * exponentials are v_exp_f32 (base 2) with scale * log2(e) folded into one
