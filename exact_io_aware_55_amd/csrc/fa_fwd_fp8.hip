@@ -17,11 +17,12 @@
 //    maximum keeps it there); the row sum l adds the unrounded fp32 P, and
 //    descale_v / l is applied once at the end.  O is written in bf16.
 //
-// Layout (per workgroup: 8 waves x 32 queries, K/V blocks of 64 keys):
+// Layout (per workgroup: 8 waves x 32 queries, K/V blocks of 128 keys at
+// d = 128, 64 at d = 64):
 //  * a lane keeps its query's codes as the B operand of S^T = K Q^T: 32 bytes
 //    (features 64 m + 32 h .. +31, h the lane half) per 64-feature MFMA; K is
 //    read with the same byte order, two 16-byte LDS reads per MFMA;
-//  * K and V blocks sit in LDS as [D/64 sub-tiles][64 rows][64 bytes] with
+//  * K and V blocks sit in LDS as [D/64 sub-tiles][BC rows][64 bytes] with
 //    16-byte chunks XOR-swizzled per row.  V is read with ds_read_b64_tr_b8:
 //    a 16-lane group reads 8 consecutive rows x 16 bytes and lane j receives
 //    byte column j of those rows.  A lane's P bytes hold keys
@@ -40,7 +41,6 @@ namespace fa {
 
 namespace fwd8 {
 constexpr int BR = 256;     // queries per workgroup (8 waves x 32)
-constexpr int BC = 64;      // keys per K/V block
 constexpr int NT = 512;     // threads per workgroup
 constexpr int NW = NT / 64; // waves
 constexpr int NSTAGE = 3;   // K/V blocks resident in the LDS ring
@@ -78,6 +78,10 @@ __global__ __launch_bounds__(fwd8::NT, 1) void fwd_fp8_kernel(
     const float* __restrict__ v_descale, __bf16* __restrict__ O, float* __restrict__ LSE, int H, int G,
     int N, int window, float scale_log2, int nqb) {
     using namespace fwd8;
+    // keys per K/V block: 128 at d = 128 (halves the per-block barrier, load
+    // and loop work against the short fp8 products; measured 10% faster),
+    // 64 at d = 64
+    constexpr int BC = D == 128 ? 128 : 64;
     constexpr int TILE = BC * D;               // bytes of one K or V block
     constexpr int STAGE = 2 * TILE;            // K then V
     constexpr int SUB = BC * 64;               // one 64-feature sub-tile
@@ -86,6 +90,8 @@ __global__ __launch_bounds__(fwd8::NT, 1) void fwd_fp8_kernel(
     constexpr int SEGS = TILE / 1024;          // 1 KB segments per tensor and block
     constexpr int SEG_SUB = SUB / 1024;        // segments per sub-tile
     constexpr int NL = 2 * SEGS / NW;          // direct loads per wave and block
+    constexpr int KT = BC / 32;                // 32-key score tiles per block
+    constexpr int KP = BC / 64;                // 64-key P V products per feature tile
     static_assert((2 * SEGS) % NW == 0 && NL >= 1, "segments per wave");
     static_assert(NL <= 15, "vmcnt immediate");
     __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * STAGE + 1024];
@@ -208,10 +214,10 @@ __global__ __launch_bounds__(fwd8::NT, 1) void fwd_fp8_kernel(
         const lds_char* vb0 = stage + v_rd0;
         const lds_char* vb1 = stage + v_rd1;
         asm volatile("" : "+v"(kb0), "+v"(kb1), "+v"(vb0), "+v"(vb1));
-        // S^T = K Q^T for two 32-key tiles
-        f32x16 s[2];
+        // S^T = K Q^T for the block's 32-key tiles
+        f32x16 s[KT];
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
+        for (int kt = 0; kt < KT; ++kt) {
             s[kt] = f32x16{};
 #pragma unroll
             for (int m = 0; m < DK; ++m) {
@@ -226,7 +232,7 @@ __global__ __launch_bounds__(fwd8::NT, 1) void fwd_fp8_kernel(
             const int lim_c = my_q - j0 - 4 * hl;
             const int lim_w = lim_c - window + 1;
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
+            for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int off = kt * 32 + (r >> 2) * 8 + (r & 3);
@@ -237,13 +243,13 @@ __global__ __launch_bounds__(fwd8::NT, 1) void fwd_fp8_kernel(
         float mx = s[0][0];
         if constexpr (POS) {
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
+            for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
             mx = halves_max(mx);
         } else {
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
+            for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) mx = fminf(mx, s[kt][r]);
             mx = halves_min(mx);
@@ -260,10 +266,10 @@ __global__ __launch_bounds__(fwd8::NT, 1) void fwd_fp8_kernel(
         const float m_sub = m_run == -INFINITY ? 0.f : m_run;
         // P = exp2(x - m); l sums the fp32 values, the product uses E4M3.
         // Byte 16 kt + r of the packed operand holds register r of tile kt.
-        i32x8 pw;
+        i32x8 pw[KP];
         float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+        for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
             for (int r = 0; r < 16; r += 4) {
                 float p[4];
@@ -276,22 +282,24 @@ __global__ __launch_bounds__(fwd8::NT, 1) void fwd_fp8_kernel(
                 ls1 += p[1] + p[3];
                 int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
                 w = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w, true);
-                pw[kt * 4 + (r >> 2)] = w;
+                pw[kt >> 1][(kt & 1) * 4 + (r >> 2)] = w;
             }
         l_run += ls0 + ls1;
         __builtin_amdgcn_sched_barrier(0);
         // O^T += V^T P^T: four transposing reads give the 32 key bytes of one
         // feature row, in the order of the P bytes
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            const lds_char* vb = ((dt & 1) ? vb1 : vb0) + (dt >> 1) * SUB;
-            const i32x2 a0 = lds_read_tr8(vb);
-            const i32x2 a1 = lds_read_tr8(vb + 16 * 64);
-            const i32x2 a2 = lds_read_tr8(vb + 32 * 64);
-            const i32x2 a3 = lds_read_tr8(vb + 48 * 64);
-            const i32x8 va = {a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
-            oacc[dt] = mfma_fp8(va, pw, oacc[dt]);
-        }
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int j = 0; j < KP; ++j) {
+                const lds_char* vb = ((dt & 1) ? vb1 : vb0) + (dt >> 1) * SUB + j * 64 * 64;
+                const i32x2 a0 = lds_read_tr8(vb);
+                const i32x2 a1 = lds_read_tr8(vb + 16 * 64);
+                const i32x2 a2 = lds_read_tr8(vb + 32 * 64);
+                const i32x2 a3 = lds_read_tr8(vb + 48 * 64);
+                const i32x8 va = {a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
+                oacc[dt] = mfma_fp8(va, pw[j], oacc[dt]);
+            }
         __builtin_amdgcn_sched_barrier(0);
     };
 #pragma clang loop unroll(disable)
