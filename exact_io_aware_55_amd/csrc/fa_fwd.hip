@@ -17,8 +17,9 @@
 //  * K and V are staged row-major in LDS (64-byte rows of 32 features, 16-byte
 //    chunks XOR-swizzled per row); V^T comes from transposing LDS reads
 //    (ds_read_b64_tr_b16) with keys in the k-slot order of the P^T registers.
-//  * K/V blocks stream through a 3-stage LDS ring by direct global -> LDS
-//    loads issued two blocks ahead: one barrier per block.
+//  * K/V blocks (128 keys at d = 128, 64 at d = 64) stream through an LDS
+//    ring (2 and 3 stages) by direct global -> LDS loads issued one or two
+//    blocks ahead: one barrier per block.
 //  * exponentials are v_exp_f32 (base 2) with scale * log2(e) folded into one
 //    FMA per score.
 #include <type_traits>
@@ -30,10 +31,8 @@ namespace fa {
 
 namespace fwd {
 constexpr int BR = 256;     // queries per workgroup (8 waves x 32)
-constexpr int BC = 64;      // keys per K/V block
 constexpr int NT = 512;     // threads per workgroup
 constexpr int NW = NT / 64; // waves
-constexpr int NSTAGE = 3;   // K/V blocks resident in the LDS ring
 }  // namespace fwd
 
 // LDS layout of one K or V block (BC keys): D/32 sub-tiles [BC keys][32
@@ -57,6 +56,13 @@ __global__ __launch_bounds__(fwd::NT, 1) void fwd_bf16_kernel(
     __bf16* __restrict__ O, float* __restrict__ LSE, int H, int G, int N, int window, float scale_log2,
     int nqb) {
     using namespace fwd;
+    // keys per K/V block and blocks resident in the LDS ring: 128 keys in a
+    // 2-stage ring at d = 128 (half the per-block barrier, load and loop work;
+    // 129 KB of LDS), 64 keys in a 3-stage ring at d = 64.  Loads run
+    // NSTAGE - 1 blocks ahead.
+    constexpr int BC = D == 128 ? 128 : 64;
+    constexpr int NSTAGE = D == 128 ? 2 : 3;
+    constexpr int KT = BC / 32;                // 32-key score tiles per block
     constexpr int TILE = BC * D * 2;           // one K or V block
     constexpr int STAGE = 2 * TILE;            // K then V
     constexpr int SUB = BC * 64;               // one sub-tile (32 features)
@@ -67,7 +73,7 @@ __global__ __launch_bounds__(fwd::NT, 1) void fwd_bf16_kernel(
     constexpr int SEG_SUB = SUB / 1024;        // segments per sub-tile
     static_assert(SEGS % NW == 0, "segments per wave");
 
-    static_assert(2 * SEG_W <= 15, "vmcnt immediate");
+    static_assert((NSTAGE - 1) * 2 * SEG_W <= 15, "vmcnt immediate");
     // the ring, then 1 KB that absorbs the direct loads of blocks past the
     // last one (every block issues the same loads, so no branch is needed)
     __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * STAGE + 1024];
@@ -136,8 +142,8 @@ __global__ __launch_bounds__(fwd::NT, 1) void fwd_bf16_kernel(
         }
     };
 
-    issue_tile(t_lo);
-    issue_tile(t_lo + 1);
+#pragma unroll
+    for (int i = 0; i < NSTAGE - 1; ++i) issue_tile(t_lo + i);
 
     // Queries of this lane, as B-operand chunks of S^T = K Q^T.  Rows past N
     // read row N-1 (finite data whose results are never stored).
@@ -179,9 +185,9 @@ __global__ __launch_bounds__(fwd::NT, 1) void fwd_bf16_kernel(
     // S^T = K Q^T, the online softmax and O^T += V^T P^T.
     auto block = [&](int t, auto mask_tag) {
         constexpr bool MASK = decltype(mask_tag)::value;
-        FA_WAIT_VMCNT(2 * SEG_W);
+        FA_WAIT_VMCNT((NSTAGE - 2) * 2 * SEG_W);
         __builtin_amdgcn_s_barrier();
-        if constexpr (MASK) issue_tile(t + 2);  // masked blocks may return early
+        if constexpr (MASK) issue_tile(t + NSTAGE - 1);  // masked blocks may return early
 
         const int j0 = t * BC;
         // every key after this wave's queries, or before all of their windows
@@ -194,10 +200,10 @@ __global__ __launch_bounds__(fwd::NT, 1) void fwd_bf16_kernel(
         const lds_char* kb1 = stage + k_rd1;
         const lds_char* vb = stage + v_rd;
         asm volatile("" : "+v"(kb0), "+v"(kb1), "+v"(vb));
-        // S^T = K Q^T for two 32-key tiles
-        f32x16 s[2];
+        // S^T = K Q^T for the block's 32-key tiles
+        f32x16 s[KT];
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
+        for (int kt = 0; kt < KT; ++kt) {
             s[kt] = f32x16{};
 #pragma unroll
             for (int c = 0; c < DC; ++c) {
@@ -205,9 +211,9 @@ __global__ __launch_bounds__(fwd::NT, 1) void fwd_bf16_kernel(
                 s[kt] = mfma32x32x16(lds_read_b128(a), qreg[c], s[kt]);
             }
         }
-        // unmasked blocks start the loads of block t + 2 here, behind the K
-        // reads, rather than as a burst at the top
-        if constexpr (!MASK) issue_tile(t + 2);
+        // unmasked blocks start the loads of block t + NSTAGE - 1 here,
+        // behind the K reads, rather than as a burst at the top
+        if constexpr (!MASK) issue_tile(t + NSTAGE - 1);
         // keep the V reads below the softmax (register pressure)
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (MASK) {
@@ -218,7 +224,7 @@ __global__ __launch_bounds__(fwd::NT, 1) void fwd_bf16_kernel(
             const int lim_c = my_q - j0 - 4 * hl;         // causal: off <= lim_c
             const int lim_w = lim_c - window + 1;         // window: off >= lim_w
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
+            for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int off = kt * 32 + (r >> 2) * 8 + (r & 3);
@@ -229,13 +235,13 @@ __global__ __launch_bounds__(fwd::NT, 1) void fwd_bf16_kernel(
         float mx = s[0][0];
         if constexpr (POS) {
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
+            for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
             mx = halves_max(mx);
         } else {
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
+            for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) mx = fminf(mx, s[kt][r]);
             mx = halves_min(mx);
@@ -255,10 +261,10 @@ __global__ __launch_bounds__(fwd::NT, 1) void fwd_bf16_kernel(
         const float m_sub = m_run == -INFINITY ? 0.f : m_run;
         // P = exp2(x - m): the row sum accumulates in fp32 (so LSE keeps
         // fp32 accuracy); the PV product uses P rounded to bf16
-        u32x4 pw[4];
+        u32x4 pw[2 * KT];
         float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+        for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
             for (int r = 0; r < 16; r += 2) {
                 float p0 = fast_exp2(__builtin_fmaf(s[kt][r], scale_log2, -m_sub));
@@ -279,7 +285,7 @@ __global__ __launch_bounds__(fwd::NT, 1) void fwd_bf16_kernel(
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
-            for (int cc = 0; cc < 4; ++cc) {
+            for (int cc = 0; cc < 2 * KT; ++cc) {
                 const lds_char* a0 = vb + dt * SUB + cc * 16 * 64;
                 const bf16x4 lo = lds_read_tr16(a0);
                 const bf16x4 hi = lds_read_tr16(a0 + 8 * 64);
