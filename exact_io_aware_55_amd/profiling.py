@@ -7,12 +7,15 @@ summary::
 
     python -m exact_io_aware_55_amd.profiling trace DIR OUT.md TITLE COMMAND
     python -m exact_io_aware_55_amd.profiling traffic FETCH WRITE COPY_FETCH COPY_WRITE OUT.md WORKLOAD
+    python -m exact_io_aware_55_amd.profiling counters MFMA_DIR LDS_DIR TRACE_DIR OUT.md WORKLOAD
 
 ``DIR`` holds a ``--kernel-trace --stats`` run (``*_kernel_stats.csv``); the
 traffic arguments are the output folders of four ``--pmc`` runs: FETCH_SIZE
 and WRITE_SIZE of the bench workload, and the same two counters for the
 ``bench.py --copy-calibration`` device copy of 1 GiB, whose known byte count
-scales the counters to bytes.
+scales the counters to bytes.  ``counters`` summarises two more ``--pmc``
+runs: matrix-core busy cycles and bf16 MFMA operations, and LDS bank / address
+conflicts and LDS activity.
 """
 import csv
 import glob
@@ -106,6 +109,76 @@ def traffic(fetch, write, copy_fetch, copy_write, out, workload, compulsory=None
     return fs, ws, lines
 
 
+def _counter_rows(folder):
+    """kernel -> {counter: mean value, '_ns': mean dispatch duration}."""
+    acc, dur = {}, {}
+    for f in glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            k = _short(r["Kernel_Name"])
+            acc.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+            dur.setdefault(k, []).append(float(r["End_Timestamp"]) - float(r["Start_Timestamp"]))
+    return {k: dict({c: sum(v) / len(v) for c, v in cs.items()}, _ns=sum(dur[k]) / len(dur[k]))
+            for k, cs in acc.items()}
+
+
+def _agent(folder):
+    for f in glob.glob(os.path.join(folder, "**", "*agent_info.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Agent_Type"] == "GPU":
+                return int(r["Num_Xcc"]), int(r["Cu_Count"]), int(r["Simd_Per_Cu"])
+    return 8, 256, 4
+
+
+def _trace_ns(folder):
+    """kernel -> average duration (ns) from a --kernel-trace --stats run."""
+    rows = csv.DictReader(open(_one(os.path.join(folder, "**", "*kernel_stats.csv"))))
+    return {_short(r["Name"]): float(r["AverageNs"]) for r in rows}
+
+
+def counters(mfma_dir, lds_dir, trace_dir, out, workload):
+    m, l = _counter_rows(mfma_dir), _counter_rows(lds_dir)
+    tns = _trace_ns(trace_dir)
+    xcc, cus, simds = _agent(mfma_dir)
+    lines = [f"# Matrix-core and LDS counters per launch: {workload}", "",
+             "Commands (from the repository root on one MI355X, after "
+             "`cd /tmp && export TMPDIR=/tmp`; `$REPO` is the repository root):", "", "```",
+             "rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_BUSY_CU_CYCLES "
+             "GRBM_GUI_ACTIVE --output-format csv -d $REPO/gpurun_out/pmc_mfma -o bench -- "
+             "python3 $REPO/bench.py --steps 2 --warmup 1 --no-naive --no-cpu --no-extra",
+             "rocprofv3 --pmc SQ_LDS_BANK_CONFLICT SQ_LDS_ADDR_CONFLICT SQ_LDS_IDX_ACTIVE SQ_INSTS_LDS "
+             "SQ_BUSY_CU_CYCLES --output-format csv -d $REPO/gpurun_out/pmc_lds -o bench -- "
+             "python3 $REPO/bench.py --steps 2 --warmup 1 --no-naive --no-cpu --no-extra",
+             "python -m exact_io_aware_55_amd.profiling counters gpurun_out/pmc_mfma gpurun_out/pmc_lds "
+             f"gpurun_out/prof profiles/<this file> {workload}",
+             "```", "",
+             f"Derived columns (the GPU reports {xcc} XCDs, {cus} CUs, {simds} SIMDs per CU):",
+             "- clock = GRBM_GUI_ACTIVE / XCDs / launch duration, the duration taken from the "
+             "kernel-trace run (`gpurun_out/prof`, the command in the kernel-trace summary): counter "
+             "collection lengthens each launch, so its own timestamps would understate the clock;",
+             "- MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / XCDs x CUs x SIMDs): the share "
+             "of SIMD cycles at the running clock in which the matrix core was busy;",
+             "- MFMA flops = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 (a 32x32x16 bf16 MFMA is 32768 flops "
+             "and counts 64);",
+             "- LDS active = SQ_LDS_IDX_ACTIVE / SQ_BUSY_CU_CYCLES.", "",
+             "| kernel | launch (us, traced) | clock (GHz) | MFMA busy | MFMA flops (G) | LDS bank conflicts | "
+             "LDS address conflicts | LDS instructions (M) | LDS active |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    for k, c in m.items():
+        grbm = c.get("GRBM_GUI_ACTIVE", 0.0) / xcc
+        ns = tns.get(k, c["_ns"])
+        clock = grbm / ns if ns else 0.0
+        busy = c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (grbm * cus * simds) if grbm else 0.0
+        flops = c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) * 512 / 1e9
+        d = l.get(k, {})
+        act = d.get("SQ_LDS_IDX_ACTIVE", 0.0) / d["SQ_BUSY_CU_CYCLES"] if d.get("SQ_BUSY_CU_CYCLES") else 0.0
+        lines.append(f"| `{k}` | {ns / 1e3:.0f} | {clock:.2f} | {100 * busy:.1f}% | {flops:.0f} | "
+                     f"{d.get('SQ_LDS_BANK_CONFLICT', float('nan')):.0f} | "
+                     f"{d.get('SQ_LDS_ADDR_CONFLICT', float('nan')):.0f} | "
+                     f"{d.get('SQ_INSTS_LDS', 0.0) / 1e6:.1f} | {100 * act:.0f}% |")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
 def compulsory_bytes(B, H, N, d, causal):
     """Bytes each kernel must move at least (bf16 tensors, fp32 statistics)."""
     t = B * H * N * d * 2                       # one [B,N,H,d] bf16 tensor
@@ -122,6 +195,8 @@ def compulsory_bytes(B, H, N, d, causal):
 def main(argv):
     if len(argv) >= 5 and argv[0] == "trace":
         trace(argv[1], argv[2], argv[3], argv[4])
+    elif len(argv) >= 6 and argv[0] == "counters":
+        counters(argv[1], argv[2], argv[3], argv[4], argv[5])
     elif len(argv) >= 7 and argv[0] == "traffic":
         workload = argv[6]
         shape = {p[0]: p[1:] for p in workload.split("_") if p[:1] in "bhnd" and p[1:].isdigit()}
