@@ -44,7 +44,6 @@ constexpr int NT = 256;      // threads per workgroup (4 waves, one per SIMD)
 constexpr int NW = 4;
 constexpr int KB = 128;      // keys per workgroup (32 per wave)
 constexpr int BR = 64;       // queries per step
-constexpr int NSTAGE = 3;    // query blocks resident in the LDS ring
 constexpr int ROWPAD = 64;   // row-statistic padding (= BR)
 }  // namespace bwd
 
@@ -111,6 +110,11 @@ __global__ __launch_bounds__(bwd::NT, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     constexpr int STAGE = 2 * QT + NW * 1024;  // Q, dO, one stats copy per wave
     constexpr int KVB = KB * D * 2;            // bytes of a K or V block
     constexpr int SUBK = KB * 64;              // K/V sub-tile: KB rows x 32 features
+    // query blocks resident in the LDS ring: 4 at d = 128, where one
+    // barrier serves two steps (145 KB of LDS), 3 at d = 64, where two
+    // workgroups share a CU and each step has its barrier
+    constexpr int NSTAGE = D == 128 ? 4 : 3;
+    constexpr bool PAIRED = NSTAGE == 4;
     constexpr int RING = NSTAGE * STAGE;
     constexpr int SEG_QO = 2 * QT / 1024 / NW; // Q + dO segments per wave per step
     constexpr int DMA_W = SEG_QO + 1;          // direct loads per wave per step
@@ -266,11 +270,22 @@ __global__ __launch_bounds__(bwd::NT, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
 
 #pragma clang loop unroll(disable)
     for (int it = 0; it < nst_all; ++it) {
-        // this step's loads are done once at most one step's loads are in
-        // flight; after the barrier nobody reads the stage of step it - 1,
-        // which the loads of step it + 2 (spread over the units below) refill
-        FA_WAIT_VMCNT(DMA_W);
-        __builtin_amdgcn_s_barrier();
+        // 3 stages: this step's loads are done once at most one step's loads
+        // are in flight; after the barrier nobody reads the stage of step
+        // it - 1, which the loads of step it + 2 (spread over the units below)
+        // refill.  4 stages (paired): even steps wait for every load in flight
+        // (those of this step and the next), and their barrier retires all
+        // reads of steps it - 2 and it - 1, whose stages the loads of steps
+        // it + 2 and it + 3 refill; odd steps need neither.
+        if constexpr (PAIRED) {
+            if ((it & 1) == 0) {
+                FA_WAIT_VMCNT(0);
+                __builtin_amdgcn_s_barrier();
+            }
+        } else {
+            FA_WAIT_VMCNT(DMA_W);
+            __builtin_amdgcn_s_barrier();
+        }
 
         int g_unused;
         const int i0 = step_of(it, g_unused) * BR;
