@@ -47,11 +47,6 @@ constexpr int BR = 64;       // queries per step
 constexpr int ROWPAD = 64;   // row-statistic padding (= BR)
 }  // namespace bwd
 
-__device__ __forceinline__ int xcd_remap_b(int bid, int nblocks) {
-    const int per = nblocks >> 3, rem = nblocks & 7;
-    const int x = bid & 7, i = bid >> 3;
-    return x * per + (x < rem ? x : rem) + i;
-}
 
 // ---------------------------------------------------------------------------
 // 1. -D_i = -sum_k dO_ik O_ik and LSE_i * log2(e) (padded rows).
@@ -134,9 +129,8 @@ __global__ __launch_bounds__(bwd::NT, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     // attention the G query heads hk G .. hk G + G - 1 share K/V head hk, and
     // the workgroup walks the query blocks of all of them (G = 1: one head)
     const int Hkv = H / G;
-    const int logical = xcd_remap_b(blockIdx.x, gridDim.x);
-    const int bhk = logical / nkb;
-    const int kb = logical - bhk * nkb;
+    int bhk, kb;                               // causal: key block 0 (the longest) first
+    order_blocks(blockIdx.x, gridDim.x, nkb, CAUSAL, false, bhk, kb);
     const int b = bhk / Hkv, hk = bhk - b * Hkv;
     const int row_stride = H * D;
     const unsigned row_bytes = (unsigned)row_stride * 2u;
@@ -493,10 +487,8 @@ __global__ __launch_bounds__(bwdq::NT, 1) void bwd_dq_kernel(
     const int l32 = lane & 31, hl = lane >> 5;
     const int tg = lane >> 4, tj = lane & 15;
 
-    const int logical = xcd_remap_b(blockIdx.x, gridDim.x);
-    const int bh = logical / nqb;
-    int qb = logical - bh * nqb;
-    if (CAUSAL) qb = nqb - 1 - qb;             // longest rows first
+    int bh, qb;                                // causal: longest query blocks first
+    order_blocks(blockIdx.x, gridDim.x, nqb, CAUSAL, true, bh, qb);
     const int b = bh / H, h = bh - b * H;
     const int row_stride = H * D;
     const long head_off = ((long)b * N * H + h) * D;

@@ -89,6 +89,30 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
     return x * per + (x < rem ? x : rem) + i;
 }
 
+// (head, block) of a workgroup.  Ids the hardware sends to one XCD (ids
+// congruent mod 8) cover whole heads, so their K/V (or Q/dO) stay in that
+// XCD's L2.  With a causal mask the work of a block depends on its index:
+// `desc` says the longest block has the highest index (query blocks) rather
+// than index 0 (key blocks).  When every XCD's share is a whole number of
+// heads, the XCD takes the longest block of each of its heads first, then the
+// next longest, and so on, so no long block starts at the end of the grid.
+// Otherwise heads are taken one at a time, each longest block first.
+__device__ __forceinline__ void order_blocks(int bid, int nblocks, int nb, bool causal, bool desc, int& bh,
+                                             int& blk) {
+    int rank;
+    if (causal && nblocks % (8 * nb) == 0) {
+        const int nh = nblocks / (8 * nb);     // heads per XCD
+        const int x = bid & 7, i = bid >> 3;
+        rank = i / nh;
+        bh = x * nh + (i - rank * nh);
+    } else {
+        const int logical = xcd_remap(bid, nblocks);
+        bh = logical / nb;
+        rank = logical - bh * nb;
+    }
+    blk = causal && desc ? nb - 1 - rank : rank;
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ u32x4 ld_global16(const void* p) {

@@ -83,10 +83,8 @@ __global__ __launch_bounds__(fwd::NT, 1) void fwd_bf16_kernel(
     const int l32 = lane & 31, hl = lane >> 5;
 
     const int nblocks = gridDim.x;
-    const int logical = xcd_remap(blockIdx.x, nblocks);
-    const int bh = logical / nqb;
-    int qb = logical - bh * nqb;
-    if (CAUSAL) qb = nqb - 1 - qb;             // longest rows first
+    int bh, qb;                                // causal: longest query blocks first
+    order_blocks(blockIdx.x, nblocks, nqb, CAUSAL, true, bh, qb);
     const int b = bh / H, h = bh - b * H;
     const int row_stride = H * D;              // elements between sequence rows (N*H*D < 2^31)
     const long head_off = ((long)b * N * H + h) * D;

@@ -100,10 +100,8 @@ __global__ __launch_bounds__(fwd8::NT, 1) void fwd_fp8_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, hl = lane >> 5;
 
-    const int logical = xcd_remap(blockIdx.x, gridDim.x);
-    const int bh = logical / nqb;
-    int qb = logical - bh * nqb;
-    if (CAUSAL) qb = nqb - 1 - qb;             // longest rows first
+    int bh, qb;                                // causal: longest query blocks first
+    order_blocks(blockIdx.x, gridDim.x, nqb, CAUSAL, true, bh, qb);
     const int b = bh / H, h = bh - b * H;
     const int Hkv = H / G, hk = h / G;
     const int row_stride = H * D;              // elements between rows (Q bytes, O bf16)
