@@ -91,7 +91,9 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* __restrict__
 // ---------------------------------------------------------------------------
 // 2. dK, dV: key-block kernel
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL>
+// WIN: a sliding window narrower than N (causal only); without it the mask
+// is the causal compare alone
+template <int D, bool CAUSAL, bool WIN>
 __global__ __launch_bounds__(bwd::NT, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const __bf16* __restrict__ dO, const float* __restrict__ stats, int delta_off,
@@ -373,7 +375,7 @@ __global__ __launch_bounds__(bwd::NT, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
                             if constexpr (MASK) {
                                 // hidden pairs get exp2(-inf) = 0, and so dS = 0 as dP is finite
                                 const int off = 32 * m + 8 * (rr >> 2) + (rr & 3);
-                                const bool vis = (off >= lim_c) & (off <= lim_w);
+                                const bool vis = WIN ? (off >= lim_c) & (off <= lim_w) : off >= lim_c;
                                 x = vis ? x : -INFINITY;
                             }
                             const float p = fast_exp2(x);
@@ -458,7 +460,6 @@ constexpr int BR = 256;      // queries per workgroup (8 waves x 32)
 constexpr int BC = 64;       // keys per K/V block
 constexpr int NT = 512;
 constexpr int NW = 8;
-constexpr int NSTAGE = 3;
 }  // namespace bwdq
 
 template <int D, bool CAUSAL>
@@ -468,6 +469,10 @@ __global__ __launch_bounds__(bwdq::NT, 1) void bwd_dq_kernel(
     __bf16* __restrict__ dQ, int H, int G, int N, int window, int Npad, float scale, float scale_log2,
     int nqb) {
     using namespace bwdq;
+    // K/V blocks resident in the LDS ring: 4 at d = 128, where one barrier
+    // serves two blocks (129 KB of LDS), 3 at d = 64
+    constexpr int NSTAGE = D == 128 ? 4 : 3;
+    constexpr bool PAIRED = NSTAGE == 4;
     constexpr int DC = D / 16;
     constexpr int DT = D / 32;
     constexpr int TILE = BC * D * 2;           // one K or V block
@@ -576,8 +581,21 @@ __global__ __launch_bounds__(bwdq::NT, 1) void bwd_dq_kernel(
     // S^T = K Q^T, dP^T = V dO^T (lane = query), dS^T, dQ^T += K^T dS^T
     auto tile = [&](int t, auto masked) {
         constexpr bool MASK = decltype(masked)::value;
-        FA_WAIT_VMCNT(2 * SEG_W);
-        __builtin_amdgcn_s_barrier();
+        // 3 stages: wait for this block (the next may be in flight); the
+        // barrier retires the reads of block t - 1, whose stage the loads of
+        // block t + 2 refill.  4 stages (paired): even blocks (counted from
+        // t_lo) wait for both blocks in flight, and their barrier retires the
+        // reads of blocks t - 2 and t - 1, whose stages blocks t + 2 and t + 3
+        // refill; odd blocks need neither.
+        if constexpr (PAIRED) {
+            if (((t - t_lo) & 1) == 0) {
+                FA_WAIT_VMCNT(0);
+                __builtin_amdgcn_s_barrier();
+            }
+        } else {
+            FA_WAIT_VMCNT(2 * SEG_W);
+            __builtin_amdgcn_s_barrier();
+        }
         if constexpr (MASK) issue_tile(t + 2);
 
         const int j0 = t * BC;
@@ -694,15 +712,18 @@ hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const vo
     const dim3 grid((unsigned)(B * Hkv * nkb)), block(bwd::NT);
     const float sl2 = scale * kLog2e;
     const int delta_off = (int)((const char*)delta - (const char*)lse2);
-#define FA_BWD_LAUNCH(DD, CC)                                                                        \
-    hipLaunchKernelGGL((bwd_dkdv_kernel<DD, CC>), grid, block, 0, stream, Qp, Kp, Vp, dOp, lse2,    \
+#define FA_BWD_LAUNCH(DD, CC, WW)                                                                    \
+    hipLaunchKernelGGL((bwd_dkdv_kernel<DD, CC, WW>), grid, block, 0, stream, Qp, Kp, Vp, dOp, lse2, \
                        delta_off, dKp, dVp, H, G, N, win, Npad, scale, sl2, nkb)
+    const bool narrow = causal && win < N;     // a window that hides keys
     if (d == 128) {
-        if (causal) FA_BWD_LAUNCH(128, true);
-        else FA_BWD_LAUNCH(128, false);
+        if (narrow) FA_BWD_LAUNCH(128, true, true);
+        else if (causal) FA_BWD_LAUNCH(128, true, false);
+        else FA_BWD_LAUNCH(128, false, false);
     } else {
-        if (causal) FA_BWD_LAUNCH(64, true);
-        else FA_BWD_LAUNCH(64, false);
+        if (narrow) FA_BWD_LAUNCH(64, true, true);
+        else if (causal) FA_BWD_LAUNCH(64, true, false);
+        else FA_BWD_LAUNCH(64, false, false);
     }
 #undef FA_BWD_LAUNCH
     return hipGetLastError();
