@@ -15,15 +15,17 @@
 //   2. bwd_dkdv: one workgroup per block of 128 keys of one head (4 waves, one
 //      per SIMD, 32 keys each).  K and V of a wave's keys stay in registers.
 //      The workgroup walks the query blocks of 64 rows that can see its keys;
-//      Q, dO and the row statistics stream into a 3-stage LDS ring by direct
+//      Q, dO and the row statistics stream into an LDS ring (4 stages and one
+//      barrier per two steps at d = 128, 3 stages at d = 64) by direct
 //      global -> LDS loads.  Per block it recomputes S = Q K^T and P, forms
 //      dP = dO V^T and dS, and accumulates dV^T += dO^T P and dK^T += Q^T dS
 //      in registers.
 //   3. bwd_dq:   one workgroup per block of 256 queries (8 waves, 32 queries
 //      each, two waves per SIMD), laid out like the forward: Q and dO of a
 //      wave's queries stay in registers, K/V blocks of 64 keys stream through
-//      a 3-stage LDS ring.  Per block it recomputes S^T = K Q^T, P^T and
-//      dP^T = V dO^T (one query per lane, so LSE and D are per-lane scalars),
+//      an LDS ring (4 stages at d = 128, 3 at d = 64).  Per block it
+//      recomputes S^T = K Q^T, P^T and dP^T = V dO^T (one query per lane, so
+//      LSE and D are per-lane scalars),
 //      forms dS^T and accumulates dQ^T += K^T dS^T with dS^T straight from
 //      registers.  Splitting dQ out costs two extra matrix products (S and dP
 //      are formed twice) but needs no atomics and no LDS round trip for dS,
