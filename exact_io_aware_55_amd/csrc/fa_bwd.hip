@@ -47,6 +47,7 @@ constexpr int NW = 4;
 constexpr int KB = 128;      // keys per workgroup (32 per wave)
 constexpr int BR = 64;       // queries per step
 constexpr int ROWPAD = 64;   // row-statistic padding (= BR)
+constexpr int PRE_RPT = 2;   // preprocess rows per thread (2 measured best; 4 and 8 slower)
 }  // namespace bwd
 
 
@@ -54,6 +55,8 @@ constexpr int ROWPAD = 64;   // row-statistic padding (= BR)
 // 1. -D_i = -sum_k dO_ik O_ik and LSE_i * log2(e) (padded rows).
 // Rows are enumerated in [B, H, Npad] order.
 // ---------------------------------------------------------------------------
+// Each thread keeps RPT rows' loads in flight (2 RPT 16-byte loads): the
+// kernel is bound by HBM latency and bandwidth, not arithmetic.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* __restrict__ O,
                                                       const __bf16* __restrict__ dO,
@@ -62,31 +65,47 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* __restrict__
                                                       float* __restrict__ delta, int H, int N,
                                                       int Npad, long rows) {
     constexpr int TPR = D / 8;                 // threads per row (8 elements each)
-    constexpr int RPB = 256 / TPR;             // rows per block
+    constexpr int RG = 256 / TPR;              // row groups per block
+    constexpr int RPT = bwd::PRE_RPT;          // rows per thread
     const int tid = threadIdx.x;
-    const long row = (long)blockIdx.x * RPB + tid / TPR;
-    const int part = tid % TPR;
-    const long bh = row / Npad;
-    const int i = (int)(row - bh * Npad);
-    const bool live = row < rows && i < N;
-    float acc = 0.f;
-    if (live) {
-        const long b = bh / H, h = bh - b * H;
-        const long off = ((b * N + i) * H + h) * D + part * 8;
-        const u32x4 a = ld_global16(O + off), g = ld_global16(dO + off);
+    const int part = tid % TPR, rg = tid / TPR;
+    u32x4 a[RPT], g[RPT];
+    long row[RPT];
+    bool live[RPT];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const float a0 = __builtin_bit_cast(float, a[w] << 16), a1 = __builtin_bit_cast(float, a[w] & 0xffff0000u);
-            const float g0 = __builtin_bit_cast(float, g[w] << 16), g1 = __builtin_bit_cast(float, g[w] & 0xffff0000u);
-            acc = __builtin_fmaf(a0, g0, acc);
-            acc = __builtin_fmaf(a1, g1, acc);
+    for (int j = 0; j < RPT; ++j) {
+        // rows of one block: RPT passes of RG consecutive rows
+        row[j] = ((long)blockIdx.x * RPT + j) * RG + rg;
+        const long bh = row[j] / Npad;
+        const int i = (int)(row[j] - bh * Npad);
+        live[j] = row[j] < rows && i < N;
+        if (live[j]) {
+            const long b = bh / H, h = bh - b * H;
+            const long off = ((b * N + i) * H + h) * D + part * 8;
+            a[j] = ld_global16(O + off);
+            g[j] = ld_global16(dO + off);
         }
     }
 #pragma unroll
-    for (int s = TPR / 2; s > 0; s >>= 1) acc += __shfl_xor(acc, s);
-    if (row < rows && part == 0) {
-        delta[row] = live ? -acc : 0.f;       // stored negated: it seeds dP
-        lse2[row] = live ? LSE[bh * N + i] * kLog2e : INFINITY;
+    for (int j = 0; j < RPT; ++j) {
+        float acc = 0.f;
+        if (live[j]) {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const float a0 = __builtin_bit_cast(float, a[j][w] << 16), a1 = __builtin_bit_cast(float, a[j][w] & 0xffff0000u);
+                const float g0 = __builtin_bit_cast(float, g[j][w] << 16), g1 = __builtin_bit_cast(float, g[j][w] & 0xffff0000u);
+                acc = __builtin_fmaf(a0, g0, acc);
+                acc = __builtin_fmaf(a1, g1, acc);
+            }
+        }
+#pragma unroll
+        for (int s = TPR / 2; s > 0; s >>= 1) acc += __shfl_xor(acc, s);
+        if (row[j] < rows && part == 0) {
+            const long bh = row[j] / Npad;
+            const int i = (int)(row[j] - bh * Npad);
+            delta[row[j]] = live[j] ? -acc : 0.f;   // stored negated: it seeds dP
+            lse2[row[j]] = live[j] ? LSE[bh * N + i] * kLog2e : INFINITY;
+        }
     }
 }
 
@@ -689,7 +708,7 @@ hipError_t launch_bwd_preprocess(const void* o, const void* dout, const float* l
     auto dOp = static_cast<const __bf16*>(dout);
     const int Npad = bwd_rows_padded(N);
     const long rows = (long)B * H * Npad;
-    const int rpb = 256 / (d / 8);
+    const int rpb = 256 / (d / 8) * bwd::PRE_RPT;
     const dim3 grid((unsigned)((rows + rpb - 1) / rpb));
     if (d == 128)
         hipLaunchKernelGGL((bwd_pre_kernel<128>), grid, dim3(256), 0, stream, Op, dOp, lse, lse2, delta, H, N, Npad, rows);
