@@ -86,6 +86,20 @@ def test_bwd_causal_n4096_d64(gpu_lib):
     full_size_properties(x, grads)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_b4_h32_n4096_d128(gpu_lib, causal):
+    """The benchmark's forward+backward shape and launch configuration
+    (B=4, H=32, N=4096, d=128, bf16): two heads checked fully against the
+    oracle; every head checked for finite gradients and the invariants
+    sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i."""
+    w = workloads.MHA_N4096_D128_CAUSAL if causal else workloads.MHA_N4096_D128
+    print(f"\n[bwd] {w.name}", flush=True)
+    x = inputs.make_qkv(w.B, w.N, w.H, w.d, torch.bfloat16, seed=w.seed, with_do=True)
+    grads = run(gpu_lib, x, w.causal)
+    compare_heads(x, grads, w.scale, w.causal, [(0, 0), (w.B - 1, w.H - 1)], w.name)
+    full_size_properties(x, grads)
+
+
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("N", [512, 1024, 2048, 4096, 8192])
 def test_bwd_sweep(gpu_lib, N, d):

@@ -116,3 +116,20 @@ def test_fp8_forward_full_size_sampled(gpu_lib):
         bd = fp8_fwd_error_bound(*args, rows=[i])
         assert_within_bound(got_o[b, i, h][None], ro, bd, f"row {(b, h, i)}", slack=1.0)
         assert abs(got_l[b, h, i] - rl[0]) <= 1e-3
+
+
+def test_fp8_forward_long_causal_sampled(gpu_lib):
+    """B=1 H=32 N=16384 d=128 causal (the second FP8 benchmark shape): sampled
+    rows against the oracle's rows, each within the element-wise bound."""
+    B, N, H, d = 1, 16384, 32, 128
+    print(f"\n[fp8 fwd] long causal B{B} N{N} H{H} d{d}", flush=True)
+    x = inputs.make_qkv_fp8(B, N, H, d, seed=36)
+    o, lse = run(gpu_lib, x, True)
+    q, k, v = decoded(x)
+    got_o, got_l = inputs.to_f64(o), inputs.to_f64(lse)
+    for b, h, i in inputs.pick_rows(B, H, N, 24, seed=37):
+        args = (q[b, :, h], k[b, :, h], v[b, :, h], d ** -0.5, True)
+        ro, rl = oracle.head_forward(*args, rows=[i])
+        bd = fp8_fwd_error_bound(*args, rows=[i])
+        assert_within_bound(got_o[b, i, h][None], ro, bd, f"row {(b, h, i)}", slack=1.0)
+        assert abs(got_l[b, h, i] - rl[0]) <= 1e-3
