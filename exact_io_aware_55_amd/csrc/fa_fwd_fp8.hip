@@ -13,8 +13,8 @@
 // run on the fp8 matrix core (v_mfma_f32_32x32x64_f8f6f4, fp32 accumulate):
 //  * S^T = K Q^T from the codes; scale * descale_q * descale_k * log2(e) is
 //    folded into the one FMA before each exponential;
-//  * O^T += V^T P^T with P rounded to E4M3 (P <= 2^8 < 448, the lazy running
-//    maximum keeps it there); the row sum l adds the unrounded fp32 P, and
+//  * O^T += V^T P^T with P rounded to E4M3 (P <= 2^8 < 448: the running
+//    maximum is raised whenever a block's probabilities would exceed that); the row sum l adds the unrounded fp32 P, and
 //    descale_v / l is applied once at the end.  O is written in bf16.
 //
 // Layout (per workgroup: 8 waves x 32 queries, K/V blocks of 128 keys at
@@ -183,9 +183,8 @@ __global__ __launch_bounds__(fwd8::NT, 1) void fwd_fp8_kernel(
     f32x16 oacc[DT];
 #pragma unroll
     for (int i = 0; i < DT; ++i) oacc[i] = f32x16{};
-    // lazy running maximum (log2 units): raised only when a block's maximum
-    // exceeds it by more than kLazy, so P = exp2(x - m) <= 2^kLazy = 256
-    constexpr float kLazy = 8.f;
+    // running maximum (log2 units): raised only when a block's probabilities
+    // grow too large (see below), so P = exp2(x - m) stays <= 256 < 448
     float m_run = -INFINITY;
     float l_run = 0.f;
     constexpr float masked = POS ? -INFINITY : INFINITY;
@@ -238,50 +237,62 @@ __global__ __launch_bounds__(fwd8::NT, 1) void fwd_fp8_kernel(
                     s[kt][r] = vis ? s[kt][r] : masked;
                 }
         }
-        float mx = s[0][0];
-        if constexpr (POS) {
+        // P = exp2(x - m) against the running maximum as it stands; l sums the
+        // fp32 values, the product uses E4M3.  Byte 16 kt + r of the packed
+        // operand holds register r of tile kt.  A lane whose block sum exceeds
+        // kSumMax (so some P might exceed 2^8), or whose row has no maximum
+        // yet, sends the wave through the slow path: block maximum, rescale of
+        // O and l, exponentials again.  Every P that reaches the E4M3 product
+        // is then at most 2^8 < 448, and O, l and LSE all use the same m.
+        constexpr float kSumMax = 256.f;
+        i32x8 pw[KP];
+        float ls0, ls1;
+        auto exps = [&](float m_sub) {
+            ls0 = 0.f;
+            ls1 = 0.f;
 #pragma unroll
             for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
-            mx = halves_max(mx);
-        } else {
+                for (int r = 0; r < 16; r += 4) {
+                    float p[4];
 #pragma unroll
-            for (int kt = 0; kt < KT; ++kt)
+                    for (int e = 0; e < 4; ++e) {
+                        p[e] = fast_exp2(__builtin_fmaf(s[kt][r + e], sl2, -m_sub));
+                        if constexpr (MASK) p[e] = s[kt][r + e] == masked ? 0.f : p[e];
+                    }
+                    ls0 += p[0] + p[2];
+                    ls1 += p[1] + p[3];
+                    int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+                    w = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w, true);
+                    pw[kt >> 1][(kt & 1) * 4 + (r >> 2)] = w;
+                }
+        };
+        exps(m_run == -INFINITY ? 0.f : m_run);
+        if (__builtin_amdgcn_ballot_w64(!(ls0 + ls1 <= kSumMax) || m_run == -INFINITY) != 0) {
+            float mx = s[0][0];
+            if constexpr (POS) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fminf(mx, s[kt][r]);
-            mx = halves_min(mx);
-        }
-        const float mt = mx * sl2;
-        if (__builtin_amdgcn_ballot_w64(mt > m_run + kLazy) != 0) {
-            const float m_new = fmaxf(m_run, mt);
+                for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
+                mx = halves_max(mx);
+            } else {
+#pragma unroll
+                for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) mx = fminf(mx, s[kt][r]);
+                mx = halves_min(mx);
+            }
+            const float m_new = fmaxf(m_run, mx * sl2);
+            // a row that has seen no visible key yet has l = 0 and O = 0: any
+            // finite alpha will do, and -inf - -inf is NaN
             const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
             m_run = m_new;
             l_run *= alpha;
 #pragma unroll
             for (int i = 0; i < DT; ++i) oacc[i] *= alpha;
+            exps(m_run == -INFINITY ? 0.f : m_run);
         }
-        const float m_sub = m_run == -INFINITY ? 0.f : m_run;
-        // P = exp2(x - m); l sums the fp32 values, the product uses E4M3.
-        // Byte 16 kt + r of the packed operand holds register r of tile kt.
-        i32x8 pw[KP];
-        float ls0 = 0.f, ls1 = 0.f;
-#pragma unroll
-        for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-            for (int r = 0; r < 16; r += 4) {
-                float p[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    p[e] = fast_exp2(__builtin_fmaf(s[kt][r + e], sl2, -m_sub));
-                    if constexpr (MASK) p[e] = s[kt][r + e] == masked ? 0.f : p[e];
-                }
-                ls0 += p[0] + p[2];
-                ls1 += p[1] + p[3];
-                int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
-                w = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w, true);
-                pw[kt >> 1][(kt & 1) * 4 + (r >> 2)] = w;
-            }
         l_run += ls0 + ls1;
         __builtin_amdgcn_sched_barrier(0);
         // O^T += V^T P^T: four transposing reads give the 32 key bytes of one
