@@ -250,7 +250,7 @@ def cpu_baseline(x, args, flops_per_head):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: every (batch, head) is independent and this build "
+        print("bench.py measures one GPU only: every (batch, head) is independent and the library "
               "has no multi-GPU path; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 

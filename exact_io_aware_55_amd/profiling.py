@@ -58,7 +58,8 @@ def _short(name):
 def trace(folder, out, title, command):
     rows = list(csv.DictReader(open(_one(os.path.join(folder, "**", "*kernel_stats.csv")))))
     lines = [f"# {title}", "", "Command (from the repository root on one MI355X, after "
-             "`cd /tmp && export TMPDIR=/tmp`; `$REPO` is the repository root):", "",
+             "`cd /tmp && export TMPDIR=/tmp`; `$REPO` is the repository root, `$OUT` the folder "
+             "that receives the profiler output):", "",
              "```", command, "```", "",
              "| kernel | calls | average (us) | min (us) | max (us) | share |",
              "|---|---|---|---|---|---|"]
@@ -141,19 +142,20 @@ def counters(mfma_dir, lds_dir, trace_dir, out, workload):
     xcc, cus, simds = _agent(mfma_dir)
     lines = [f"# Matrix-core and LDS counters per launch: {workload}", "",
              "Commands (from the repository root on one MI355X, after "
-             "`cd /tmp && export TMPDIR=/tmp`; `$REPO` is the repository root):", "", "```",
+             "`cd /tmp && export TMPDIR=/tmp`; `$REPO` is the repository root, `$OUT` the folder "
+             "that receives the profiler output):", "", "```",
              "rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_BUSY_CU_CYCLES "
-             "GRBM_GUI_ACTIVE --output-format csv -d $REPO/gpurun_out/pmc_mfma -o bench -- "
+             "GRBM_GUI_ACTIVE --output-format csv -d $OUT/pmc_mfma -o bench -- "
              "python3 $REPO/bench.py --steps 2 --warmup 1 --no-naive --no-cpu --no-extra",
              "rocprofv3 --pmc SQ_LDS_BANK_CONFLICT SQ_LDS_ADDR_CONFLICT SQ_LDS_IDX_ACTIVE SQ_INSTS_LDS "
-             "SQ_BUSY_CU_CYCLES --output-format csv -d $REPO/gpurun_out/pmc_lds -o bench -- "
+             "SQ_BUSY_CU_CYCLES --output-format csv -d $OUT/pmc_lds -o bench -- "
              "python3 $REPO/bench.py --steps 2 --warmup 1 --no-naive --no-cpu --no-extra",
-             "python -m exact_io_aware_55_amd.profiling counters gpurun_out/pmc_mfma gpurun_out/pmc_lds "
-             f"gpurun_out/prof profiles/<this file> {workload}",
+             "python -m exact_io_aware_55_amd.profiling counters $OUT/pmc_mfma $OUT/pmc_lds "
+             f"$OUT/prof profiles/<this file> {workload}",
              "```", "",
              f"Derived columns (the GPU reports {xcc} XCDs, {cus} CUs, {simds} SIMDs per CU):",
              "- clock = GRBM_GUI_ACTIVE / XCDs / launch duration, the duration taken from the "
-             "kernel-trace run (`gpurun_out/prof`, the command in the kernel-trace summary): counter "
+             "kernel-trace run (`$OUT/prof`, the command in the kernel-trace summary): counter "
              "collection lengthens each launch, so its own timestamps would understate the clock;",
              "- MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / XCDs x CUs x SIMDs): the share "
              "of SIMD cycles at the running clock in which the matrix core was busy;",
@@ -205,17 +207,18 @@ def main(argv):
         fs, ws, lines = traffic(*argv[1:5], argv[5], workload, comp)
         head = [f"# HBM traffic per launch: {workload}", "",
                 "Commands (from the repository root on one MI355X, after "
-                "`cd /tmp && export TMPDIR=/tmp`; `$REPO` is the repository root):", "", "```",
-                "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $REPO/gpurun_out/pmc_fetch -o bench -- "
+                "`cd /tmp && export TMPDIR=/tmp`; `$REPO` is the repository root, `$OUT` the folder "
+             "that receives the profiler output):", "", "```",
+                "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $OUT/pmc_fetch -o bench -- "
                 "python3 $REPO/bench.py --steps 2 --warmup 1 --no-naive --no-cpu --no-extra",
-                "rocprofv3 --pmc WRITE_SIZE --output-format csv -d $REPO/gpurun_out/pmc_write -o bench -- "
+                "rocprofv3 --pmc WRITE_SIZE --output-format csv -d $OUT/pmc_write -o bench -- "
                 "python3 $REPO/bench.py --steps 2 --warmup 1 --no-naive --no-cpu --no-extra",
-                "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $REPO/gpurun_out/pmc_copy_fetch -o copy -- "
+                "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $OUT/pmc_copy_fetch -o copy -- "
                 "python3 $REPO/bench.py --copy-calibration",
-                "rocprofv3 --pmc WRITE_SIZE --output-format csv -d $REPO/gpurun_out/pmc_copy_write -o copy -- "
+                "rocprofv3 --pmc WRITE_SIZE --output-format csv -d $OUT/pmc_copy_write -o copy -- "
                 "python3 $REPO/bench.py --copy-calibration",
-                "python -m exact_io_aware_55_amd.profiling traffic gpurun_out/pmc_fetch gpurun_out/pmc_write "
-                f"gpurun_out/pmc_copy_fetch gpurun_out/pmc_copy_write profiles/<this file> {workload}",
+                "python -m exact_io_aware_55_amd.profiling traffic $OUT/pmc_fetch $OUT/pmc_write "
+                f"$OUT/pmc_copy_fetch $OUT/pmc_copy_write profiles/<this file> {workload}",
                 "```", "",
                 f"Calibration: a plain 1 GiB device copy reads FETCH_SIZE and WRITE_SIZE that scale to its "
                 f"known bytes by x{fs:.4f} (fetch) and x{ws:.4f} (write); the same factors convert the "
