@@ -15,7 +15,7 @@
  * "Flash Attention", sections "Tiling" and "Speicherbedarf und
  * Laufzeitverhalten"; glossary page "Flash Attention", section "How it
  * works".)  The per-row statistic is exported as LSE = m + ln(l), which
- * carries the page's "maximum and sum per row".
+ * carries the row maximum and row sum that the pages keep.
  *
  * The backward recomputes P = exp(S - LSE) tile by tile instead of storing
  * the N x N matrix (explainer page, "Recomputation beim Rueckwaertsdurchlauf";

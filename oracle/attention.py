@@ -22,12 +22,13 @@ definition is the right reference:
 * softmax over the whole row, done in two passes (row max, then exponentials
   and their sum), the numerically stable form the pages describe,
 * O = P V, and the per-row statistics exported as one log-sum-exp
-  LSE = m + ln(l) (the pages keep "max and sum per row"; LSE carries the same
-  information, P = exp(S - LSE)).
+  LSE = m + ln(l) (the pages keep the row maximum and the row sum; LSE carries
+  the same information, P = exp(S - LSE)).
 
-The backward pass has no formula on the pages beyond "recompute the scores
-from Q, K (and V) instead of storing N x N" ("Recomputation beim
-Rueckwaertsdurchlauf"; glossary "How it works").  The oracle uses the textbook
+The pages give no backward formula; they only say that the backward pass
+recomputes the scores from Q and K rather than storing an N x N matrix
+(explainer, "Recomputation beim Rueckwaertsdurchlauf"; glossary "How it
+works").  The oracle uses the textbook
 softmax Jacobian:
 
     dV = P^T dO,  dP = dO V^T,  Delta_i = sum_j P_ij dP_ij,
