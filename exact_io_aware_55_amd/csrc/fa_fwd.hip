@@ -22,6 +22,10 @@
 //    blocks ahead: one barrier per block.
 //  * exponentials are v_exp_f32 (base 2) with scale * log2(e) folded into one
 //    FMA per score.
+//  * the running maximum is raised lazily: at d = 128 the exponentials run
+//    against it with no block maximum, and a block sum that grows too large
+//    sends the wave through a rescaling slow path; at d = 64 the block
+//    maximum comes first and only a large rise rescales.
 #include <type_traits>
 
 #include "fa_common.h"
@@ -48,9 +52,7 @@ constexpr int NW = NT / 64; // waves
 __device__ __forceinline__ int k_swz(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
 __device__ __forceinline__ int v_swz(int row) { return ((row >> 1) & 1) << 1; }
 
-// POS: scale >= 0 (row maxima of S); otherwise the maxima of scale * S are
-// the minima of S.  A template flag keeps the choice out of the loop.
-template <int D, bool CAUSAL, bool POS>
+template <int D, bool CAUSAL>
 __global__ __launch_bounds__(fwd::NT, 1) void fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     __bf16* __restrict__ O, float* __restrict__ LSE, int H, int G, int N, int window, float scale_log2,
@@ -160,14 +162,10 @@ __global__ __launch_bounds__(fwd::NT, 1) void fwd_bf16_kernel(
     f32x16 oacc[DT];
 #pragma unroll
     for (int i = 0; i < DT; ++i) oacc[i] = f32x16{};
-    // Running max of scale*log2(e)*s for this lane's query.  It is raised only
-    // when a block's maximum exceeds it by more than kLazy (log2 units), so
-    // P = exp2(x - m) stays below 2^kLazy; the output and LSE use the same m,
-    // so the result is exact whichever m was used.
-    constexpr float kLazy = 8.f;
+    // Running max of scale*log2(e)*s for this lane's query (log2 units),
+    // raised only when a block's probabilities grow too large (see below).
     float m_run = -INFINITY;
     float l_run = 0.f;         // running sum over this lane's half of the keys
-    constexpr float masked = POS ? -INFINITY : INFINITY;
 
     // per-lane LDS byte offsets of the operand reads (within a stage)
     const int k_rd0 = l32 * 64 + ((hl ^ k_swz(l32)) << 4);          // even k-chunks c
@@ -214,10 +212,14 @@ __global__ __launch_bounds__(fwd::NT, 1) void fwd_bf16_kernel(
         if constexpr (!MASK) issue_tile(t + NSTAGE - 1);
         // keep the V reads below the softmax (register pressure)
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (MASK) {
-            // keys past N and, for causal, keys after the query.  Key of
-            // register r = j0 + 4 hl + off(kt, r), off a constant: compare the
-            // constant with one per-lane limit
+        // x = scale log2(e) s - m_sub in place, the exponent of P against the
+        // running maximum as it stands; a masked key gets x = -inf, so its P
+        // is exactly 0 (also when scale == 0)
+        const float m_sub = m_run == -INFINITY ? 0.f : m_run;
+        {
+            // keys past N and, for causal, keys after the query or before its
+            // window.  Key of register r = j0 + 4 hl + off(kt, r), off a
+            // constant: compare the constant with one per-lane limit
             const int lim_n = N - j0 - 4 * hl;            // visible iff off < lim_n
             const int lim_c = my_q - j0 - 4 * hl;         // causal: off <= lim_c
             const int lim_w = lim_c - window + 1;         // window: off >= lim_w
@@ -225,28 +227,41 @@ __global__ __launch_bounds__(fwd::NT, 1) void fwd_bf16_kernel(
             for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int off = kt * 32 + (r >> 2) * 8 + (r & 3);
-                    const bool vis = off < lim_n && (!CAUSAL || (off <= lim_c && off >= lim_w));
-                    s[kt][r] = vis ? s[kt][r] : masked;
+                    const float x = __builtin_fmaf(s[kt][r], scale_log2, -m_sub);
+                    if constexpr (MASK) {
+                        const int off = kt * 32 + (r >> 2) * 8 + (r & 3);
+                        const bool vis = off < lim_n && (!CAUSAL || (off <= lim_c && off >= lim_w));
+                        s[kt][r] = vis ? x : -INFINITY;
+                    } else {
+                        s[kt][r] = x;
+                    }
                 }
         }
-        float mx = s[0][0];
-        if constexpr (POS) {
+        // P = exp2(x): the row sum accumulates the fp32 values (so LSE keeps
+        // fp32 accuracy), the PV product uses P rounded to bf16
+        u32x4 pw[2 * KT];
+        float ls0, ls1;
+        auto exps = [&]() {
+            float la[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
-            mx = halves_max(mx);
-        } else {
-#pragma unroll
-            for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fminf(mx, s[kt][r]);
-            mx = halves_min(mx);
-        }
-        const float mt = mx * scale_log2;
-        if (__builtin_amdgcn_ballot_w64(mt > m_run + kLazy) != 0) {
-            const float m_new = fmaxf(m_run, mt);
+                for (int r = 0; r < 16; r += 2) {
+                    const float p0 = fast_exp2(s[kt][r]);
+                    const float p1 = fast_exp2(s[kt][r + 1]);
+                    la[(r >> 1) & 1] += p0;
+                    la[2 + ((r >> 1) & 1)] += p1;
+                    pw[kt * 2 + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(p0, p1);
+                }
+            ls0 = la[0] + la[1];
+            ls1 = la[2] + la[3];
+        };
+        // Raise the running maximum to the block's (rows with no visible key
+        // yet keep -inf), rescale O and l, and shift x to the new maximum.
+        // O, l and LSE all use the same m, so the result is exact whichever m
+        // was used.
+        auto raise = [&](float mx) {
+            const float m_new = fmaxf(m_run, m_sub + mx);
             // a row that has seen no visible key yet (possible at a sliding
             // window's edge while other rows of the wave rescale) has l = 0
             // and O = 0: any finite alpha will do, and -inf - -inf is NaN
@@ -255,27 +270,44 @@ __global__ __launch_bounds__(fwd::NT, 1) void fwd_bf16_kernel(
             l_run *= alpha;
 #pragma unroll
             for (int i = 0; i < DT; ++i) oacc[i] *= alpha;
-        }
-        const float m_sub = m_run == -INFINITY ? 0.f : m_run;
-        // P = exp2(x - m): the row sum accumulates in fp32 (so LSE keeps
-        // fp32 accuracy); the PV product uses P rounded to bf16
-        u32x4 pw[2 * KT];
-        float ls0 = 0.f, ls1 = 0.f;
+            const float delta = m_new == -INFINITY ? 0.f : m_new - m_sub;
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt)
+            for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-                float p0 = fast_exp2(__builtin_fmaf(s[kt][r], scale_log2, -m_sub));
-                float p1 = fast_exp2(__builtin_fmaf(s[kt][r + 1], scale_log2, -m_sub));
-                // a masked score must give exactly 0, also when scale == 0
-                if constexpr (MASK) {
-                    p0 = s[kt][r] == masked ? 0.f : p0;
-                    p1 = s[kt][r + 1] == masked ? 0.f : p1;
-                }
-                ls0 += p0;
-                ls1 += p1;
-                pw[kt * 2 + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(p0, p1);
+                for (int r = 0; r < 16; ++r) s[kt][r] -= delta;
+        };
+        auto block_max = [&]() {
+            float mx = s[0][0];
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
+            return halves_max(mx);
+        };
+        if constexpr (D == 128) {
+            // Exponentials first, against the running maximum.  A lane whose
+            // block sum exceeds 2^16, or whose row has no maximum yet, sends
+            // the wave through the slow path (block maximum, rescale,
+            // exponentials again).  A lane sums BC / 2 values of its query,
+            // so its sum passes 2^16 only through an x above 8: the slow path
+            // always raises the maximum, and on the fast path P < 2^16 keeps
+            // P, l and O far from the fp32 range.
+            exps();
+            if (__builtin_expect(
+                    __builtin_amdgcn_ballot_w64(!(ls0 + ls1 <= 65536.f) || m_run == -INFINITY) != 0, 0)) {
+                raise(block_max());
+                exps();
             }
+        } else {
+            // Block maximum first; the running maximum is raised only when the
+            // block's exceeds it by more than 8 (log2 units), so P < 2^8.  At
+            // d = 64 a block has a quarter of the products, too few to hide a
+            // branch that waits for the row sum.
+            const float mx = block_max();
+            if (__builtin_expect(__builtin_amdgcn_ballot_w64(mx > 8.f || m_run == -INFINITY) != 0, 0))
+                raise(mx);
+            exps();
+        }
         l_run += ls0 + ls1;
         __builtin_amdgcn_sched_barrier(0);
         // O^T += V^T P^T; the A operand (8 keys of one feature row) comes
@@ -432,14 +464,10 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
     auto go = [&](auto kern) {
         hipLaunchKernelGGL(kern, grid, block, 0, stream, Qp, Kp, Vp, Op, lse, H, G, N, win, sl2, nqb);
     };
-    const bool pos = sl2 >= 0.f;
-    if (d == 128) {
-        if (causal) pos ? go(fwd_bf16_kernel<128, true, true>) : go(fwd_bf16_kernel<128, true, false>);
-        else pos ? go(fwd_bf16_kernel<128, false, true>) : go(fwd_bf16_kernel<128, false, false>);
-    } else {
-        if (causal) pos ? go(fwd_bf16_kernel<64, true, true>) : go(fwd_bf16_kernel<64, true, false>);
-        else pos ? go(fwd_bf16_kernel<64, false, true>) : go(fwd_bf16_kernel<64, false, false>);
-    }
+    if (d == 128)
+        causal ? go(fwd_bf16_kernel<128, true>) : go(fwd_bf16_kernel<128, false>);
+    else
+        causal ? go(fwd_bf16_kernel<64, true>) : go(fwd_bf16_kernel<64, false>);
     return hipGetLastError();
 }
 

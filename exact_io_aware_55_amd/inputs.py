@@ -20,7 +20,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-__all__ = ["make_qkv", "make_qkv_fp8", "to_f64"]
+__all__ = ["make_qkv", "make_qkv_fp8", "make_qkv_ramp", "to_f64"]
 
 
 def make_qkv(B, N, H, d, dtype=torch.bfloat16, seed=0, with_do=False, gain=1.0, H_kv=None):
@@ -53,6 +53,26 @@ def make_qkv_fp8(B, N, H, d, seed=0, gain=1.0, H_kv=None):
         out[name + "8"] = codes.view(torch.uint8).contiguous()
         out[name + "_descale"] = descale.to(torch.float32).contiguous()
     return out
+
+
+def make_qkv_ramp(B, N, H, d, span, seed=0, descending=False, dtype=torch.bfloat16):
+    """Inputs whose scores climb (or fall) steadily along the keys.
+
+    Each (batch, head) draws one direction u ~ N(0, I_d); query rows are
+    u + 0.25 n and key rows are r_j u + 0.25 n' (n, n' i.i.d. N(0, I_d)) with
+    r_j rising linearly from 0 to ``span`` over the keys (falling with
+    ``descending``); V is i.i.d. N(0, 1).  Scores q_i . k_j then grow by about
+    span |u|^2 from the first key to the last, so a running row maximum is
+    raised many times along a row.  Returns CPU tensors 'q', 'k', 'v'."""
+    g = torch.Generator().manual_seed(int(seed))
+    u = torch.randn((B, 1, H, d), generator=g, dtype=torch.float32)
+    r = torch.linspace(0.0, float(span), N, dtype=torch.float32)
+    if descending:
+        r = r.flip(0)
+    q = u + 0.25 * torch.randn((B, N, H, d), generator=g, dtype=torch.float32)
+    k = r[None, :, None, None] * u + 0.25 * torch.randn((B, N, H, d), generator=g, dtype=torch.float32)
+    v = torch.randn((B, N, H, d), generator=g, dtype=torch.float32)
+    return {n: t.to(dtype).contiguous() for n, t in (("q", q), ("k", k), ("v", v))}
 
 
 def to_f64(t):

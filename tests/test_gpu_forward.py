@@ -50,6 +50,25 @@ def test_bf16_scale_edge_cases(gpu_lib, causal):
         check_full(gpu_lib, 1, 130, 2, 128, causal, seed=8, scale=sc)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("descending", [False, True])
+def test_bf16_running_max_moves(gpu_lib, d, causal, descending):
+    """Scores that climb along the keys raise each row's running maximum many
+    times (about 100 log2 units over the row), so every block takes the
+    rescaling path; falling scores keep the first block's maximum throughout."""
+    B, N, H = 1, 1000, 2
+    span = 100.0 / (math.sqrt(d) * math.log2(math.e))
+    x = inputs.make_qkv_ramp(B, N, H, d, span, seed=31 + d, descending=descending)
+    sc = d ** -0.5
+    print(f"\n[fwd bf16] ramp d={d} causal={causal} descending={descending}", flush=True)
+    o, lse = run_bf16(gpu_lib, x, causal, scale=sc)
+    ro, rl = oracle.forward(*(inputs.to_f64(x[n]) for n in ("q", "k", "v")), sc, causal)
+    what = f"ramp d{d} causal={causal} descending={descending}"
+    assert_bf16_close(inputs.to_f64(o), ro, what)
+    assert_lse_close(inputs.to_f64(lse), rl, what)
+
+
 def test_bf16_causal_row0_is_v0(gpu_lib):
     """Causal row 0 sees only key 0: O_0 equals V_0 bit for bit."""
     x = inputs.make_qkv(2, 300, 4, 128, torch.bfloat16, seed=11)
