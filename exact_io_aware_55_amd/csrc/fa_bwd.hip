@@ -483,7 +483,8 @@ constexpr int NT = 512;
 constexpr int NW = 8;
 }  // namespace bwdq
 
-template <int D, bool CAUSAL>
+// WIN: a sliding window narrower than N (causal only)
+template <int D, bool CAUSAL, bool WIN>
 __global__ __launch_bounds__(bwdq::NT, 1) void bwd_dq_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const __bf16* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ delta,
@@ -647,21 +648,31 @@ __global__ __launch_bounds__(bwdq::NT, 1) void bwd_dq_kernel(
         // dS^T = P^T (dP^T - D), P^T = exp2(S^T scale log2e - LSE log2e); on
         // diagonal tiles keys after the lane's query get exp2(-inf) = 0
         u32x4 dsb[4];
-        const int lim_c = my_q - j0 - 4 * hl;  // key = j0 + 4hl + off: key <= q <=> off <= lim_c
-        const int lim_w = lim_c - window + 1;  // window: key > q - window <=> off >= lim_w
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[kt][r] = __builtin_fmaf(s[kt][r], scale_log2, -lq);
+        // a masked tile masks only the waves that do not see all of it
+        if constexpr (MASK) {
+            const bool whole = j0 + BC - 1 <= qw && (!WIN || j0 >= qw + 32 - window);
+            if (__builtin_expect(!whole, 1)) {
+                const int lim_c = my_q - j0 - 4 * hl;  // key = j0 + 4hl + off: key <= q <=> off <= lim_c
+                const int lim_w = lim_c - window + 1;  // window: key > q - window <=> off >= lim_w
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int off = kt * 32 + (r >> 2) * 8 + (r & 3);
+                        s[kt][r] = (off <= lim_c && (!WIN || off >= lim_w)) ? s[kt][r] : -INFINITY;
+                    }
+            }
+        }
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int r = 0; r < 16; r += 2) {
-                float x0 = __builtin_fmaf(s[kt][r], scale_log2, -lq);
-                float x1 = __builtin_fmaf(s[kt][r + 1], scale_log2, -lq);
-                if constexpr (MASK) {
-                    const int o0 = kt * 32 + (r >> 2) * 8 + (r & 3);
-                    x0 = (o0 <= lim_c && o0 >= lim_w) ? x0 : -INFINITY;
-                    x1 = (o0 + 1 <= lim_c && o0 + 1 >= lim_w) ? x1 : -INFINITY;
-                }
-                const float d0 = fast_exp2(x0) * (dp[kt][r] + dq_row);
-                const float d1 = fast_exp2(x1) * (dp[kt][r + 1] + dq_row);
+                const float d0 = fast_exp2(s[kt][r]) * (dp[kt][r] + dq_row);
+                const float d1 = fast_exp2(s[kt][r + 1]) * (dp[kt][r + 1] + dq_row);
                 dsb[kt * 2 + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(d0, d1);
             }
         // dQ^T += K^T dS^T; A operand = K^T from the row-major K block
@@ -764,15 +775,18 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void
     const int nqb = (N + bwdq::BR - 1) / bwdq::BR;
     const dim3 grid((unsigned)(B * H * nqb)), block(bwdq::NT);
     const float sl2 = scale * kLog2e;
-#define FA_BWDQ_LAUNCH(DD, CC)                                                                      \
-    hipLaunchKernelGGL((bwd_dq_kernel<DD, CC>), grid, block, 0, stream, Qp, Kp, Vp, dOp, lse2,     \
+    const bool narrow = causal && win < N;
+#define FA_BWDQ_LAUNCH(DD, CC, WW)                                                                  \
+    hipLaunchKernelGGL((bwd_dq_kernel<DD, CC, WW>), grid, block, 0, stream, Qp, Kp, Vp, dOp, lse2, \
                        delta, dQp, H, G, N, win, Npad, scale, sl2, nqb)
     if (d == 128) {
-        if (causal) FA_BWDQ_LAUNCH(128, true);
-        else FA_BWDQ_LAUNCH(128, false);
+        if (narrow) FA_BWDQ_LAUNCH(128, true, true);
+        else if (causal) FA_BWDQ_LAUNCH(128, true, false);
+        else FA_BWDQ_LAUNCH(128, false, false);
     } else {
-        if (causal) FA_BWDQ_LAUNCH(64, true);
-        else FA_BWDQ_LAUNCH(64, false);
+        if (narrow) FA_BWDQ_LAUNCH(64, true, true);
+        else if (causal) FA_BWDQ_LAUNCH(64, true, false);
+        else FA_BWDQ_LAUNCH(64, false, false);
     }
 #undef FA_BWDQ_LAUNCH
     return hipGetLastError();

@@ -52,7 +52,9 @@ constexpr int NW = NT / 64; // waves
 __device__ __forceinline__ int k_swz(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
 __device__ __forceinline__ int v_swz(int row) { return ((row >> 1) & 1) << 1; }
 
-template <int D, bool CAUSAL>
+// WIN: a sliding window narrower than N (causal only); without it the
+// causal mask is one compare per score
+template <int D, bool CAUSAL, bool WIN>
 __global__ __launch_bounds__(fwd::NT, 1) void fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     __bf16* __restrict__ O, float* __restrict__ LSE, int H, int G, int N, int window, float scale_log2,
@@ -216,26 +218,31 @@ __global__ __launch_bounds__(fwd::NT, 1) void fwd_bf16_kernel(
         // running maximum as it stands; a masked key gets x = -inf, so its P
         // is exactly 0 (also when scale == 0)
         const float m_sub = m_run == -INFINITY ? 0.f : m_run;
-        {
-            // keys past N and, for causal, keys after the query or before its
-            // window.  Key of register r = j0 + 4 hl + off(kt, r), off a
-            // constant: compare the constant with one per-lane limit
-            const int lim_n = N - j0 - 4 * hl;            // visible iff off < lim_n
-            const int lim_c = my_q - j0 - 4 * hl;         // causal: off <= lim_c
-            const int lim_w = lim_c - window + 1;         // window: off >= lim_w
 #pragma unroll
-            for (int kt = 0; kt < KT; ++kt)
+        for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float x = __builtin_fmaf(s[kt][r], scale_log2, -m_sub);
-                    if constexpr (MASK) {
+            for (int r = 0; r < 16; ++r) s[kt][r] = __builtin_fmaf(s[kt][r], scale_log2, -m_sub);
+        // A masked block masks only the waves that do not see all of it:
+        // causal, keys after the query or before its window (a query never
+        // sees a key past N, so that needs no test of its own); otherwise
+        // keys past N.  Key of register r = j0 + 4 hl + off(kt, r), off a
+        // constant: compare the constant with one per-lane limit.
+        if constexpr (MASK) {
+            const bool whole = CAUSAL ? (j0 + BC - 1 <= qw && (!WIN || j0 >= qw + 32 - window))
+                                      : j0 + BC <= N;
+            if (__builtin_expect(!whole, 1)) {
+                const int lim_n = N - j0 - 4 * hl;        // visible iff off < lim_n
+                const int lim_c = my_q - j0 - 4 * hl;     // causal: off <= lim_c
+                const int lim_w = lim_c - window + 1;     // window: off >= lim_w
+#pragma unroll
+                for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
                         const int off = kt * 32 + (r >> 2) * 8 + (r & 3);
-                        const bool vis = off < lim_n && (!CAUSAL || (off <= lim_c && off >= lim_w));
-                        s[kt][r] = vis ? x : -INFINITY;
-                    } else {
-                        s[kt][r] = x;
+                        const bool vis = CAUSAL ? off <= lim_c && (!WIN || off >= lim_w) : off < lim_n;
+                        s[kt][r] = vis ? s[kt][r] : -INFINITY;
                     }
-                }
+            }
         }
         // P = exp2(x): the row sum accumulates the fp32 values (so LSE keeps
         // fp32 accuracy), the PV product uses P rounded to bf16
@@ -464,10 +471,14 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
     auto go = [&](auto kern) {
         hipLaunchKernelGGL(kern, grid, block, 0, stream, Qp, Kp, Vp, Op, lse, H, G, N, win, sl2, nqb);
     };
-    if (d == 128)
-        causal ? go(fwd_bf16_kernel<128, true>) : go(fwd_bf16_kernel<128, false>);
-    else
-        causal ? go(fwd_bf16_kernel<64, true>) : go(fwd_bf16_kernel<64, false>);
+    const bool narrow = causal && win < N;
+    if (d == 128) {
+        if (!causal) go(fwd_bf16_kernel<128, false, false>);
+        else narrow ? go(fwd_bf16_kernel<128, true, true>) : go(fwd_bf16_kernel<128, true, false>);
+    } else {
+        if (!causal) go(fwd_bf16_kernel<64, false, false>);
+        else narrow ? go(fwd_bf16_kernel<64, true, true>) : go(fwd_bf16_kernel<64, true, false>);
+    }
     return hipGetLastError();
 }
 

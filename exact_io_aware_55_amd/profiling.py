@@ -1,6 +1,7 @@
 """Turns rocprofv3 output of ``bench.py`` runs into the text summaries kept
 under ``profiles/`` (a kernel-trace table and an HBM-traffic table plus the
-``traffic.json`` that ``bench.py`` reads for its roofline ``traffic`` field).
+``traffic.json`` that ``bench.py`` reads for its roofline ``traffic`` field),
+and the growth of those bytes with the sequence length (``scaling``).
 
 Usage, from the repository root, after the rocprofv3 runs listed in each
 summary::
@@ -8,6 +9,7 @@ summary::
     python -m exact_io_aware_55_amd.profiling trace DIR OUT.md TITLE COMMAND
     python -m exact_io_aware_55_amd.profiling traffic FETCH WRITE COPY_FETCH COPY_WRITE OUT.md WORKLOAD
     python -m exact_io_aware_55_amd.profiling counters MFMA_DIR LDS_DIR TRACE_DIR OUT.md WORKLOAD
+    python -m exact_io_aware_55_amd.profiling scaling COPY_FETCH COPY_WRITE OUT.md B H d N:FETCH:WRITE ...
 
 ``DIR`` holds a ``--kernel-trace --stats`` run (``*_kernel_stats.csv``); the
 traffic arguments are the output folders of four ``--pmc`` runs: FETCH_SIZE
@@ -194,11 +196,75 @@ def compulsory_bytes(B, H, N, d, causal):
     }
 
 
+def scaling(copy_fetch, copy_write, out, B, H, d, runs):
+    """HBM bytes per launch of each kernel of a causal fwd + bwd step at
+    several sequence lengths (``runs``: (N, fetch_dir, write_dir), N rising).
+    Bytes that grow like N (O(N d) traffic) double when N doubles; traffic
+    that grew like the N x N score matrix would quadruple."""
+    cf, cw = _counter(copy_fetch), _counter(copy_write)
+    copy = [k for k in cf if "copy" in k.lower()][0]
+    gib_kib = (1 << 30) / 1024
+    fs, ws = gib_kib / cf[copy], gib_kib / cw[copy]
+    per = {}
+    for N, fdir, wdir in runs:
+        f, w = _counter(fdir), _counter(wdir)
+        comp = compulsory_bytes(B, H, N, d, True)
+        for stage, (prefix, _) in STAGES.items():
+            names = [k for k in f if k.startswith(prefix)]
+            if names:
+                k = names[0]
+                per.setdefault(stage, {})[N] = (k, f[k] * fs * 1024 + w.get(k, 0.0) * ws * 1024, comp[stage])
+    ns = [r[0] for r in runs]
+    head = [f"# HBM bytes against sequence length: B={B} H={H} d={d} causal, forward + backward", "",
+            "Commands (from the repository root on one MI355X, after `cd /tmp && export TMPDIR=/tmp`; "
+            "`$REPO` is the repository root, `$OUT` the folder that receives the profiler output), "
+            "for each N in " + ", ".join(str(n) for n in ns) + ":", "", "```"]
+    for n in ns:
+        for c, tag in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
+            head.append(f"rocprofv3 --pmc {c} --output-format csv -d $OUT/pmc_{tag}_n{n} -o bench -- "
+                        f"python3 $REPO/bench.py --B {B} --H {H} --N {n} --d {d} --causal --steps 2 "
+                        "--warmup 1 --no-naive --no-cpu --no-extra")
+    head += ["rocprofv3 --pmc FETCH_SIZE --output-format csv -d $OUT/pmc_copy_fetch -o copy -- "
+             "python3 $REPO/bench.py --copy-calibration",
+             "rocprofv3 --pmc WRITE_SIZE --output-format csv -d $OUT/pmc_copy_write -o copy -- "
+             "python3 $REPO/bench.py --copy-calibration",
+             "python -m exact_io_aware_55_amd.profiling scaling $OUT/pmc_copy_fetch $OUT/pmc_copy_write "
+             f"profiles/<this file> {B} {H} {d} " + " ".join(f"{n}:$OUT/pmc_fetch_n{n}:$OUT/pmc_write_n{n}"
+                                                             for n in ns),
+             "```", "",
+             f"Counters scaled to bytes by a plain 1 GiB device copy (x{fs:.4f} fetch, x{ws:.4f} write). "
+             "MB = 10^6 bytes per launch; 'x compulsory' divides by the bytes the kernel must move "
+             "(inputs read once, outputs written once); 'growth' is bytes(N) / bytes(N/2).", "",
+             "| kernel | " + " | ".join(f"N={n} MB (x compulsory)" for n in ns) + " | " +
+             " | ".join(f"growth {ns[i]}/{ns[i - 1]}" for i in range(1, len(ns))) + " |",
+             "|---|" + "---|" * (2 * len(ns) - 1)]
+    lines = []
+    worst = 0.0
+    for stage, byn in per.items():
+        k = byn[ns[0]][0]
+        cells = [f"{byn[n][1] / 1e6:.1f} (x{byn[n][1] / byn[n][2]:.2f})" for n in ns]
+        growth = [byn[ns[i]][1] / byn[ns[i - 1]][1] for i in range(1, len(ns))]
+        worst = max(worst, *growth)
+        lines.append(f"| `{k}` | " + " | ".join(cells) + " | " + " | ".join(f"{g:.2f}" for g in growth) + " |")
+    tail = ["", f"Largest growth per doubling of N: {worst:.2f} (O(N d) traffic gives 2, traffic of "
+            "the N x N score matrix would give 4).  At the largest N the N x N bf16 score matrix of "
+            f"all heads would be {B * H * ns[-1] ** 2 * 2 / 2 ** 30:.0f} GiB."]
+    with open(out, "w") as fh:
+        fh.write("\n".join(head + lines + tail) + "\n")
+    return worst
+
+
 def main(argv):
     if len(argv) >= 5 and argv[0] == "trace":
         trace(argv[1], argv[2], argv[3], argv[4])
     elif len(argv) >= 6 and argv[0] == "counters":
         counters(argv[1], argv[2], argv[3], argv[4], argv[5])
+    elif len(argv) >= 8 and argv[0] == "scaling":
+        runs = []
+        for spec in argv[7:]:
+            n, fdir, wdir = spec.split(":")
+            runs.append((int(n), fdir, wdir))
+        scaling(argv[1], argv[2], argv[3], int(argv[4]), int(argv[5]), int(argv[6]), runs)
     elif len(argv) >= 7 and argv[0] == "traffic":
         workload = argv[6]
         shape = {p[0]: p[1:] for p in workload.split("_") if p[:1] in "bhnd" and p[1:].isdigit()}
