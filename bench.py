@@ -48,6 +48,9 @@ def parse():
                     help="target CPU time of the oracle sample")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the other workloads (causal, long causal, d=64 causal)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="run only the shape sweep at 16384 tokens (H=16, N 512..16384, d 64 and "
+                         "128, non-causal, forward + backward) beside the naive GPU baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device-to-device copy of 1 GiB (3 times), the "
                          "reference for scaling HBM byte counters")
@@ -213,6 +216,56 @@ def fp8_workloads(torch, binding, inputs, workloads, seed):
     return out
 
 
+# Shape sweep at a fixed 16384 tokens per batch: B = 16384 / N, H = 16,
+# non-causal, forward + backward, each N beside the naive materialised
+# attention on the same GPU.
+SWEEP_N = (512, 1024, 2048, 4096, 8192, 16384)
+SWEEP_D = (64, 128)
+
+
+def shape_sweep(torch, binding, inputs, workloads, seed):
+    rows = []
+    dev = torch.device("cuda:0")
+    for d in SWEEP_D:
+        for N in SWEEP_N:
+            B, H = 16384 // N, 16
+            scale = d ** -0.5
+            x = inputs.make_qkv(B, N, H, d, torch.bfloat16, seed=seed, with_do=True)
+            q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "do"))
+            o, lse = binding.forward(q, k, v, causal=False)
+            _, calls = binding.backward_steps(q, k, v, o, do, lse, causal=False)
+
+            def fwd():
+                binding.forward(q, k, v, causal=False, out=o, lse=lse)
+
+            def step():
+                fwd()
+                for c in calls:
+                    c()
+
+            fwd_fl = workloads.fwd_flops(B, H, N, d, False)
+            bwd_fl = workloads.bwd_flops(B, H, N, d, False)
+            f_ms = median_ms(torch, fwd)
+            s_ms = median_ms(torch, step)
+            row = {"N": N, "B": B, "H": H, "d": d,
+                   "fwd_ms": round(f_ms, 4), "fwd_tflops": round(fwd_fl / (f_ms * 1e-3) / 1e12, 1),
+                   "fwd_bwd_ms": round(s_ms, 4),
+                   "fwd_bwd_tflops": round((fwd_fl + bwd_fl) / (s_ms * 1e-3) / 1e12, 1)}
+            try:
+                n_ms = median_ms(torch, lambda: naive_step(torch, q, k, v, do, scale, False),
+                                 reps=2, samples=3)
+                row["naive_fwd_bwd_ms"] = round(n_ms, 3)
+                row["naive_fwd_bwd_tflops"] = round((fwd_fl + bwd_fl) / (n_ms * 1e-3) / 1e12, 1)
+                row["speedup_over_naive"] = round(n_ms / s_ms, 2)
+            except RuntimeError as exc:   # out of memory for the materialised matrices
+                row["naive_error"] = str(exc)[:120]
+            print(json.dumps({"sweep_row": row}), file=sys.stderr, flush=True)
+            rows.append(row)
+            del x, q, k, v, do, o, lse, calls
+            torch.cuda.empty_cache()
+    return rows
+
+
 def cpu_baseline(x, args, flops_per_head):
     """fp64 oracle (forward + backward per head) on a bounded sample of heads."""
     import numpy as np
@@ -267,6 +320,13 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     binding.load()
+    if args.sweep:
+        rows = shape_sweep(torch, binding, inputs, workloads, args.seed)
+        print(json.dumps({"metric": "attention TFLOP/s (fwd+bwd) bf16, shape sweep at 16384 tokens",
+                          "unit": "TFLOP/s", "dtype": "bf16", "data": "synthetic",
+                          "config": {"workload": "sweep_16384_tokens_h16_noncausal"},
+                          "sweep": rows}), flush=True)
+        return
     dev = torch.device("cuda:0")
     B, H, N, d, causal = args.B, args.H, args.N, args.d, args.causal
     scale = d ** -0.5

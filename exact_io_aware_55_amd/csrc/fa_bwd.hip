@@ -153,7 +153,7 @@ __global__ __launch_bounds__(bwd::NT, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     // the workgroup walks the query blocks of all of them (G = 1: one head)
     const int Hkv = H / G;
     int bhk, kb;                               // causal: key block 0 (the longest) first
-    order_blocks(blockIdx.x, gridDim.x, nkb, CAUSAL, false, bhk, kb);
+    order_blocks(blockIdx.x, gridDim.x, nkb, CAUSAL, false, bhk, kb, causal_group<D>());
     const int b = bhk / Hkv, hk = bhk - b * Hkv;
     const int row_stride = H * D;
     const unsigned row_bytes = (unsigned)row_stride * 2u;
@@ -212,7 +212,8 @@ __global__ __launch_bounds__(bwd::NT, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     __builtin_amdgcn_s_barrier();
 
     // ---- query steps: for each query head g of the group, blocks
-    // first..nsteps-1, rotated per key block ----
+    // first..nsteps-1 in order, so the key blocks of one head that run at
+    // once read the same query blocks at about the same time (L2 hits) ----
     // causal: queries k0 .. k0 + KB - 1 + window - 1 can see these keys
     // (query i sees keys j with i - window < j <= i; window >= N: plain causal)
     const int nsteps = (N + BR - 1) / BR;
@@ -220,12 +221,9 @@ __global__ __launch_bounds__(bwd::NT, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     const int last = CAUSAL ? min(nsteps - 1, (k0 + KB - 2 + window) / BR) : nsteps - 1;
     const int nst = last - first + 1;          // per query head
     const int nst_all = G * nst;
-    const int stagger = kb % nst;
     auto step_of = [&](int it, int& g) {       // query block of step it, and its head
         g = it / nst;
-        int s = it - g * nst + stagger;
-        s = s >= nst ? s - nst : s;
-        return first + s;
+        return first + (it - g * nst);
     };
 
     // direct loads of one step: SEG_QO segments of Q/dO per wave + the stats;
@@ -515,7 +513,7 @@ __global__ __launch_bounds__(bwdq::NT, 1) void bwd_dq_kernel(
     const int tg = lane >> 4, tj = lane & 15;
 
     int bh, qb;                                // causal: longest query blocks first
-    order_blocks(blockIdx.x, gridDim.x, nqb, CAUSAL, true, bh, qb);
+    order_blocks(blockIdx.x, gridDim.x, nqb, CAUSAL, true, bh, qb, causal_group<D>());
     const int b = bh / H, h = bh - b * H;
     const int row_stride = H * D;
     const long head_off = ((long)b * N * H + h) * D;

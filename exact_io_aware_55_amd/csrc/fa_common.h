@@ -94,17 +94,27 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
 // XCD's L2.  With a causal mask the work of a block depends on its index:
 // `desc` says the longest block has the highest index (query blocks) rather
 // than index 0 (key blocks).  When every XCD's share is a whole number of
-// heads, the XCD takes the longest block of each of its heads first, then the
-// next longest, and so on, so no long block starts at the end of the grid.
-// Otherwise heads are taken one at a time, each longest block first.
+// heads, the XCD takes its heads `group` at a time: the longest block of each
+// head of the group, then the next longest, and so on, so no long block
+// starts near the end of the grid.  Small groups keep the blocks running at
+// once on few heads, whose operand re-reads then stay in L2: at d = 128 pairs
+// of heads made the causal backward 4.7% faster than all heads at once and
+// cut the dK/dV kernel's L2 misses threefold at 16384 tokens.  At d = 64
+// pairs made the causal forward up to 12% slower, so there all heads go at
+// once.  Otherwise heads are taken one at a time, each longest block first.
+template <int D>
+constexpr int causal_group() { return D == 128 ? 2 : 1 << 20; }
 __device__ __forceinline__ void order_blocks(int bid, int nblocks, int nb, bool causal, bool desc, int& bh,
-                                             int& blk) {
+                                             int& blk, int group) {
     int rank;
     if (causal && nblocks % (8 * nb) == 0) {
         const int nh = nblocks / (8 * nb);     // heads per XCD
         const int x = bid & 7, i = bid >> 3;
-        rank = i / nh;
-        bh = x * nh + (i - rank * nh);
+        const int grp = nh < group ? nh : group;
+        const int gi = i / (grp * nb), j = i - gi * (grp * nb);
+        const int gsz = min(grp, nh - gi * grp);   // the last group may be smaller
+        rank = j / gsz;
+        bh = x * nh + gi * grp + (j - rank * gsz);
     } else {
         const int logical = xcd_remap(bid, nblocks);
         bh = logical / nb;

@@ -88,7 +88,7 @@ __global__ __launch_bounds__(fwd::NT, 1) void fwd_bf16_kernel(
 
     const int nblocks = gridDim.x;
     int bh, qb;                                // causal: longest query blocks first
-    order_blocks(blockIdx.x, nblocks, nqb, CAUSAL, true, bh, qb);
+    order_blocks(blockIdx.x, nblocks, nqb, CAUSAL, true, bh, qb, causal_group<D>());
     const int b = bh / H, h = bh - b * H;
     const int row_stride = H * D;              // elements between sequence rows (N*H*D < 2^31)
     const long head_off = ((long)b * N * H + h) * D;

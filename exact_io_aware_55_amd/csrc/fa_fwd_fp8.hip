@@ -101,7 +101,7 @@ __global__ __launch_bounds__(fwd8::NT, 1) void fwd_fp8_kernel(
     const int l32 = lane & 31, hl = lane >> 5;
 
     int bh, qb;                                // causal: longest query blocks first
-    order_blocks(blockIdx.x, gridDim.x, nqb, CAUSAL, true, bh, qb);
+    order_blocks(blockIdx.x, gridDim.x, nqb, CAUSAL, true, bh, qb, causal_group<D>());
     const int b = bh / H, h = bh - b * H;
     const int Hkv = H / G, hk = h / G;
     const int row_stride = H * D;              // elements between rows (Q bytes, O bf16)
