@@ -627,11 +627,14 @@ __global__ __launch_bounds__(bwdq::NT, 1) void bwd_dq_kernel(
         const lds_char* kt0 = stage + tr0;
         const lds_char* kt1 = stage + tr1;
         asm volatile("" : "+v"(ka0), "+v"(ka1), "+v"(kt0), "+v"(kt1));
+        // dP^T's accumulator starts at -D (one per lane: the lane's query),
+        // so it ends as dP^T - D
         f32x16 s[2], dp[2];
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
             s[kt] = f32x16{};
-            dp[kt] = f32x16{};
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dp[kt][r] = dq_row;
 #pragma unroll
             for (int c = 0; c < DC; ++c) {
                 const lds_char* a = ((c & 1) ? ka1 : ka0) + (c >> 1) * SUB + kt * 32 * 64;
@@ -669,8 +672,8 @@ __global__ __launch_bounds__(bwdq::NT, 1) void bwd_dq_kernel(
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int r = 0; r < 16; r += 2) {
-                const float d0 = fast_exp2(s[kt][r]) * (dp[kt][r] + dq_row);
-                const float d1 = fast_exp2(s[kt][r + 1]) * (dp[kt][r + 1] + dq_row);
+                const float d0 = fast_exp2(s[kt][r]) * dp[kt][r];
+                const float d1 = fast_exp2(s[kt][r + 1]) * dp[kt][r + 1];
                 dsb[kt * 2 + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(d0, d1);
             }
         // dQ^T += K^T dS^T; A operand = K^T from the row-major K block
