@@ -86,6 +86,33 @@ def test_bwd_causal_n4096_d64(gpu_lib):
     full_size_properties(x, grads)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("H", [24, 40])
+def test_causal_grid_orders_every_head(gpu_lib, H, d):
+    """Causal grids whose heads split evenly over the 8 XCDs take them in
+    groups (pairs at d = 128), the last group smaller when an XCD's share is
+    odd: 3 heads per XCD at H = 24, 5 at H = 40.  Every head's forward and
+    gradients against the oracle, so a head or block that the ordering
+    skipped or ran twice fails.  The gradients are held to the element-wise
+    bound of the bf16 roundings (a skipped or doubled block misses it by
+    orders of magnitude), not to the fixed tolerances of the method's
+    workloads: at this shape one dV entry of 40 heads reads 2.1e-2 max-abs
+    error, inside that bound, with relative L2 2.3e-3."""
+    B, N = 1, 1024
+    scale = d ** -0.5
+    print(f"\n[fwd+bwd causal] B{B} H{H} N{N} d{d}", flush=True)
+    x = inputs.make_qkv(B, N, H, d, torch.bfloat16, seed=500 + H + d, with_do=True)
+    q, k, v, do = (x[n].to(DEV) for n in ("q", "k", "v", "do"))
+    o, lse = gpu_lib.forward(q, k, v, causal=True)
+    grads = gpu_lib.backward(q, k, v, o, do, lse, causal=True)
+    torch.cuda.synchronize()
+    qn, kn, vn = (inputs.to_f64(x[n]) for n in ("q", "k", "v"))
+    ro, rl = oracle.forward(qn, kn, vn, scale, True)
+    assert_bf16_close(inputs.to_f64(o), ro, f"H{H} d{d} O")
+    assert np.abs(inputs.to_f64(lse) - rl).max() <= 1e-3
+    compare_heads(x, grads, scale, True, [(0, h) for h in range(H)], f"H{H} d{d}", strict=False)
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_bwd_b4_h32_n4096_d128(gpu_lib, causal):
     """The benchmark's forward+backward shape and launch configuration

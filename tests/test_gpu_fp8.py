@@ -62,6 +62,9 @@ SHAPES = [
     (1, 700, 4, 1, 64, True, 129),
     (1, 1, 2, 2, 128, False, None),
     (1, 2048, 2, 2, 128, False, None),
+    # 24 heads split evenly over the 8 XCDs (3 each): the causal grid takes
+    # them in pairs, the last group a single head
+    (1, 1024, 24, 24, 128, True, None),
 ]
 
 
