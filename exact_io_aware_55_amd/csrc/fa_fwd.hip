@@ -7,7 +7,7 @@
 // exp(m_old - m_new) whenever the maximum grows, divides by l once at the end
 // and writes only O and one statistic per row (LSE = m + ln l).
 //
-// bf16 kernel layout (per workgroup: 8 waves, 256 queries, K/V blocks of 64):
+// bf16 kernel layout (per workgroup: 8 waves, 256 queries):
 //  * each wave owns 32 queries and keeps them in registers as the B operand of
 //    S^T = K Q^T, so a lane holds the scores of ONE query against 16 keys of
 //    each 32-key MFMA tile.  The row max/sum are in-lane reductions plus one
@@ -21,7 +21,8 @@
 //    ring (2 and 3 stages) by direct global -> LDS loads issued one or two
 //    blocks ahead: one barrier per block.
 //  * exponentials are v_exp_f32 (base 2) with scale * log2(e) folded into one
-//    FMA per score.
+//    FMA per score, which turns S^T in place into the exponents
+//    x = scale log2(e) s - m (masked keys: -inf).
 //  * the running maximum is raised lazily: at d = 128 the exponentials run
 //    against it with no block maximum, and a block sum that grows too large
 //    sends the wave through a rescaling slow path; at d = 64 the block
