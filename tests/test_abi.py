@@ -60,6 +60,8 @@ def test_forward_argument_errors(lib, fn):
     for d in (0, 32, 96, 256):
         assert _fwd(lib, fn, d=d) == binding.FA_ERR_UNSUPPORTED
     assert _fwd(lib, fn, N=1 << 20, H=64, d=128) == binding.FA_ERR_UNSUPPORTED
+    # the first size past the limit: N * H * d = 2^30 exactly
+    assert _fwd(lib, fn, N=1 << 20, H=8, d=128) == binding.FA_ERR_UNSUPPORTED
     for i in range(5):
         ptrs = [FAKE] * 5
         ptrs[i] = FAKE + 8

@@ -86,6 +86,40 @@ def test_bwd_causal_n4096_d64(gpu_lib):
     full_size_properties(x, grads)
 
 
+def test_largest_supported_size(gpu_lib):
+    """The largest sizes the C ABI accepts: N * H * d just under 2^30 (here
+    B=1, H=8, d=128, N = 2^20 - 300, ragged), causal, where the kernels'
+    32-bit byte offsets within one batch reach 2^31.  Forward: sampled rows
+    of the first and last head against the oracle (each row sees up to N
+    keys).  Backward: finite gradients and the invariants sum_j dK_j = 0 and
+    sum_j dV_j = sum_i dO_i per head, which hold at any size."""
+    B, H, d = 1, 8, 128
+    N = (1 << 20) - 300
+    assert N * H * d < (1 << 30) <= (N + 300) * H * d
+    scale = d ** -0.5
+    print(f"\n[fwd+bwd causal] B{B} H{H} N{N} d{d}", flush=True)
+    x = inputs.make_qkv(B, N, H, d, torch.bfloat16, seed=77, with_do=True)
+    q, k, v, do = (x[n].to(DEV) for n in ("q", "k", "v", "do"))
+    o, lse = gpu_lib.forward(q, k, v, causal=True)
+    dq, dk, dv = gpu_lib.backward(q, k, v, o, do, lse, causal=True)
+    torch.cuda.synchronize()
+    rows = [0, 1, 255, 256, 65535, 65536, N // 2, N - 257, N - 256, N - 1]
+    for h in (0, H - 1):
+        qh, kh, vh = (inputs.to_f64(x[n][:, :, h:h + 1]) for n in ("q", "k", "v"))
+        picks = [(0, 0, i) for i in rows]
+        ro, rl = oracle.forward_rows(qh, kh, vh, scale, True, picks)
+        go = np.stack([inputs.to_f64(o[0, i, h]) for i in rows])
+        gl = np.array([float(lse[0, h, i]) for i in rows])
+        assert_bf16_close(go, ro, f"largest size head {h} sampled rows")
+        assert np.abs(gl - rl).max() <= 1e-3, f"largest size head {h} LSE"
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+    for t in (dq, dk, dv):
+        assert torch.isfinite(t.float()).all()
+    dk_sum = dk.double().sum(1)
+    assert (dk_sum.abs() <= 2e-2 * dk.double().abs().sum(1) + 1e-3).all()
+    assert torch.allclose(dv.double().sum(1), do.double().sum(1), rtol=2e-2, atol=0.5)
+
+
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("H", [24, 40])
 def test_causal_grid_orders_every_head(gpu_lib, H, d):
