@@ -2,7 +2,8 @@
 
 One step = one pass of the whole hot path over one batch: the forward
 (fa_fwd: tiled online softmax, writes O and LSE) followed by the backward by
-recomputation (fa_bwd_preprocess, fa_bwd_dkdv, fa_bwd_dq).
+recomputation as fa_bwd runs it (fa_bwd_dq_stats: dQ and the row statistics;
+then fa_bwd_dkdv).
 Default workload: B=4, H=32, N=4096, d=128, bf16, non-causal, scale 1/sqrt(d),
 seeded N(0,1) inputs resident in HBM before timing starts.
 
@@ -82,7 +83,6 @@ def source_digest(*names):
 # kernel name -> (sources that define it, how its algorithmic work is counted)
 KERNELS = {
     "fwd": ("fa_fwd.hip", "fa_common.h"),
-    "bwd_preprocess": ("fa_bwd.hip", "fa_common.h"),
     "bwd_dkdv": ("fa_bwd.hip", "fa_common.h"),
     "bwd_dq": ("fa_bwd.hip", "fa_common.h"),
 }
@@ -347,7 +347,7 @@ def main():
     fwd()
     _, bwd_calls = binding.backward_steps(q, k, v, o, do, lse, causal=causal, scale=scale,
                                           workspace=ws, out=(dq, dk, dv))
-    stages = [("fwd", fwd)] + list(zip(("bwd_preprocess", "bwd_dkdv", "bwd_dq"), bwd_calls))
+    stages = [("fwd", fwd)] + list(zip(("bwd_dq", "bwd_dkdv"), bwd_calls))
     for _ in range(args.warmup):
         for _, f in stages:
             f()
@@ -385,8 +385,6 @@ def main():
         "fwd": ("mfma", fwd_fl),
         "bwd_dkdv": ("mfma", 8.0 * N * N * d * B * H * half),
         "bwd_dq": ("mfma", 6.0 * N * N * d * B * H * half),
-        # HBM-bound helper: read O, dO (bf16) and LSE, write the two padded row statistics
-        "bwd_preprocess": ("hbm", rows * d * 2 * 2 + rows * 4 + 2 * B * H * ((N + 63) // 64 * 64) * 4),
     }
     kernels = {}
     for name, ms in per.items():

@@ -18,8 +18,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfa.so")
 
 EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_bwd_workspace_size", "fa_bwd", "fa_bwd_preprocess",
-           "fa_bwd_dkdv", "fa_bwd_dq", "fa_fwd_gqa", "fa_bwd_gqa", "fa_fwd_window", "fa_bwd_window",
-           "fa_fwd_fp8", "fa_strerror")
+           "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_dq_stats", "fa_fwd_gqa", "fa_bwd_gqa", "fa_fwd_window",
+           "fa_bwd_window", "fa_fwd_fp8", "fa_strerror")
 
 FA_OK = 0
 FA_ERR_INVALID_ARG = -1
@@ -56,6 +56,8 @@ def load(path: str = LIB_PATH):
     lib.fa_bwd_dkdv.restype = i
     lib.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, sz, vp]
     lib.fa_bwd_dq.restype = i
+    lib.fa_bwd_dq_stats.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, sz, vp]
+    lib.fa_bwd_dq_stats.restype = i
     lib.fa_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
     lib.fa_fwd_gqa.restype = i
     lib.fa_bwd_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
@@ -208,12 +210,14 @@ def backward(q, k, v, o, do, lse, causal=False, scale=None, workspace=None, out=
     return dq, dk, dv
 
 
-def backward_steps(q, k, v, o, do, lse, causal=False, scale=None, workspace=None, out=None):
-    """The same backward as :func:`backward`, issued as its three C-ABI steps.
+def backward_steps(q, k, v, o, do, lse, causal=False, scale=None, workspace=None, out=None,
+                   preprocess=False):
+    """The same backward as :func:`backward`, issued as separate C-ABI steps.
 
-    Returns ((dQ, dK, dV), calls) where ``calls`` is a list of three
-    zero-argument callables (preprocess, dK/dV, dQ) that enqueue the steps
-    again on the current stream, for timing."""
+    Returns ((dQ, dK, dV), calls) where ``calls`` is a list of zero-argument
+    callables that enqueue the steps again on the current stream, for timing:
+    (dQ with the row statistics, dK/dV), the order fa_bwd runs; with
+    ``preprocess`` the three-step order (preprocess, dK/dV, dQ)."""
     lib = load()
     B, N, H, d = _check_inputs(torch.bfloat16, q, k, v, o, do)
     need = bwd_workspace_size(B, H, N, d)
@@ -222,14 +226,22 @@ def backward_steps(q, k, v, o, do, lse, causal=False, scale=None, workspace=None
     nbytes = ws.numel() * ws.element_size()
     sc = _scale(scale, d)
     c = int(bool(causal))
-    calls = [
-        lambda: _check(lib.fa_bwd_preprocess(_ptr(o), _ptr(do), _ptr(lse), B, H, N, d, _ptr(ws), nbytes,
-                                             _stream())),
-        lambda: _check(lib.fa_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dk), _ptr(dv),
-                                       B, H, N, d, sc, c, _ptr(ws), nbytes, _stream())),
-        lambda: _check(lib.fa_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dq), B, H, N, d, sc, c,
-                                     _ptr(ws), nbytes, _stream())),
-    ]
+    dkdv = lambda: _check(lib.fa_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dk), _ptr(dv),
+                                          B, H, N, d, sc, c, _ptr(ws), nbytes, _stream()))
+    if preprocess:
+        calls = [
+            lambda: _check(lib.fa_bwd_preprocess(_ptr(o), _ptr(do), _ptr(lse), B, H, N, d, _ptr(ws),
+                                                 nbytes, _stream())),
+            dkdv,
+            lambda: _check(lib.fa_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dq), B, H, N, d, sc,
+                                         c, _ptr(ws), nbytes, _stream())),
+        ]
+    else:
+        calls = [
+            lambda: _check(lib.fa_bwd_dq_stats(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse),
+                                               _ptr(dq), B, H, N, d, sc, c, _ptr(ws), nbytes, _stream())),
+            dkdv,
+        ]
     for call in calls:
         call()
     return (dq, dk, dv), calls

@@ -176,17 +176,20 @@ int bwd_dkdv_impl(const void* q, const void* k, const void* v, const void* dout,
     return FA_OK;
 }
 
-int bwd_dq_impl(const void* q, const void* k, const void* v, const void* dout, void* dq, int B, int H,
-                int H_kv, int N, int d, float scale, int causal, int window, void* workspace,
-                size_t workspace_bytes, hipStream_t stream) {
+// o and lse null: the statistics come from the workspace (fa_bwd_preprocess);
+// otherwise the kernel forms them and writes them there
+int bwd_dq_impl(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                const float* lse, void* dq, int B, int H, int H_kv, int N, int d, float scale, int causal,
+                int window, void* workspace, size_t workspace_bytes, hipStream_t stream) {
     int rc = all_aligned({q, k, v, dout, dq});
     if (rc != FA_OK) return rc;
+    if (o && (rc = all_aligned({o, lse})) != FA_OK) return rc;
     if ((rc = check_bwd_shape(B, H, N, d, scale)) != FA_OK) return rc;
     if ((rc = check_groups(H, H_kv)) != FA_OK) return rc;
     Workspace ws;
     if ((rc = check_workspace(workspace, workspace_bytes, B, H, N, d, &ws)) != FA_OK) return rc;
-    if (fa::launch_bwd_dq(q, k, v, dout, dq, B, H, H_kv, N, d, scale, causal != 0, window, ws.lse2, ws.delta,
-                          stream) != hipSuccess)
+    if (fa::launch_bwd_dq(q, k, v, dout, dq, B, H, H_kv, N, d, scale, causal != 0, window, o, lse, ws.lse2,
+                          ws.delta, stream) != hipSuccess)
         return FA_ERR_LAUNCH;
     return FA_OK;
 }
@@ -202,8 +205,16 @@ int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, v
 int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, void* dq, int B, int H,
               int N, int d, float scale, int causal, void* workspace, size_t workspace_bytes,
               hipStream_t stream) {
-    return bwd_dq_impl(q, k, v, dout, dq, B, H, H, N, d, scale, causal, 0, workspace, workspace_bytes,
-                       stream);
+    return bwd_dq_impl(q, k, v, nullptr, dout, nullptr, dq, B, H, H, N, d, scale, causal, 0, workspace,
+                       workspace_bytes, stream);
+}
+
+int fa_bwd_dq_stats(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                    const float* lse, void* dq, int B, int H, int N, int d, float scale, int causal,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!o || !lse) return FA_ERR_INVALID_ARG;
+    return bwd_dq_impl(q, k, v, o, dout, lse, dq, B, H, H, N, d, scale, causal, 0, workspace,
+                       workspace_bytes, stream);
 }
 
 namespace {
@@ -218,13 +229,13 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const v
     if ((rc = check_groups(H, H_kv)) != FA_OK) return rc;
     Workspace ws;
     if ((rc = check_workspace(workspace, workspace_bytes, B, H, N, d, &ws)) != FA_OK) return rc;
-    if ((rc = fa_bwd_preprocess(o, dout, lse, B, H, N, d, workspace, workspace_bytes, stream)) != FA_OK)
+    // dQ first: it forms the row statistics and leaves them in the workspace
+    // for the key-block kernel
+    if ((rc = bwd_dq_impl(q, k, v, o, dout, lse, dq, B, H, H_kv, N, d, scale, causal, window, workspace,
+                          workspace_bytes, stream)) != FA_OK)
         return rc;
-    if ((rc = bwd_dkdv_impl(q, k, v, dout, dk, dv, B, H, H_kv, N, d, scale, causal, window, workspace,
-                            workspace_bytes, stream)) != FA_OK)
-        return rc;
-    return bwd_dq_impl(q, k, v, dout, dq, B, H, H_kv, N, d, scale, causal, window, workspace,
-                       workspace_bytes, stream);
+    return bwd_dkdv_impl(q, k, v, dout, dk, dv, B, H, H_kv, N, d, scale, causal, window, workspace,
+                         workspace_bytes, stream);
 }
 }  // namespace
 

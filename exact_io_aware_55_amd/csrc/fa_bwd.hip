@@ -481,11 +481,16 @@ constexpr int NT = 512;
 constexpr int NW = 8;
 }  // namespace bwdq
 
-// WIN: a sliding window narrower than N (causal only)
-template <int D, bool CAUSAL, bool WIN>
+// WIN: a sliding window narrower than N (causal only).  STATS: the kernel
+// forms the row statistics itself from O, dO and the forward's LSE (D_i =
+// dO_i . O_i, LSE_i log2 e), uses them, and writes both padded rows into
+// lse2 / delta for the key-block kernel, which then runs after it; without
+// STATS it reads them there, written by the preprocess kernel.
+template <int D, bool CAUSAL, bool WIN, bool STATS>
 __global__ __launch_bounds__(bwdq::NT, 1) void bwd_dq_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-    const __bf16* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ delta,
+    const __bf16* __restrict__ dO, const __bf16* __restrict__ O, const float* __restrict__ LSE,
+    float* __restrict__ lse2, float* __restrict__ delta,
     __bf16* __restrict__ dQ, int H, int G, int N, int window, int Npad, float scale, float scale_log2,
     int nqb) {
     using namespace bwdq;
@@ -579,8 +584,38 @@ __global__ __launch_bounds__(bwdq::NT, 1) void bwd_dq_kernel(
             oreg[c] = as_bf16x8(ld_global16(os + 16 * c));
         }
     }
-    float lq = lse2[(long)bh * Npad + q_rd];
-    float dq_row = delta[(long)bh * Npad + q_rd];  // -D of this lane's query
+    float lq, dq_row;                          // LSE log2 e and -D of this lane's query
+    if constexpr (STATS) {
+        // D = dO . O over the lane's half of the features (those of its Q and
+        // dO registers), then the other half from the partner lane
+        const __bf16* os_ = O + head_off + (long)q_rd * row_stride + 8 * hl;
+        float part = 0.f;
+#pragma unroll
+        for (int c = 0; c < DC; ++c) {
+            const u32x4 ov = ld_global16(os_ + 16 * c);
+            const u32x4 gv = __builtin_bit_cast(u32x4, oreg[c]);
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                part = __builtin_fmaf(__builtin_bit_cast(float, ov[w] << 16),
+                                      __builtin_bit_cast(float, gv[w] << 16), part);
+                part = __builtin_fmaf(__builtin_bit_cast(float, ov[w] & 0xffff0000u),
+                                      __builtin_bit_cast(float, gv[w] & 0xffff0000u), part);
+            }
+        }
+        const float dsum = halves_sum(part);
+        // rows past N (padding): LSE = +inf and D = 0, so P = 0 and dS = 0
+        const bool live = my_q < N;
+        const float lrow = LSE[(long)bh * N + q_rd];
+        lq = live ? lrow * kLog2e : INFINITY;
+        dq_row = live ? -dsum : 0.f;
+        if (hl == 0 && my_q < Npad) {
+            lse2[(long)bh * Npad + my_q] = lq;
+            delta[(long)bh * Npad + my_q] = dq_row;
+        }
+    } else {
+        lq = lse2[(long)bh * Npad + q_rd];
+        dq_row = delta[(long)bh * Npad + q_rd];
+    }
     // consume the loads here so no wait for them lands inside the loop
 #pragma unroll
     for (int c = 0; c < DC; ++c) asm volatile("" : "+v"(qreg[c]), "+v"(oreg[c]));
@@ -764,22 +799,32 @@ hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const vo
 
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dout, void* dq,
                          int B, int H, int Hkv, int N, int d, float scale, bool causal, int window,
-                         const float* lse2, const float* delta, hipStream_t stream) {
+                         const void* o, const float* lse, float* lse2, float* delta, hipStream_t stream) {
     const int G = H / Hkv;
     const int win = window > 0 ? window : kNoWindow;
     auto Qp = static_cast<const __bf16*>(q);
     auto Kp = static_cast<const __bf16*>(k);
     auto Vp = static_cast<const __bf16*>(v);
     auto dOp = static_cast<const __bf16*>(dout);
+    auto Op = static_cast<const __bf16*>(o);
     auto dQp = static_cast<__bf16*>(dq);
     const int Npad = bwd_rows_padded(N);
     const int nqb = (N + bwdq::BR - 1) / bwdq::BR;
     const dim3 grid((unsigned)(B * H * nqb)), block(bwdq::NT);
     const float sl2 = scale * kLog2e;
     const bool narrow = causal && win < N;
+    const bool stats = o != nullptr;
 #define FA_BWDQ_LAUNCH(DD, CC, WW)                                                                  \
-    hipLaunchKernelGGL((bwd_dq_kernel<DD, CC, WW>), grid, block, 0, stream, Qp, Kp, Vp, dOp, lse2, \
-                       delta, dQp, H, G, N, win, Npad, scale, sl2, nqb)
+    do {                                                                                            \
+        if (stats)                                                                                  \
+            hipLaunchKernelGGL((bwd_dq_kernel<DD, CC, WW, true>), grid, block, 0, stream, Qp, Kp,  \
+                               Vp, dOp, Op, lse, lse2, delta, dQp, H, G, N, win, Npad, scale, sl2,  \
+                               nqb);                                                                \
+        else                                                                                        \
+            hipLaunchKernelGGL((bwd_dq_kernel<DD, CC, WW, false>), grid, block, 0, stream, Qp, Kp, \
+                               Vp, dOp, Op, lse, lse2, delta, dQp, H, G, N, win, Npad, scale, sl2,  \
+                               nqb);                                                                \
+    } while (0)
     if (d == 128) {
         if (narrow) FA_BWDQ_LAUNCH(128, true, true);
         else if (causal) FA_BWDQ_LAUNCH(128, true, false);

@@ -27,7 +27,9 @@ hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float*
 
 // Backward steps: row statistics (padded D and LSE * log2 e); the
 // key-block kernel (dK, dV); the query-block kernel (dQ).  Row statistics are
-// padded per head to bwd_rows_padded(N) rows.
+// padded per head to bwd_rows_padded(N) rows.  launch_bwd_dq with o and lse
+// (not null) forms the statistics itself and writes them to lse2 / delta;
+// with o == nullptr it reads them there.
 int bwd_rows_padded(int N);
 hipError_t launch_bwd_preprocess(const void* o, const void* dout, const float* lse, int B, int H,
                                  int N, int d, float* lse2, float* delta, hipStream_t stream);
@@ -36,6 +38,6 @@ hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const vo
                            int window, const float* lse2, const float* delta, hipStream_t stream);
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dout, void* dq,
                          int B, int H, int Hkv, int N, int d, float scale, bool causal, int window,
-                         const float* lse2, const float* delta, hipStream_t stream);
+                         const void* o, const float* lse, float* lse2, float* delta, hipStream_t stream);
 
 }  // namespace fa

@@ -192,7 +192,7 @@ def compulsory_bytes(B, H, N, d, causal):
         "fwd": 4 * t + rows * 4,                # Q K V in, O and LSE out
         "bwd_preprocess": 2 * t + rows * 4 + 2 * pad,
         "bwd_dkdv": 6 * t + 2 * pad,            # Q K V dO + stats in, dK dV out
-        "bwd_dq": 5 * t + 2 * pad,              # Q K V dO + stats in, dQ out
+        "bwd_dq": 6 * t + rows * 4 + 2 * pad,   # Q K V dO O + LSE in, dQ + stats out
     }
 
 
@@ -293,8 +293,8 @@ def main(argv):
                 "measured / compulsory |", "|---|---|---|---|---|---|---|"]
         tail = ["", "Compulsory bytes: the forward reads Q, K, V and writes O and LSE; the preprocess "
                 "reads O, dO and LSE and writes both padded row statistics; dK/dV reads Q, K, V, dO and "
-                "the statistics and writes dK, dV; dQ reads Q, K, V, dO and the statistics and writes "
-                "dQ.  The N x N score matrix never reaches HBM."]
+                "the statistics and writes dK, dV; dQ reads Q, K, V, dO, O and LSE and writes dQ and "
+                "the statistics.  The N x N score matrix never reaches HBM."]
         with open(argv[5], "w") as fh:
             fh.write("\n".join(head + lines + tail) + "\n")
     else:

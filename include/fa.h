@@ -94,9 +94,10 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
            int B, int H, int N, int d, float scale, int causal,
            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* The three steps fa_bwd runs, exported separately so a caller can schedule
- * or time them individually.  They share fa_bwd's workspace; the first must
- * complete (same stream) before either of the others:
+/* Three backward steps, exported separately so a caller can schedule or
+ * time them individually (fa_bwd itself runs the two-step order below:
+ * fa_bwd_dq_stats, then fa_bwd_dkdv).  They share fa_bwd's workspace; the
+ * first must complete (same stream) before either of the others:
  *   fa_bwd_preprocess: -D_i = -sum_k dO_ik O_ik and LSE_i * log2(e) into the
  *                      workspace.  D is the softmax-Jacobian term of the
  *                      backward (not on the pages, which only require
@@ -119,6 +120,20 @@ int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
 int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, void* dq,
               int B, int H, int N, int d, float scale, int causal,
               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* dQ step that forms the row statistics itself, so no preprocess step runs
+ * (the backward by recomputation of the explainer page "Flash Attention",
+ * section "Recomputation beim Rueckwaertsdurchlauf"; D is the softmax-Jacobian
+ * term of that backward, not on the pages):
+ * per query it reads O and dO (bf16 [B,N,H,d], O as produced by fa_fwd) and
+ * the forward's lse (fp32 [B,H,N]), forms D_i = sum_k dO_ik O_ik and
+ * LSE_i * log2(e), uses them for dQ, and writes both into the workspace
+ * (same layout and padding as fa_bwd_preprocess).  fa_bwd_dkdv may run after
+ * it on the same stream.  fa_bwd runs exactly this pair: fa_bwd_dq_stats,
+ * then fa_bwd_dkdv.  Arguments, errors and limits as for fa_bwd. */
+int fa_bwd_dq_stats(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                    const float* lse, void* dq, int B, int H, int N, int d, float scale, int causal,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Grouped-query attention (explainer page "Flash Attention", section
  * "Varianten und Erweiterungen", subsection "Grouped Query Attention": several

@@ -186,6 +186,18 @@ def test_backward_step_argument_errors(lib):
     assert q(None, *ok5[1:], 1, 1, 8, 64, 0.1, 0, V(FAKE), 1 << 20, None) == binding.FA_ERR_INVALID_ARG
     assert q(*ok5, 1, 1, 8, 64, 0.1, 0, V(FAKE + 128), 1 << 20, None) == binding.FA_ERR_WORKSPACE
     assert q(*ok5, 1, 1, 8, 32, 0.1, 0, V(FAKE), 1 << 20, None) == binding.FA_ERR_UNSUPPORTED
+    # dQ with its own row statistics: q, k, v, o, dout, lse, dq
+    s = lib.fa_bwd_dq_stats
+    ok7 = [V(FAKE)] * 7
+    for i in range(7):
+        args = list(ok7)
+        args[i] = None
+        assert s(*args, 1, 1, 8, 64, 0.1, 0, V(FAKE), 1 << 20, None) == binding.FA_ERR_INVALID_ARG
+        args[i] = V(FAKE + 4)
+        assert s(*args, 1, 1, 8, 64, 0.1, 0, V(FAKE), 1 << 20, None) == binding.FA_ERR_MISALIGNED
+    assert s(*ok7, 1, 1, 8, 64, 0.1, 0, V(FAKE), 16, None) == binding.FA_ERR_WORKSPACE
+    assert s(*ok7, 1, 1, 8, 96, 0.1, 0, V(FAKE), 1 << 20, None) == binding.FA_ERR_UNSUPPORTED
+    assert s(*ok7, 1, 1, 8, 64, float("nan"), 0, V(FAKE), 1 << 20, None) == binding.FA_ERR_INVALID_ARG
 
 
 def test_missing_library_fails_loudly(tmp_path):

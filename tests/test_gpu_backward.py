@@ -86,6 +86,28 @@ def test_bwd_causal_n4096_d64(gpu_lib):
     full_size_properties(x, grads)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_three_step_backward(gpu_lib, d, causal):
+    """The three separately exported steps (fa_bwd_preprocess, fa_bwd_dkdv,
+    fa_bwd_dq reading the statistics from the workspace) against the oracle,
+    and against fa_bwd (fa_bwd_dq_stats then fa_bwd_dkdv): the two orders
+    differ only in the summation order of D."""
+    B, N, H = 2, 700, 3
+    scale = d ** -0.5
+    print(f"\n[bwd three steps] d={d} causal={causal}", flush=True)
+    x = inputs.make_qkv(B, N, H, d, torch.bfloat16, seed=61 + d, with_do=True)
+    q, k, v, do = (x[n].to(DEV) for n in ("q", "k", "v", "do"))
+    o, lse = gpu_lib.forward(q, k, v, causal=causal)
+    steps, _ = gpu_lib.backward_steps(q, k, v, o, do, lse, causal=causal, preprocess=True)
+    fused = gpu_lib.backward(q, k, v, o, do, lse, causal=causal)
+    torch.cuda.synchronize()
+    compare_heads(x, steps, scale, causal, [(b, h) for b in range(B) for h in range(H)],
+                  f"three steps d{d} causal={causal}")
+    for a, f in zip(steps, fused):
+        assert (a.float() - f.float()).abs().max().item() <= 2e-2
+
+
 def test_largest_supported_size(gpu_lib):
     """The largest sizes the C ABI accepts: N * H * d just under 2^30 (here
     B=1, H=8, d=128, N = 2^20 - 300, ragged), causal, where the kernels'
