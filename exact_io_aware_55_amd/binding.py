@@ -91,13 +91,51 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _on_device(t):
+    return t.is_cuda
+
+
+def _need(t, name, dtype, shape, device):
+    """A caller-supplied tensor the kernels read or write: it must be a
+    contiguous tensor of ``dtype`` and ``shape`` on ``device``.  The C ABI
+    sees only a raw pointer, so a host tensor or a short buffer would reach
+    the kernels unchecked."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a tensor")
+    if not _on_device(t) or t.device != device:
+        raise ValueError(f"{name} must be on {device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: expected {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _need_bytes(t, name, nbytes, device):
+    """A workspace: a contiguous device tensor of at least ``nbytes`` bytes."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a tensor")
+    if not _on_device(t) or t.device != device:
+        raise ValueError(f"{name} must be on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise ValueError(f"{name} holds {have} bytes, {nbytes} needed")
+    return t
+
+
 def _check_inputs(dtype, *ts):
     shape = ts[0].shape
     if len(shape) != 4:
         raise ValueError("tensors must be [B, N, H, d]")
     for t in ts:
-        if not t.is_cuda:
+        if not _on_device(t):
             raise ValueError("tensors must be on the GPU")
+        if t.device != ts[0].device:
+            raise ValueError("tensors must be on one device")
         if t.dtype != dtype:
             raise ValueError(f"expected {dtype}, got {t.dtype}")
         if t.shape != shape:
@@ -112,9 +150,33 @@ def _check_gqa(dtype, q_like, kv_like):
     multiple of H_kv.  Returns (B, N, H, H_kv, d)."""
     B, N, H, d = _check_inputs(dtype, *q_like)
     Bk, Nk, Hkv, dk = _check_inputs(dtype, *kv_like)
+    if kv_like[0].device != q_like[0].device:
+        raise ValueError("tensors must be on one device")
     if (Bk, Nk, dk) != (B, N, d) or Hkv < 1 or H % Hkv != 0:
         raise ValueError("k and v must be [B, N, H_kv, d] with H a multiple of H_kv")
     return B, N, H, Hkv, d
+
+
+def _outputs(out, like, names):
+    """Caller-supplied output tensors (or None: allocate like ``like``)."""
+    if out is None:
+        return tuple(torch.empty_like(t) for t in like)
+    if len(out) != len(like):
+        raise ValueError(f"out must hold {len(like)} tensors")
+    return tuple(_need(o, n, t.dtype, t.shape, t.device) for o, t, n in zip(out, like, names))
+
+
+def _lse_out(lse, B, H, N, device):
+    if lse is None:
+        return torch.empty((B, H, N), device=device, dtype=torch.float32)
+    return _need(lse, "lse", torch.float32, (B, H, N), device)
+
+
+def _workspace(workspace, B, H, N, d, device):
+    need = bwd_workspace_size(B, H, N, d)
+    if workspace is None:
+        return torch.empty(need, device=device, dtype=torch.uint8)
+    return _need_bytes(workspace, "workspace", need, device)
 
 
 def _scale(scale, d):
@@ -130,8 +192,8 @@ def forward(q, k, v, causal=False, scale=None, out=None, lse=None, window=None):
     fa_fwd_window and implies causal."""
     lib = load()
     B, N, H, Hkv, d = _check_gqa(torch.bfloat16, (q,), (k, v))
-    o = torch.empty_like(q) if out is None else out
-    lse_t = torch.empty((B, H, N), device=q.device, dtype=torch.float32) if lse is None else lse
+    (o,) = _outputs(None if out is None else (out,), (q,), ("out",))
+    lse_t = _lse_out(lse, B, H, N, q.device)
     if window is not None:
         _check(lib.fa_fwd_window(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), B, H, Hkv, N, d,
                                  _scale(scale, d), int(window), _stream()))
@@ -152,14 +214,16 @@ def forward_fp8(q8, k8, v8, q_descale, k_descale, v_descale, causal=False, scale
     1/sqrt(d)).  Returns (O [B,N,H,d] bf16, LSE [B,H,N] fp32)."""
     lib = load()
     B, N, H, Hkv, d = _check_gqa(torch.uint8, (q8,), (k8, v8))
-    for t, heads in ((q_descale, H), (k_descale, Hkv), (v_descale, Hkv)):
-        if (not t.is_cuda or t.dtype != torch.float32 or tuple(t.shape) != (B, heads)
-                or not t.is_contiguous()):
-            raise ValueError("descales must be contiguous fp32 GPU tensors [B, H] (q) and [B, H_kv] (k, v)")
+    for t, name, heads in ((q_descale, "q_descale", H), (k_descale, "k_descale", Hkv),
+                           (v_descale, "v_descale", Hkv)):
+        _need(t, name, torch.float32, (B, heads), q8.device)
     if window is not None:
         causal = True
-    o = torch.empty((B, N, H, d), device=q8.device, dtype=torch.bfloat16) if out is None else out
-    lse_t = torch.empty((B, H, N), device=q8.device, dtype=torch.float32) if lse is None else lse
+    if out is None:
+        o = torch.empty((B, N, H, d), device=q8.device, dtype=torch.bfloat16)
+    else:
+        o = _need(out, "out", torch.bfloat16, (B, N, H, d), q8.device)
+    lse_t = _lse_out(lse, B, H, N, q8.device)
     _check(lib.fa_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(q_descale), _ptr(k_descale), _ptr(v_descale),
                           _ptr(o), _ptr(lse_t), B, H, Hkv, N, d, _scale(scale, d), int(bool(causal)),
                           0 if window is None else int(window), _stream()))
@@ -170,8 +234,8 @@ def forward_f32(q, k, v, causal=False, scale=None, out=None, lse=None):
     """fp32 forward.  Returns (O [B,N,H,d] fp32, LSE [B,H,N] fp32)."""
     lib = load()
     B, N, H, d = _check_inputs(torch.float32, q, k, v)
-    o = torch.empty_like(q) if out is None else out
-    lse_t = torch.empty((B, H, N), device=q.device, dtype=torch.float32) if lse is None else lse
+    (o,) = _outputs(None if out is None else (out,), (q,), ("out",))
+    lse_t = _lse_out(lse, B, H, N, q.device)
     _check(lib.fa_fwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), B, H, N, d,
                           _scale(scale, d), int(bool(causal)), _stream()))
     return o, lse_t
@@ -187,14 +251,9 @@ def backward(q, k, v, o, do, lse, causal=False, scale=None, workspace=None, out=
     fa_bwd_gqa, else fa_bwd; ``window`` as in :func:`forward`: fa_bwd_window)."""
     lib = load()
     B, N, H, Hkv, d = _check_gqa(torch.bfloat16, (q, o, do), (k, v))
-    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
-        raise ValueError("lse must be contiguous fp32 [B, H, N]")
-    need = bwd_workspace_size(B, H, N, d)
-    ws = torch.empty(need, device=q.device, dtype=torch.uint8) if workspace is None else workspace
-    if out is None:
-        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    else:
-        dq, dk, dv = out
+    _need(lse, "lse", torch.float32, (B, H, N), q.device)
+    ws = _workspace(workspace, B, H, N, d, q.device)
+    dq, dk, dv = _outputs(out, (q, k, v), ("dq", "dk", "dv"))
     if window is not None:
         _check(lib.fa_bwd_window(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
                                  _ptr(dk), _ptr(dv), B, H, Hkv, N, d, _scale(scale, d), int(window),
@@ -220,9 +279,9 @@ def backward_steps(q, k, v, o, do, lse, causal=False, scale=None, workspace=None
     ``preprocess`` the three-step order (preprocess, dK/dV, dQ)."""
     lib = load()
     B, N, H, d = _check_inputs(torch.bfloat16, q, k, v, o, do)
-    need = bwd_workspace_size(B, H, N, d)
-    ws = torch.empty(need, device=q.device, dtype=torch.uint8) if workspace is None else workspace
-    dq, dk, dv = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)) if out is None else out
+    _need(lse, "lse", torch.float32, (B, H, N), q.device)
+    ws = _workspace(workspace, B, H, N, d, q.device)
+    dq, dk, dv = _outputs(out, (q, k, v), ("dq", "dk", "dv"))
     nbytes = ws.numel() * ws.element_size()
     sc = _scale(scale, d)
     c = int(bool(causal))

@@ -768,7 +768,7 @@ hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const vo
                            void* dv, int B, int H, int Hkv, int N, int d, float scale, bool causal,
                            int window, const float* lse2, const float* delta, hipStream_t stream) {
     const int G = H / Hkv;
-    const int win = window > 0 ? window : kNoWindow;
+    const int win = effective_window(window, N);
     auto Qp = static_cast<const __bf16*>(q);
     auto Kp = static_cast<const __bf16*>(k);
     auto Vp = static_cast<const __bf16*>(v);
@@ -801,7 +801,7 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void
                          int B, int H, int Hkv, int N, int d, float scale, bool causal, int window,
                          const void* o, const float* lse, float* lse2, float* delta, hipStream_t stream) {
     const int G = H / Hkv;
-    const int win = window > 0 ? window : kNoWindow;
+    const int win = effective_window(window, N);
     auto Qp = static_cast<const __bf16*>(q);
     auto Kp = static_cast<const __bf16*>(k);
     auto Vp = static_cast<const __bf16*>(v);

@@ -468,7 +468,7 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
     auto Kp = static_cast<const __bf16*>(k);
     auto Vp = static_cast<const __bf16*>(v);
     auto Op = static_cast<__bf16*>(o);
-    const int win = window > 0 ? window : kNoWindow;
+    const int win = effective_window(window, N);
     auto go = [&](auto kern) {
         hipLaunchKernelGGL(kern, grid, block, 0, stream, Qp, Kp, Vp, Op, lse, H, G, N, win, sl2, nqb);
     };

@@ -349,7 +349,7 @@ hipError_t launch_fwd_fp8(const void* q, const void* k, const void* v, const flo
     auto Kp = static_cast<const uint8_t*>(k);
     auto Vp = static_cast<const uint8_t*>(v);
     auto Op = static_cast<__bf16*>(o);
-    const int win = window > 0 ? window : kNoWindow;
+    const int win = effective_window(window, N);
     auto go = [&](auto kern) {
         hipLaunchKernelGGL(kern, grid, block, 0, stream, Qp, Kp, Vp, q_descale, k_descale, v_descale, Op,
                            lse, H, G, N, win, sl2, nqb);

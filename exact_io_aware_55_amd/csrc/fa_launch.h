@@ -11,6 +11,11 @@ namespace fa {
 // head h uses K/V head h / (H / Hkv).  window (causal only): query i sees keys
 // j with i - window < j <= i; window <= 0 means no window.
 constexpr int kNoWindow = 1 << 30;
+// The window the kernels see.  A window of N or more hides no key, so it is
+// plain causal attention; it becomes kNoWindow, which keeps the kernels'
+// 32-bit window arithmetic (row + window, row - window) far from overflow
+// for any caller value up to INT_MAX.
+inline int effective_window(int window, int N) { return window > 0 && window < N ? window : kNoWindow; }
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                            int H, int Hkv, int N, int d, float scale, bool causal, int window,
                            hipStream_t stream);

@@ -6,10 +6,8 @@ recomputation of Q K^T that the pages note makes the total flop count slightly
 higher; "Speicherbedarf und Laufzeitverhalten" on the explainer page), and a
 causal mask halves both.
 
-The compulsory HBM bytes are the tensors that must cross HBM at least once:
-forward reads Q, K, V and writes O and LSE; backward reads Q, K, V, O, dO, LSE
-and writes dQ, dK, dV, plus its own small row-statistic buffer and the fp32
-dQ accumulator.
+The bytes each kernel must move (the tensors that cross HBM at least once)
+are counted per kernel in ``profiling.compulsory_bytes``.
 """
 
 from __future__ import annotations
@@ -50,22 +48,6 @@ def fwd_flops(B, H, N, d, causal, window=None):
 
 def bwd_flops(B, H, N, d, causal, window=None):
     return 2.5 * fwd_flops(B, H, N, d, causal, window)
-
-
-def fwd_bytes(B, H, N, d, elem=2):
-    """Compulsory HBM bytes of one forward: read Q,K,V, write O, LSE (fp32)."""
-    return B * H * (4 * N * d * elem + 4 * N)
-
-
-def bwd_bytes(B, H, N, d, elem=2):
-    """Compulsory HBM bytes of one backward including the fp32 dQ accumulator.
-
-    Reads Q, K, V, O, dO (5 N d elem) and LSE, writes dQ, dK, dV (3 N d elem),
-    writes then reads the row statistic D (2 x 4N) and the fp32 dQ
-    accumulator (zero-fill, read-modify-write traffic counted once each way:
-    2 x 4 N d), and the final dQ conversion read (4 N d).
-    """
-    return B * H * (8 * N * d * elem + 4 * N + 8 * N + 12 * N * d)
 
 
 @dataclass(frozen=True)

@@ -1,0 +1,193 @@
+"""CPU checks of the Python binding's argument validation.
+
+The C ABI receives raw pointers only, so it cannot tell a host tensor or a
+short buffer from a good one.  The binding must therefore reject every
+caller-supplied tensor that is on the wrong device or has the wrong dtype,
+shape, contiguity or size, before any call into the library.  Here host
+tensors stand in for device tensors (the device test is patched), and the
+library is replaced by a stub that fails the test if any entry point other
+than the pure host-side workspace-size query is reached."""
+
+import pytest
+import torch
+
+from exact_io_aware_55_amd import binding
+
+B, N, H, HKV, D = 2, 40, 4, 2, 64
+
+
+class NoLaunch:
+    """Stands in for libfa.so: answers the workspace-size query (a host-only
+    function of the real library) and fails on anything else."""
+
+    def __init__(self, real):
+        self._real = real
+
+    def fa_bwd_workspace_size(self, *a):
+        return self._real.fa_bwd_workspace_size(*a)
+
+    def fa_strerror(self, code):
+        return self._real.fa_strerror(code)
+
+    def __getattr__(self, name):
+        raise AssertionError(f"{name} was called although an argument was invalid")
+
+
+@pytest.fixture
+def lib(monkeypatch):
+    real = binding.load()
+    monkeypatch.setattr(binding, "_lib", NoLaunch(real))
+    monkeypatch.setattr(binding, "_on_device", lambda t: True)
+    yield binding
+
+
+def bf(*shape):
+    return torch.zeros(shape, dtype=torch.bfloat16)
+
+
+def qkv(hkv=H):
+    return bf(B, N, H, D), bf(B, N, hkv, D), bf(B, N, hkv, D)
+
+
+def host_only(t):
+    """A tensor that fails the (patched) device test."""
+    t._not_on_device = True
+    return t
+
+
+@pytest.fixture
+def device_test(monkeypatch):
+    monkeypatch.setattr(binding, "_on_device", lambda t: not getattr(t, "_not_on_device", False))
+
+
+BAD_LSE = {
+    "dtype": lambda: torch.zeros(B, H, N, dtype=torch.float64),
+    "shape": lambda: torch.zeros(B, H, N + 1),
+    "layout": lambda: torch.zeros(B, N, H).transpose(1, 2),
+}
+BAD_OUT = {
+    "dtype": lambda s: torch.zeros(s, dtype=torch.float32),
+    "shape": lambda s: torch.zeros((s[0], s[1] - 1, *s[2:]), dtype=torch.bfloat16),
+    "layout": lambda s: torch.zeros((s[0], s[2], s[1], s[3]), dtype=torch.bfloat16).transpose(1, 2),
+}
+
+
+@pytest.mark.parametrize("bad", sorted(BAD_OUT))
+def test_forward_rejects_bad_out(lib, bad):
+    q, k, v = qkv()
+    with pytest.raises(ValueError):
+        lib.forward(q, k, v, out=BAD_OUT[bad](q.shape))
+
+
+@pytest.mark.parametrize("bad", sorted(BAD_LSE))
+@pytest.mark.parametrize("entry", ["forward", "forward_gqa", "forward_window", "forward_f32"])
+def test_forward_rejects_bad_lse(lib, bad, entry):
+    if entry == "forward_f32":
+        q, k, v = (t.float() for t in qkv())
+        call = lambda **kw: lib.forward_f32(q, k, v, **kw)
+    else:
+        q, k, v = qkv(HKV if entry == "forward_gqa" else H)
+        extra = {"window": 8} if entry == "forward_window" else {}
+        call = lambda **kw: lib.forward(q, k, v, **extra, **kw)
+    with pytest.raises(ValueError):
+        call(lse=BAD_LSE[bad]())
+
+
+def bwd_args(hkv=H):
+    q, k, v = qkv(hkv)
+    return q, k, v, bf(B, N, H, D), bf(B, N, H, D), torch.zeros(B, H, N)
+
+
+@pytest.mark.parametrize("bad", sorted(BAD_LSE))
+@pytest.mark.parametrize("entry", ["backward", "backward_steps"])
+def test_backward_rejects_bad_lse(lib, bad, entry):
+    q, k, v, o, do, _ = bwd_args()
+    with pytest.raises(ValueError):
+        getattr(lib, entry)(q, k, v, o, do, BAD_LSE[bad]())
+
+
+@pytest.mark.parametrize("which", [0, 1, 2])
+@pytest.mark.parametrize("bad", sorted(BAD_OUT))
+@pytest.mark.parametrize("hkv", [H, HKV])
+def test_backward_rejects_bad_gradient_outputs(lib, which, bad, hkv):
+    q, k, v, o, do, lse = bwd_args(hkv)
+    out = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)]
+    out[which] = BAD_OUT[bad](out[which].shape)
+    with pytest.raises(ValueError):
+        lib.backward(q, k, v, o, do, lse, out=tuple(out))
+    if hkv == H:
+        with pytest.raises(ValueError):
+            lib.backward_steps(q, k, v, o, do, lse, out=tuple(out))
+
+
+def test_backward_rejects_wrong_number_of_outputs(lib):
+    q, k, v, o, do, lse = bwd_args()
+    with pytest.raises(ValueError):
+        lib.backward(q, k, v, o, do, lse, out=(torch.empty_like(q), torch.empty_like(k)))
+
+
+@pytest.mark.parametrize("entry", ["backward", "backward_steps"])
+def test_backward_rejects_short_or_strided_workspace(lib, entry):
+    q, k, v, o, do, lse = bwd_args()
+    need = lib.bwd_workspace_size(B, H, N, D)
+    assert need > 0
+    with pytest.raises(ValueError):
+        getattr(lib, entry)(q, k, v, o, do, lse, workspace=torch.zeros(need - 1, dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        getattr(lib, entry)(q, k, v, o, do, lse, workspace=torch.zeros(2 * need, dtype=torch.uint8)[::2])
+    with pytest.raises(ValueError):
+        getattr(lib, entry)(q, k, v, o, do, lse, workspace=[0] * need)
+
+
+def test_host_tensors_are_rejected(lib, device_test):
+    """With the real device test in place, each host tensor is refused."""
+    q, k, v, o, do, lse = bwd_args()
+    need = lib.bwd_workspace_size(B, H, N, D)
+    with pytest.raises(ValueError):
+        lib.backward(q, k, v, o, do, host_only(torch.zeros(B, H, N)))
+    with pytest.raises(ValueError):
+        lib.backward(q, k, v, o, do, lse, workspace=host_only(torch.zeros(need, dtype=torch.uint8)))
+    with pytest.raises(ValueError):
+        lib.backward(q, k, v, o, do, lse,
+                     out=(torch.empty_like(q), host_only(torch.empty_like(k)), torch.empty_like(v)))
+    with pytest.raises(ValueError):
+        lib.forward(q, k, v, out=host_only(torch.empty_like(q)))
+    with pytest.raises(ValueError):
+        lib.forward(q, k, v, lse=host_only(torch.zeros(B, H, N)))
+    with pytest.raises(ValueError):
+        lib.forward(host_only(bf(B, N, H, D)), k, v)
+
+
+def fp8_args():
+    q8 = torch.zeros(B, N, H, D, dtype=torch.uint8)
+    k8 = torch.zeros(B, N, HKV, D, dtype=torch.uint8)
+    v8 = torch.zeros(B, N, HKV, D, dtype=torch.uint8)
+    return q8, k8, v8, torch.ones(B, H), torch.ones(B, HKV), torch.ones(B, HKV)
+
+
+@pytest.mark.parametrize("what", ["q_descale", "k_descale", "v_descale", "out", "lse"])
+def test_fp8_rejects_bad_tensors(lib, what):
+    q8, k8, v8, qd, kd, vd = fp8_args()
+    kw = {}
+    if what == "q_descale":
+        qd = torch.ones(B, HKV)
+    elif what == "k_descale":
+        kd = torch.ones(B, HKV, dtype=torch.float64)
+    elif what == "v_descale":
+        vd = torch.ones(HKV, B).t()
+    elif what == "out":
+        kw["out"] = torch.zeros(B, N, H, D, dtype=torch.float32)
+    else:
+        kw["lse"] = torch.zeros(B, H, N - 1)
+    with pytest.raises(ValueError):
+        lib.forward_fp8(q8, k8, v8, qd, kd, vd, **kw)
+
+
+def test_valid_arguments_reach_the_library(lib):
+    """The stub refuses launches: a fully valid call gets past validation and
+    fails only there, so the checks above are not rejecting everything."""
+    q, k, v, o, do, lse = bwd_args()
+    with pytest.raises(AssertionError, match="fa_bwd"):
+        lib.backward(q, k, v, o, do, lse)
+    with pytest.raises(AssertionError, match="fa_fwd"):
+        lib.forward(q, k, v)

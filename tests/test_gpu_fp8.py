@@ -92,6 +92,16 @@ def test_fp8_forward_deterministic(gpu_lib):
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+@pytest.mark.parametrize("w", [300, 2 ** 31 - 1])
+def test_fp8_window_at_least_n_is_causal_bitwise(gpu_lib, w):
+    """A window of N or more (here N and INT_MAX) hides no key: the result is
+    plain causal attention bit for bit."""
+    x = inputs.make_qkv_fp8(1, 300, 4, 128, seed=38, H_kv=2)
+    o1, l1 = run(gpu_lib, x, True, window=w)
+    o2, l2 = run(gpu_lib, x, True)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
 def test_fp8_bad_descale_gives_nan_rows_of_that_head_only(gpu_lib):
     x = inputs.make_qkv_fp8(1, 200, 4, 64, seed=33, H_kv=2)
     x["k_descale"][0, 1] = 0.0                     # K/V head 1 serves query heads 2 and 3
