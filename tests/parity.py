@@ -318,9 +318,14 @@ def check_parity(x, scale, causal, o=None, lse=None, grads=None, window=None, gr
             s_["loosened_elems"] += r["loosened_elems"]
             s_["loosened_l2"] += int(r["loosened_l2"])
             s_["tensors"] += 1
-    print(f"[parity] {what}: " + "; ".join(
+    line = f"[parity] {what}: " + "; ".join(
         f"{n} max_abs {v['max_abs']:.2e} rel_l2 {v['rel_l2']:.2e} loosened {v['loosened_elems']} elems, "
-        f"{v['loosened_l2']}/{v['tensors']} L2" for n, v in summary.items()), flush=True)
+        f"{v['loosened_l2']}/{v['tensors']} L2" for n, v in summary.items())
+    print(line, flush=True)
+    log = os.environ.get("FA_PARITY_LOG")
+    if log:                              # a record of the observed errors per check
+        with open(log, "a") as fh:
+            fh.write(line + "\n")
     return summary
 
 
