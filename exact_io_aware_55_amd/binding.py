@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libfa.so")
 
 EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_bwd_workspace_size", "fa_bwd", "fa_bwd_preprocess",
            "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_dq_stats", "fa_fwd_gqa", "fa_bwd_gqa", "fa_fwd_window",
-           "fa_bwd_window", "fa_fwd_fp8", "fa_strerror")
+           "fa_bwd_window", "fa_fwd_fp8", "fa_bwd_noalloc", "fa_bwd_noalloc_max_workspace", "fa_strerror")
 
 FA_OK = 0
 FA_ERR_INVALID_ARG = -1
@@ -27,6 +27,7 @@ FA_ERR_UNSUPPORTED = -2
 FA_ERR_MISALIGNED = -3
 FA_ERR_WORKSPACE = -4
 FA_ERR_LAUNCH = -5
+FA_ERR_SCRATCH = -6
 
 _lib = None
 
@@ -68,6 +69,10 @@ def load(path: str = LIB_PATH):
     lib.fa_bwd_window.restype = i
     lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp]
     lib.fa_fwd_fp8.restype = i
+    lib.fa_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
+    lib.fa_bwd_noalloc.restype = i
+    lib.fa_bwd_noalloc_max_workspace.argtypes = []
+    lib.fa_bwd_noalloc_max_workspace.restype = sz
     lib.fa_strerror.argtypes = [i]
     lib.fa_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -266,6 +271,20 @@ def backward(q, k, v, o, do, lse, causal=False, scale=None, workspace=None, out=
         _check(lib.fa_bwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
                               _ptr(dk), _ptr(dv), B, H, Hkv, N, d, _scale(scale, d), int(bool(causal)),
                               _ptr(ws), ws.numel() * ws.element_size(), _stream()))
+    return dq, dk, dv
+
+
+def backward_noalloc(q, k, v, o, do, lse, causal=False, scale=None, out=None):
+    """The backward of :func:`backward` through fa_bwd_noalloc, whose
+    workspace is the library's static scratch array (no device allocation
+    inside the library; the outputs are allocated here unless ``out`` gives
+    them).  Multi-head attention only."""
+    lib = load()
+    B, N, H, d = _check_inputs(torch.bfloat16, q, k, v, o, do)
+    _need(lse, "lse", torch.float32, (B, H, N), q.device)
+    dq, dk, dv = _outputs(out, (q, k, v), ("dq", "dk", "dv"))
+    _check(lib.fa_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk),
+                              _ptr(dv), B, H, N, d, _scale(scale, d), int(bool(causal)), _stream()))
     return dq, dk, dv
 
 

@@ -7,7 +7,9 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <initializer_list>
+#include <mutex>
 
 #include "../../include/fa.h"
 #include "fa_launch.h"
@@ -261,6 +263,69 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
                       workspace_bytes, stream);
 }
 
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Allocation-free backward: the workspace is a static device array.
+//
+// Each GPU that runs this library holds its own copy of `scratch` from the
+// moment the code object is loaded until the process ends.  In host code the
+// array's name is only a host-side stand-in, so its device address is looked
+// up once per device (hipGetSymbolAddress, with that device current) and only
+// that address is handed to kernels.  Every call on one GPU shares the array:
+// calls that overlap on one GPU (different streams, or threads) race.
+// Nothing in it needs clearing: the first backward step writes every row
+// statistic (padding included) before the second reads them.
+// ---------------------------------------------------------------------------
+namespace {
+constexpr size_t kScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on device `dev` (which must be current).
+int scratch_address(int dev, void** out) {
+    if (dev < 0 || dev >= kMaxDevices) return FA_ERR_UNSUPPORTED;
+    void* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return FA_ERR_LAUNCH;
+            g_scratch[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return FA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+size_t fa_bwd_noalloc_max_workspace(void) { return kScratchBytes; }
+
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                   const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
+                   int causal, hipStream_t stream) {
+    // the same checks as fa_bwd, before any HIP call
+    int rc = all_aligned({q, k, v, o, dout, lse, dq, dk, dv});
+    if (rc != FA_OK) return rc;
+    if ((rc = check_bwd_shape(B, H, N, d, scale)) != FA_OK) return rc;
+    if (fa_bwd_workspace_size(B, H, N, d) > kScratchBytes) return FA_ERR_SCRATCH;
+    // the stream's device must be the current one: the scratch address is
+    // looked up for the current device
+    int cur = 0, sdev = 0;
+    if (hipGetDevice(&cur) != hipSuccess || hipStreamGetDevice(stream, &sdev) != hipSuccess)
+        return FA_ERR_LAUNCH;
+    if (sdev != cur) return FA_ERR_INVALID_ARG;
+    void* ws = nullptr;
+    if ((rc = scratch_address(cur, &ws)) != FA_OK) return rc;
+    return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, B, H, H, N, d, scale, causal, 0, ws, kScratchBytes,
+                    stream);
+}
+
 const char* fa_strerror(int code) {
     switch (code) {
         case FA_OK: return "success";
@@ -269,6 +334,7 @@ const char* fa_strerror(int code) {
         case FA_ERR_MISALIGNED: return "pointer not 16-byte aligned";
         case FA_ERR_WORKSPACE: return "workspace null, not 256-byte aligned or smaller than fa_bwd_workspace_size()";
         case FA_ERR_LAUNCH: return "kernel launch failed";
+        case FA_ERR_SCRATCH: return "shape needs more workspace than fa_bwd_noalloc's static scratch holds";
         default: return "unknown error code";
     }
 }

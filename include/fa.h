@@ -65,7 +65,9 @@ enum {
     FA_ERR_UNSUPPORTED = -2, /* d not in {64, 128}, or N*H*d >= 2^30     */
     FA_ERR_MISALIGNED = -3,  /* a pointer not 16-byte aligned             */
     FA_ERR_WORKSPACE = -4,   /* workspace null, misaligned or too small   */
-    FA_ERR_LAUNCH = -5       /* the HIP runtime rejected a kernel launch  */
+    FA_ERR_LAUNCH = -5,      /* the HIP runtime rejected a kernel launch  */
+    FA_ERR_SCRATCH = -6      /* fa_bwd_noalloc: the shape needs more
+                                workspace than its static scratch holds  */
 };
 
 /* bf16 forward.  q, k, v: bf16 [B,N,H,d] inputs; o: bf16 [B,N,H,d] output;
@@ -196,6 +198,26 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v,
                const float* q_descale, const float* k_descale, const float* v_descale,
                void* o, float* lse, int B, int H, int H_kv, int N, int d, float scale,
                int causal, int window, hipStream_t stream);
+
+/* Backward that allocates nothing, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  It is fa_bwd (same kernels, arguments, layouts and
+ * results, bit for bit) without the workspace arguments: the workspace is a
+ * static device array of fa_bwd_noalloc_max_workspace() bytes (16 MiB) in
+ * the library, which every GPU that runs the library holds until the process
+ * ends.  Shapes with fa_bwd_workspace_size(B, H, N, d) above that (B * H *
+ * Npad above 2^21 rows, Npad = N rounded up to 64) return FA_ERR_SCRATCH
+ * before any HIP call.  `stream` must belong to the current device
+ * (FA_ERR_INVALID_ARG otherwise).  The first call on a device looks up the
+ * array's device address (hipGetSymbolAddress; FA_ERR_LAUNCH if that fails);
+ * no call allocates or frees memory.  All calls on one GPU share the array,
+ * so calls that overlap on one GPU (other streams or threads) race; calls
+ * on one stream are ordered and safe.  Nothing in the array needs clearing
+ * between calls. */
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                   const float* lse, void* dq, void* dk, void* dv,
+                   int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
+size_t fa_bwd_noalloc_max_workspace(void);
 
 /* Human-readable text for a return code (static storage). */
 const char* fa_strerror(int code);
