@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--sweep", action="store_true",
                     help="run only the shape sweep at 16384 tokens (H=16, N 512..16384, d 64 and "
                          "128, non-causal, forward + backward) beside the naive GPU baseline")
+    ap.add_argument("--mfma-calibration", action="store_true",
+                    help="run only the matrix-core calibration kernel (pure bf16 MFMA, and with 2 or "
+                         "4 vector instructions per MFMA) and print its sustained rates")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device-to-device copy of 1 GiB (3 times), the "
                          "reference for scaling HBM byte counters")
@@ -70,6 +73,34 @@ def copy_calibration():
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
                       "launches": 3}), flush=True)
+
+
+# Matrix-core calibration: (label, workgroups of 4 waves, vector instructions
+# per MFMA).  768 workgroups is one full round at 3 waves per SIMD (the
+# kernel's register use allows 3); 256 is one wave per SIMD.
+MFMA_CALIBRATION = [("w3_valu0", 768, 0), ("w3_valu2", 768, 2), ("w3_valu4", 768, 4),
+                    ("w1_valu0", 256, 0)]
+
+
+def mfma_calibration(torch, binding, iters=8000, launches=5):
+    """Sustained rate of the calibration kernel (fa_calibrate_mfma): eight
+    independent chains of 32x32x16 bf16 MFMAs per wave on register operands,
+    back to back, against the nameplate dense bf16 peak."""
+    out = {}
+    for label, n_wg, valu in MFMA_CALIBRATION:
+        o, flops = binding.calibrate_mfma(n_wg, 4, iters, valu)
+        for _ in range(2):
+            binding.calibrate_mfma(n_wg, 4, iters, valu, out=o)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(launches):
+            binding.calibrate_mfma(n_wg, 4, iters, valu, out=o)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / launches
+        tf = flops / (ms * 1e-3) / 1e12
+        out[label] = {"ms": round(ms, 4), "tflops": round(tf, 1), "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+    return out
 
 
 def source_digest(*names):
@@ -128,8 +159,13 @@ def naive_step(torch, q, k, v, do, scale, causal):
 # pages' Llama 2 70B head counts (64 query heads over 8 K/V heads), and a
 # causal sliding window of 4096 over 32768 tokens (the pages' Mistral 7B
 # example; flops counted over the visible pairs only).
+# b4_h16_n4096_d128 is the 16384-token sweep's N=4096, d=128 point, where the
+# backward alone is held to 35% of the peak; b16_h16_n1024_d64 is a second
+# sweep point.
 EXTRA_WORKLOADS = [
     ("b4_h32_n4096_d128_causal", 4, 32, 32, 4096, 128, True, None),
+    ("b4_h16_n4096_d128", 4, 16, 16, 4096, 128, False, None),
+    ("b16_h16_n1024_d64", 16, 16, 16, 1024, 64, False, None),
     ("b1_h32_n16384_d128_causal", 1, 32, 32, 16384, 128, True, None),
     ("b4_h16_n4096_d64_causal", 4, 16, 16, 4096, 64, True, None),
     ("b2_h64_hkv8_n4096_d128_causal_gqa", 2, 64, 8, 4096, 128, True, None),
@@ -184,6 +220,7 @@ def other_workloads(torch, binding, inputs, workloads, seed):
             med = median_ms(torch, f)
             res[f"{tag}_ms"] = round(med, 4)
             res[f"{tag}_tflops"] = round(fl / (med * 1e-3) / 1e12, 1)
+            res[f"{tag}_frac"] = round(fl / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
         if window is not None:
             res["pairs_skipped_frac"] = round(1 - workloads.window_pairs(N, window) / N ** 2, 4)
         out[name] = res
@@ -322,6 +359,10 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     binding.load()
+    if args.mfma_calibration:
+        print(json.dumps({"mfma_calibration": mfma_calibration(torch, binding),
+                          "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}), flush=True)
+        return
     if args.sweep:
         rows = shape_sweep(torch, binding, inputs, workloads, args.seed)
         print(json.dumps({"metric": "attention TFLOP/s (fwd+bwd) bf16, shape sweep at 16384 tokens",
@@ -432,6 +473,7 @@ def main():
     if not args.no_extra:
         out["other_workloads"] = other_workloads(torch, binding, inputs, workloads, args.seed)
         out["fp8_forward"] = fp8_workloads(torch, binding, inputs, workloads, args.seed)
+        out["mfma_calibration"] = mfma_calibration(torch, binding, launches=3)
 
     if not args.no_naive:
         try:

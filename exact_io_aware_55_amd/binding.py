@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libfa.so")
 
 EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_bwd_workspace_size", "fa_bwd", "fa_bwd_preprocess",
            "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_dq_stats", "fa_fwd_gqa", "fa_bwd_gqa", "fa_fwd_window",
-           "fa_bwd_window", "fa_fwd_fp8", "fa_bwd_noalloc", "fa_bwd_noalloc_max_workspace", "fa_strerror")
+           "fa_bwd_window", "fa_fwd_fp8", "fa_bwd_noalloc", "fa_bwd_noalloc_max_workspace", "fa_calibrate_mfma", "fa_strerror")
 
 FA_OK = 0
 FA_ERR_INVALID_ARG = -1
@@ -73,6 +73,8 @@ def load(path: str = LIB_PATH):
     lib.fa_bwd_noalloc.restype = i
     lib.fa_bwd_noalloc_max_workspace.argtypes = []
     lib.fa_bwd_noalloc_max_workspace.restype = sz
+    lib.fa_calibrate_mfma.argtypes = [vp, i, i, i, i, vp]
+    lib.fa_calibrate_mfma.restype = i
     lib.fa_strerror.argtypes = [i]
     lib.fa_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -286,6 +288,18 @@ def backward_noalloc(q, k, v, o, do, lse, causal=False, scale=None, out=None):
     _check(lib.fa_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk),
                               _ptr(dv), B, H, N, d, _scale(scale, d), int(bool(causal)), _stream()))
     return dq, dk, dv
+
+
+def calibrate_mfma(n_workgroups, waves=4, iters=4096, valu=0, out=None):
+    """Launch the matrix-core calibration kernel once on the current stream
+    (fa_calibrate_mfma).  Returns (checksum tensor, flops of the launch)."""
+    lib = load()
+    dev = torch.device("cuda", torch.cuda.current_device())
+    n = n_workgroups * 64 * waves
+    o = torch.empty(n, device=dev, dtype=torch.float32) if out is None else _need(out, "out", torch.float32,
+                                                                                   (n,), dev)
+    _check(lib.fa_calibrate_mfma(_ptr(o), n_workgroups, waves, iters, valu, _stream()))
+    return o, n_workgroups * waves * iters * 8 * 32768
 
 
 def backward_steps(q, k, v, o, do, lse, causal=False, scale=None, workspace=None, out=None,

@@ -34,7 +34,7 @@ FLAGS = [
 # any accumulator lives there, and copy the tiles back for the softmax.  The
 # long-lived d = 128 dK/dV accumulators are placed in AGPRs explicitly.
 _VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
-EXTRA = {"fa_bwd.hip": _VGPR_FORM}
+EXTRA = {"fa_bwd.hip": _VGPR_FORM, "fa_calib.hip": _VGPR_FORM}
 
 
 def _compile(src: str) -> str:

@@ -219,6 +219,20 @@ int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, c
                    int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
 size_t fa_bwd_noalloc_max_workspace(void);
 
+/* Measurement aid (not part of attention): the matrix-core calibration
+ * kernel of the roofline harness.  Launches n_workgroups workgroups of
+ * waves_per_workgroup (1..4) waves; each wave runs `iters` rounds of eight
+ * independent v_mfma_f32_32x32x16_bf16 chains on register operands (32768
+ * flops each, so n_workgroups * waves * iters * 8 * 32768 flops per launch)
+ * with valu_per_mfma (0, 2 or 4) independent vector instructions (an FMA
+ * and an exp2, alternately) after each MFMA.  out: device fp32 with
+ * n_workgroups * 64 * waves_per_workgroup elements (checksums, 4-byte
+ * aligned).  Its rate and MFMA-busy counter give the sustainable dense bf16
+ * rate and check the busy-cycle normalisation.  INVALID_ARG for out null or
+ * counts out of range; MISALIGNED; LAUNCH. */
+int fa_calibrate_mfma(float* out, int n_workgroups, int waves_per_workgroup, int iters,
+                      int valu_per_mfma, hipStream_t stream);
+
 /* Human-readable text for a return code (static storage). */
 const char* fa_strerror(int code);
 
