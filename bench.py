@@ -75,26 +75,33 @@ def copy_calibration():
                       "launches": 3}), flush=True)
 
 
-# Matrix-core calibration: (label, workgroups of 4 waves, vector instructions
-# per MFMA).  768 workgroups is one full round at 3 waves per SIMD (the
-# kernel's register use allows 3); 256 is one wave per SIMD.
-MFMA_CALIBRATION = [("w3_valu0", 768, 0), ("w3_valu2", 768, 2), ("w3_valu4", 768, 4),
-                    ("w1_valu0", 256, 0)]
+# Matrix-core calibration: (label, workgroups of 4 waves, mode).  512
+# workgroups is one full round at 2 waves per SIMD (as in the attention
+# kernels); 256 is one wave per SIMD.  Modes: 0 constant operands, 1 random
+# operands, 2 and 3 random plus 2 or 4 vector instructions per MFMA, 4 random
+# with the A operand read from LDS.
+MFMA_CALIBRATION = [("const_w2", 512, 0), ("random_w2", 512, 1), ("random_valu2_w2", 512, 2),
+                    ("random_valu4_w2", 512, 3), ("random_lds_w2", 512, 4), ("random_w1", 256, 1),
+                    ("const_w1", 256, 0)]
 
 
-def mfma_calibration(torch, binding, iters=8000, launches=5):
+def mfma_calibration(torch, binding, iters=4000, launches=10):
     """Sustained rate of the calibration kernel (fa_calibrate_mfma): eight
-    independent chains of 32x32x16 bf16 MFMAs per wave on register operands,
-    back to back, against the nameplate dense bf16 peak."""
+    independent chains of 32x32x16 bf16 MFMAs per wave, back to back, against
+    the nameplate dense bf16 peak.  A settling run first brings the clock to
+    its sustained state."""
+    o, _ = binding.calibrate_mfma(512, 4, iters, 1)
+    for _ in range(20):
+        binding.calibrate_mfma(512, 4, iters, 1, out=o)
     out = {}
-    for label, n_wg, valu in MFMA_CALIBRATION:
-        o, flops = binding.calibrate_mfma(n_wg, 4, iters, valu)
+    for label, n_wg, mode in MFMA_CALIBRATION:
+        o, flops = binding.calibrate_mfma(n_wg, 4, iters, mode)
         for _ in range(2):
-            binding.calibrate_mfma(n_wg, 4, iters, valu, out=o)
+            binding.calibrate_mfma(n_wg, 4, iters, mode, out=o)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(launches):
-            binding.calibrate_mfma(n_wg, 4, iters, valu, out=o)
+            binding.calibrate_mfma(n_wg, 4, iters, mode, out=o)
         e1.record()
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / launches
@@ -473,7 +480,7 @@ def main():
     if not args.no_extra:
         out["other_workloads"] = other_workloads(torch, binding, inputs, workloads, args.seed)
         out["fp8_forward"] = fp8_workloads(torch, binding, inputs, workloads, args.seed)
-        out["mfma_calibration"] = mfma_calibration(torch, binding, launches=3)
+        out["mfma_calibration"] = mfma_calibration(torch, binding, launches=4)
 
     if not args.no_naive:
         try:

@@ -290,16 +290,18 @@ def backward_noalloc(q, k, v, o, do, lse, causal=False, scale=None, out=None):
     return dq, dk, dv
 
 
-def calibrate_mfma(n_workgroups, waves=4, iters=4096, valu=0, out=None):
+def calibrate_mfma(n_workgroups, waves=4, iters=4096, mode=0, out=None):
     """Launch the matrix-core calibration kernel once on the current stream
-    (fa_calibrate_mfma).  Returns (checksum tensor, flops of the launch)."""
+    (fa_calibrate_mfma; ``mode`` 0 constant operands, 1 random operands, 2 and
+    3 random plus 2 or 4 vector instructions per MFMA, 4 random with the A
+    operand from LDS).  Returns (checksum tensor, flops of the launch)."""
     lib = load()
     dev = torch.device("cuda", torch.cuda.current_device())
     n = n_workgroups * 64 * waves
     o = torch.empty(n, device=dev, dtype=torch.float32) if out is None else _need(out, "out", torch.float32,
                                                                                    (n,), dev)
-    _check(lib.fa_calibrate_mfma(_ptr(o), n_workgroups, waves, iters, valu, _stream()))
-    return o, n_workgroups * waves * iters * 8 * 32768
+    _check(lib.fa_calibrate_mfma(_ptr(o), n_workgroups, waves, iters, mode, _stream()))
+    return o, n_workgroups * waves * iters * 16 * 32768
 
 
 def backward_steps(q, k, v, o, do, lse, causal=False, scale=None, workspace=None, out=None,

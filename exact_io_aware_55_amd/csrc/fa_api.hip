@@ -326,13 +326,13 @@ int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, c
                     stream);
 }
 
-int fa_calibrate_mfma(float* out, int n_workgroups, int waves_per_workgroup, int iters, int valu_per_mfma,
+int fa_calibrate_mfma(float* out, int n_workgroups, int waves_per_workgroup, int iters, int mode,
                       hipStream_t stream) {
     if (!out || n_workgroups < 1 || waves_per_workgroup < 1 || waves_per_workgroup > 4 || iters < 1)
         return FA_ERR_INVALID_ARG;
-    if (valu_per_mfma != 0 && valu_per_mfma != 2 && valu_per_mfma != 4) return FA_ERR_INVALID_ARG;
+    if (mode < 0 || mode > 4) return FA_ERR_INVALID_ARG;
     if (reinterpret_cast<uintptr_t>(out) & 3u) return FA_ERR_MISALIGNED;
-    if (fa::launch_calib_mfma(out, n_workgroups, waves_per_workgroup, iters, valu_per_mfma, stream) !=
+    if (fa::launch_calib_mfma(out, n_workgroups, waves_per_workgroup, iters, mode, stream) !=
         hipSuccess)
         return FA_ERR_LAUNCH;
     return FA_OK;

@@ -664,18 +664,37 @@ __global__ __launch_bounds__(bwdq::NT, 1) void bwd_dq_kernel(
         asm volatile("" : "+v"(ka0), "+v"(ka1), "+v"(kt0), "+v"(kt1));
         // dP^T's accumulator starts at -D (one per lane: the lane's query),
         // so it ends as dP^T - D
+        // feature-chunk major: four independent accumulator chains (S^T and
+        // dP^T of both 32-key tiles), with the K and V operands of chunk
+        // c + 1 read while the products of chunk c run
         f32x16 s[2], dp[2];
+        bf16x8 kop[2][2], vop[2][2];
+        auto read_kv = [&](int c, int buf) {
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+                const lds_char* a = ((c & 1) ? ka1 : ka0) + (c >> 1) * SUB + kt * 32 * 64;
+                kop[buf][kt] = lds_read_b128(a);
+                vop[buf][kt] = lds_read_b128(a + TILE);
+            }
+        };
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
             s[kt] = f32x16{};
 #pragma unroll
             for (int r = 0; r < 16; ++r) dp[kt][r] = dq_row;
+        }
+        read_kv(0, 0);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int c = 0; c < DC; ++c) {
-                const lds_char* a = ((c & 1) ? ka1 : ka0) + (c >> 1) * SUB + kt * 32 * 64;
-                s[kt] = mfma32x32x16(lds_read_b128(a), qreg[c], s[kt]);
-                dp[kt] = mfma32x32x16(lds_read_b128(a + TILE), oreg[c], dp[kt]);
+        for (int c = 0; c < DC; ++c) {
+            if (c + 1 < DC) read_kv(c + 1, (c + 1) & 1);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+                s[kt] = mfma32x32x16(kop[c & 1][kt], qreg[c], s[kt]);
+                dp[kt] = mfma32x32x16(vop[c & 1][kt], oreg[c], dp[kt]);
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
         // unmasked tiles start the loads of tile t + 2 here, behind the S^T and
         // dP^T reads, rather than as a burst at the top (masked tiles may
@@ -711,16 +730,29 @@ __global__ __launch_bounds__(bwdq::NT, 1) void bwd_dq_kernel(
                 const float d1 = fast_exp2(s[kt][r + 1]) * dp[kt][r + 1];
                 dsb[kt * 2 + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(d0, d1);
             }
-        // dQ^T += K^T dS^T; A operand = K^T from the row-major K block
+        // dQ^T += K^T dS^T; A operand = K^T from the row-major K block.  Key
+        // chunk major: DT independent chains, the K^T operands of chunk cc + 1
+        // read while the products of chunk cc run
+        bf16x8 kto[2][DT];
+        auto read_kt = [&](int cc, int buf) {
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int cc = 0; cc < 4; ++cc) {
+            for (int dt = 0; dt < DT; ++dt) {
                 const int off = dt * SUB + cc * 16 * 64;
-                const bf16x8 ka = __builtin_shufflevector(lds_read_tr16(kt0 + off), lds_read_tr16(kt1 + off),
-                                                          0, 1, 2, 3, 4, 5, 6, 7);
-                dqacc[dt] = mfma32x32x16(ka, __builtin_bit_cast(bf16x8, dsb[cc]), dqacc[dt]);
+                kto[buf][dt] = __builtin_shufflevector(lds_read_tr16(kt0 + off), lds_read_tr16(kt1 + off), 0, 1,
+                                                       2, 3, 4, 5, 6, 7);
             }
+        };
+        read_kt(0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+            if (cc + 1 < 4) read_kt(cc + 1, (cc + 1) & 1);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+                dqacc[dt] = mfma32x32x16(kto[cc & 1][dt], __builtin_bit_cast(bf16x8, dsb[cc]), dqacc[dt]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     };
 #pragma clang loop unroll(disable)
     for (int t = t_lo; t < t_ulo; ++t) tile(t, flag_t<CAUSAL>{});

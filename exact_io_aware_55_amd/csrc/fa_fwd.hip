@@ -200,15 +200,26 @@ __global__ __launch_bounds__(fwd::NT, 1) void fwd_bf16_kernel(
         const lds_char* vb = stage + v_rd;
         asm volatile("" : "+v"(kb0), "+v"(kb1), "+v"(vb));
         // S^T = K Q^T for the block's 32-key tiles
+        // feature-chunk major: KT independent accumulator chains, and the K
+        // operands of chunk c + 1 read while the products of chunk c run
         f32x16 s[KT];
+        bf16x8 kop[2][KT];
+        auto read_k = [&](int c, bf16x8* dst) {
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt) {
-            s[kt] = f32x16{};
+            for (int kt = 0; kt < KT; ++kt)
+                dst[kt] = lds_read_b128(((c & 1) ? kb1 : kb0) + (c >> 1) * SUB + kt * 32 * 64);
+        };
 #pragma unroll
-            for (int c = 0; c < DC; ++c) {
-                const lds_char* a = ((c & 1) ? kb1 : kb0) + (c >> 1) * SUB + kt * 32 * 64;
-                s[kt] = mfma32x32x16(lds_read_b128(a), qreg[c], s[kt]);
-            }
+        for (int kt = 0; kt < KT; ++kt) s[kt] = f32x16{};
+        read_k(0, kop[0]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int c = 0; c < DC; ++c) {
+            if (c + 1 < DC) read_k(c + 1, kop[(c + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt) s[kt] = mfma32x32x16(kop[c & 1][kt], qreg[c], s[kt]);
+            __builtin_amdgcn_sched_barrier(0);
         }
         // unmasked blocks start the loads of block t + NSTAGE - 1 here,
         // behind the K reads, rather than as a burst at the top
@@ -320,16 +331,27 @@ __global__ __launch_bounds__(fwd::NT, 1) void fwd_bf16_kernel(
         __builtin_amdgcn_sched_barrier(0);
         // O^T += V^T P^T; the A operand (8 keys of one feature row) comes
         // from two transposing reads: keys 16cc + 4h + 0..3 and +8.
+        // key-chunk major: DT independent accumulator chains, and the V^T
+        // operands of chunk cc + 1 read while the products of chunk cc run
+        bf16x8 vop[2][DT];
+        auto read_v = [&](int cc, bf16x8* dst) {
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-            for (int cc = 0; cc < 2 * KT; ++cc) {
+            for (int dt = 0; dt < DT; ++dt) {
                 const lds_char* a0 = vb + dt * SUB + cc * 16 * 64;
-                const bf16x4 lo = lds_read_tr16(a0);
-                const bf16x4 hi = lds_read_tr16(a0 + 8 * 64);
-                const bf16x8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                oacc[dt] = mfma32x32x16(va, __builtin_bit_cast(bf16x8, pw[cc]), oacc[dt]);
+                dst[dt] = __builtin_shufflevector(lds_read_tr16(a0), lds_read_tr16(a0 + 8 * 64), 0, 1, 2, 3,
+                                                  4, 5, 6, 7);
             }
+        };
+        read_v(0, vop[0]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int cc = 0; cc < 2 * KT; ++cc) {
+            if (cc + 1 < 2 * KT) read_v(cc + 1, vop[(cc + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+                oacc[dt] = mfma32x32x16(vop[cc & 1][dt], __builtin_bit_cast(bf16x8, pw[cc]), oacc[dt]);
+            __builtin_amdgcn_sched_barrier(0);
         }
         __builtin_amdgcn_sched_barrier(0);
     };

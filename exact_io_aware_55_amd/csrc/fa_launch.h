@@ -46,9 +46,9 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void
                          const void* o, const float* lse, float* lse2, float* delta, hipStream_t stream);
 
 // Matrix-core calibration: n_workgroups x `waves` waves, each `iters` rounds
-// of 8 independent 32x32x16 bf16 MFMAs (plus `valu` in {0, 2, 4} vector
-// instructions per MFMA); one checksum per thread into out.
-hipError_t launch_calib_mfma(float* out, int n_workgroups, int waves, int iters, int valu,
+// of 16 32x32x16 bf16 MFMAs on 8 independent chains; `mode` 0 - 4 as in
+// fa_calibrate_mfma; one checksum per thread into out.
+hipError_t launch_calib_mfma(float* out, int n_workgroups, int waves, int iters, int mode,
                              hipStream_t stream);
 
 }  // namespace fa

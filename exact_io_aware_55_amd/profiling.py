@@ -10,6 +10,8 @@ summary::
     python -m exact_io_aware_55_amd.profiling traffic FETCH WRITE COPY_FETCH COPY_WRITE OUT.md WORKLOAD
     python -m exact_io_aware_55_amd.profiling counters MFMA_DIR LDS_DIR TRACE_DIR OUT.md WORKLOAD
     python -m exact_io_aware_55_amd.profiling scaling COPY_FETCH COPY_WRITE OUT.md B H d N:FETCH:WRITE ...
+    python -m exact_io_aware_55_amd.profiling valu VALU_DIR TRACE_DIR OUT.md WORKLOAD
+    python -m exact_io_aware_55_amd.profiling calibration RATES.json MFMA_DIR OUT.md
 
 ``DIR`` holds a ``--kernel-trace --stats`` run (``*_kernel_stats.csv``); the
 traffic arguments are the output folders of four ``--pmc`` runs: FETCH_SIZE
@@ -17,7 +19,11 @@ and WRITE_SIZE of the bench workload, and the same two counters for the
 ``bench.py --copy-calibration`` device copy of 1 GiB, whose known byte count
 scales the counters to bytes.  ``counters`` summarises two more ``--pmc``
 runs: matrix-core busy cycles and bf16 MFMA operations, and LDS bank / address
-conflicts and LDS activity.
+conflicts and LDS activity.  ``valu`` summarises the vector-instruction group
+(vector, transcendental, MFMA and LDS instructions, MFMA/vector co-execution
+and wave waiting cycles) per kernel; ``calibration`` the matrix-core
+calibration kernel's rates (the JSON line of ``bench.py --mfma-calibration``)
+beside its clock and MFMA-busy counters.
 """
 import csv
 import glob
@@ -254,6 +260,117 @@ def scaling(copy_fetch, copy_write, out, B, H, d, runs):
     return worst
 
 
+VALU_COUNTERS = ("SQ_INSTS_VALU SQ_INSTS_VALU_TRANS_F32 SQ_INSTS_MFMA SQ_VALU_MFMA_COEXEC_CYCLES "
+                 "SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_LDS SQ_INSTS_LDS GRBM_GUI_ACTIVE")
+
+
+def valu(valu_dir, trace_dir, out, workload):
+    """Vector and transcendental instructions per MFMA, co-execution of the
+    vector unit with the matrix core, and wave waiting, per kernel."""
+    c_all = _counter_rows(valu_dir)
+    tns = _trace_ns(trace_dir)
+    xcc, cus, simds = _agent(valu_dir)
+    lines = [f"# Vector-instruction counters per launch: {workload}", "",
+             "Commands (from the repository root on one MI355X, after "
+             "`cd /tmp && export TMPDIR=/tmp`; `$REPO` is the repository root, `$OUT` the folder "
+             "that receives the profiler output):", "", "```",
+             f"rocprofv3 --pmc {VALU_COUNTERS} --output-format csv -d $OUT/pmc_valu -o bench -- "
+             "python3 $REPO/bench.py --steps 2 --warmup 1 --no-naive --no-cpu --no-extra",
+             f"python -m exact_io_aware_55_amd.profiling valu $OUT/pmc_valu $OUT/prof profiles/<this file> "
+             f"{workload}", "```", "",
+             "Derived columns (per launch; SQ_INSTS_VALU counts the MFMA instructions too, so vector "
+             "instructions = SQ_INSTS_VALU - SQ_INSTS_MFMA; the SQ_WAVE_CYCLES and SQ_WAIT_ANY counters "
+             "count in units of 4 cycles, which cancels in their ratio):",
+             "- vector / MFMA, exp2 / MFMA, LDS / MFMA: instructions issued per MFMA instruction;",
+             "- co-execution = SQ_VALU_MFMA_COEXEC_CYCLES / (GRBM_GUI_ACTIVE / XCDs x CUs x SIMDs): the "
+             "share of SIMD cycles in which a vector instruction ran beside a busy matrix core;",
+             "- waiting = SQ_WAIT_ANY / SQ_WAVE_CYCLES: the share of resident-wave cycles spent waiting "
+             "(dependencies, counters, barriers).", "",
+             "| kernel | launch (us, traced) | MFMA (M) | vector / MFMA | exp2 / MFMA | LDS / MFMA | "
+             "co-execution | waiting |", "|---|---|---|---|---|---|---|---|"]
+    for k, c in c_all.items():
+        mf = c.get("SQ_INSTS_MFMA", 0.0)
+        if not mf:
+            continue
+        grbm = c.get("GRBM_GUI_ACTIVE", 0.0) / xcc
+        co = c.get("SQ_VALU_MFMA_COEXEC_CYCLES", 0.0) / (grbm * cus * simds) if grbm else 0.0
+        wait = c.get("SQ_WAIT_ANY", 0.0) / c["SQ_WAVE_CYCLES"] if c.get("SQ_WAVE_CYCLES") else 0.0
+        lines.append(f"| `{k}` | {tns.get(k, c['_ns']) / 1e3:.0f} | {mf / 1e6:.1f} | "
+                     f"{(c['SQ_INSTS_VALU'] - mf) / mf:.2f} | {c['SQ_INSTS_VALU_TRANS_F32'] / mf:.2f} | "
+                     f"{c['SQ_INSTS_LDS'] / mf:.2f} | {100 * co:.1f}% | {100 * wait:.1f}% |")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
+CALIB_MODES = {0: "constant operands", 1: "random operands", 2: "random + FMA + exp2 per MFMA",
+               3: "random + 2 FMA + 2 exp2 per MFMA", 4: "random, A operand from LDS"}
+
+
+def calibration(rates_json, mfma_dir, out):
+    """Rates of the calibration modes (bench.py --mfma-calibration) beside the
+    clock and MFMA-busy counters of their launches (the last launches of each
+    kernel and grid size, after the clock has settled)."""
+    import collections
+
+    rates = None
+    for line in open(rates_json):
+        line = line.strip()
+        if line.startswith("{") and "mfma_calibration" in line:
+            rates = json.loads(line)["mfma_calibration"]
+    if rates is None:
+        raise SystemExit(f"no calibration line in {rates_json}")
+    xcc, cus, simds = _agent(mfma_dir)
+    per = collections.OrderedDict()
+    for f in glob.glob(os.path.join(mfma_dir, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            d = per.setdefault(int(r["Dispatch_Id"]), {"k": _short(r["Kernel_Name"]), "grid": int(r["Grid_Size"]),
+                                                       "ns": float(r["End_Timestamp"]) - float(r["Start_Timestamp"])})
+            d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    groups = collections.OrderedDict()
+    for d in per.values():
+        groups.setdefault((d["k"], d["grid"]), []).append(d)
+    lines = ["# Matrix-core calibration (fa_calibrate_mfma)", "",
+             "Commands (from the repository root on one MI355X, after "
+             "`cd /tmp && export TMPDIR=/tmp`; `$REPO` is the repository root, `$OUT` the folder "
+             "that receives the profiler output):", "", "```",
+             "python3 $REPO/bench.py --mfma-calibration > $OUT/calibration.json",
+             "rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_BUSY_CU_CYCLES "
+             "GRBM_GUI_ACTIVE --output-format csv -d $OUT/calib_mfma -o calib -- python3 $REPO/bench.py "
+             "--mfma-calibration",
+             "python -m exact_io_aware_55_amd.profiling calibration $OUT/calibration.json $OUT/calib_mfma "
+             "profiles/<this file>", "```", "",
+             "Each wave runs eight independent chains of v_mfma_f32_32x32x16_bf16 (32768 flops each) back "
+             f"to back.  Rates from HIP events over 10 launches after a settling run; the nameplate is "
+             f"2516.6 TFLOP/s (256 CUs x 4096 flop/clock x 2.4 GHz).  Counters ({xcc} XCDs, {cus} CUs, "
+             f"{simds} SIMDs per CU) from the last 5 launches of each kernel and grid: clock = "
+             "GRBM_GUI_ACTIVE / XCDs / launch duration (the counter run's own timestamps), MFMA busy = "
+             "SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / XCDs x CUs x SIMDs), executed flops = "
+             "SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512.", "",
+             "| run | mode | waves per SIMD | TFLOP/s | of nameplate | clock (GHz) | MFMA busy | "
+             "counted / executed flops |", "|---|---|---|---|---|---|---|---|"]
+    mode_kernel = {0: ("<false, 0>", None), 1: ("<true, 0>", None), 2: ("<true, 2>", None),
+                   3: ("<true, 4>", None), 4: ("calib_mfma_lds_kernel", None)}
+    for label, r in rates.items():
+        mode = {"const": 0, "random": 1, "random_valu2": 2, "random_valu4": 3, "random_lds": 4}[label.rsplit("_", 1)[0]]
+        waves = int(label.rsplit("_w", 1)[1])
+        grid = 256 * 4 * 64 * waves
+        key = [k for k in groups if mode_kernel[mode][0] in k[0] and k[1] == grid]
+        clock = busy = ratio = float("nan")
+        if key:
+            last = groups[key[0]][-5:]
+            g = sum(d["GRBM_GUI_ACTIVE"] for d in last) / xcc
+            ns = sum(d["ns"] for d in last)
+            clock = g / ns
+            busy = sum(d["SQ_VALU_MFMA_BUSY_CYCLES"] for d in last) / (g * cus * simds)
+            ex = sum(d["SQ_INSTS_VALU_MFMA_MOPS_BF16"] for d in last) * 512 / len(last)
+            flops = r["tflops"] * 1e12 * r["ms"] * 1e-3
+            ratio = flops / ex if ex else float("nan")
+        lines.append(f"| `{label}` | {CALIB_MODES[mode]} | {waves} | {r['tflops']:.0f} | "
+                     f"{100 * r['frac']:.1f}% | {clock:.2f} | {100 * busy:.1f}% | {ratio:.3f} |")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
 def main(argv):
     if len(argv) >= 5 and argv[0] == "trace":
         trace(argv[1], argv[2], argv[3], argv[4])
@@ -265,6 +382,10 @@ def main(argv):
             n, fdir, wdir = spec.split(":")
             runs.append((int(n), fdir, wdir))
         scaling(argv[1], argv[2], argv[3], int(argv[4]), int(argv[5]), int(argv[6]), runs)
+    elif len(argv) >= 5 and argv[0] == "valu":
+        valu(argv[1], argv[2], argv[3], argv[4])
+    elif len(argv) >= 4 and argv[0] == "calibration":
+        calibration(argv[1], argv[2], argv[3])
     elif len(argv) >= 7 and argv[0] == "traffic":
         workload = argv[6]
         shape = {p[0]: p[1:] for p in workload.split("_") if p[:1] in "bhnd" and p[1:].isdigit()}

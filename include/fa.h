@@ -221,17 +221,21 @@ size_t fa_bwd_noalloc_max_workspace(void);
 
 /* Measurement aid (not part of attention): the matrix-core calibration
  * kernel of the roofline harness.  Launches n_workgroups workgroups of
- * waves_per_workgroup (1..4) waves; each wave runs `iters` rounds of eight
- * independent v_mfma_f32_32x32x16_bf16 chains on register operands (32768
- * flops each, so n_workgroups * waves * iters * 8 * 32768 flops per launch)
- * with valu_per_mfma (0, 2 or 4) independent vector instructions (an FMA
- * and an exp2, alternately) after each MFMA.  out: device fp32 with
- * n_workgroups * 64 * waves_per_workgroup elements (checksums, 4-byte
- * aligned).  Its rate and MFMA-busy counter give the sustainable dense bf16
- * rate and check the busy-cycle normalisation.  INVALID_ARG for out null or
- * counts out of range; MISALIGNED; LAUNCH. */
-int fa_calibrate_mfma(float* out, int n_workgroups, int waves_per_workgroup, int iters,
-                      int valu_per_mfma, hipStream_t stream);
+ * waves_per_workgroup (1..4) waves; each wave runs `iters` rounds of 16
+ * v_mfma_f32_32x32x16_bf16 on eight independent accumulator chains (32768
+ * flops each, so n_workgroups * waves * iters * 16 * 32768 flops per launch).
+ * mode: 0 register operands that never change; 1 random register operands
+ * (eight A and eight B tiles per wave, paired differently by consecutive
+ * MFMAs); 2 mode 1 plus an FMA and an exp2 per MFMA; 3 mode 1 plus two FMAs
+ * and two exp2 per MFMA; 4 mode 1 with the A operand read from LDS (one
+ * ds_read_b128 per MFMA).  out: device fp32 with n_workgroups * 64 *
+ * waves_per_workgroup elements (checksums, 4-byte aligned).  The rates of
+ * modes 0 and 1 are the chip's dense bf16 rate with and without operand
+ * switching (the second is what real data sees); the MFMA-busy counter of
+ * mode 0 checks the busy-cycle normalisation.  INVALID_ARG for out null or
+ * counts or mode out of range; MISALIGNED; LAUNCH. */
+int fa_calibrate_mfma(float* out, int n_workgroups, int waves_per_workgroup, int iters, int mode,
+                      hipStream_t stream);
 
 /* Human-readable text for a return code (static storage). */
 const char* fa_strerror(int code);
