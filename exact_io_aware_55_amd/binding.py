@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libfa.so")
 
 EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_bwd_workspace_size", "fa_bwd", "fa_bwd_preprocess",
            "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_dq_stats", "fa_fwd_gqa", "fa_bwd_gqa", "fa_fwd_window",
-           "fa_bwd_window", "fa_fwd_fp8", "fa_bwd_noalloc", "fa_bwd_noalloc_max_workspace", "fa_calibrate_mfma", "fa_strerror")
+           "fa_bwd_window", "fa_fwd_fp8", "fa_bwd_noalloc", "fa_bwd_noalloc_max_workspace", "fa_calibrate_mfma", "fa_probe_mfma", "fa_strerror")
 
 FA_OK = 0
 FA_ERR_INVALID_ARG = -1
@@ -75,6 +75,8 @@ def load(path: str = LIB_PATH):
     lib.fa_bwd_noalloc_max_workspace.restype = sz
     lib.fa_calibrate_mfma.argtypes = [vp, i, i, i, i, vp]
     lib.fa_calibrate_mfma.restype = i
+    lib.fa_probe_mfma.argtypes = [i, vp, vp, vp, i, i, vp]
+    lib.fa_probe_mfma.restype = i
     lib.fa_strerror.argtypes = [i]
     lib.fa_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -302,6 +304,21 @@ def calibrate_mfma(n_workgroups, waves=4, iters=4096, mode=0, out=None):
                                                                                    (n,), dev)
     _check(lib.fa_calibrate_mfma(_ptr(o), n_workgroups, waves, iters, mode, _stream()))
     return o, n_workgroups * waves * iters * 16 * 32768
+
+
+def probe_mfma(a, b, fp8=False):
+    """C = A B^T per 32 x 32 tile on the matrix core (fa_probe_mfma): a, b
+    are [tiles, 32, k] GPU tensors (bf16, or uint8 E4M3 codes with fp8).
+    Returns C [tiles, 32, 32] fp32."""
+    lib = load()
+    dt = torch.uint8 if fp8 else torch.bfloat16
+    if a.dim() != 3 or a.shape[1] != 32:
+        raise ValueError("a must be [tiles, 32, k]")
+    _need(a, "a", dt, a.shape, a.device)
+    _need(b, "b", dt, a.shape, a.device)
+    c = torch.empty((a.shape[0], 32, 32), device=a.device, dtype=torch.float32)
+    _check(lib.fa_probe_mfma(int(bool(fp8)), _ptr(a), _ptr(b), _ptr(c), a.shape[0], a.shape[2], _stream()))
+    return c
 
 
 def backward_steps(q, k, v, o, do, lse, causal=False, scale=None, workspace=None, out=None,

@@ -338,6 +338,15 @@ int fa_calibrate_mfma(float* out, int n_workgroups, int waves_per_workgroup, int
     return FA_OK;
 }
 
+int fa_probe_mfma(int fp8, const void* a, const void* b, float* c, int n_tiles, int k, hipStream_t stream) {
+    if (!a || !b || !c || n_tiles < 1 || k < 1 || (fp8 != 0 && fp8 != 1)) return FA_ERR_INVALID_ARG;
+    if (k % (fp8 ? 64 : 16) != 0) return FA_ERR_INVALID_ARG;
+    if ((long long)n_tiles * 32 * k * (fp8 ? 1 : 2) >= (1LL << 31)) return FA_ERR_UNSUPPORTED;
+    if (!aligned16(a) || !aligned16(b) || (reinterpret_cast<uintptr_t>(c) & 3u)) return FA_ERR_MISALIGNED;
+    if (fa::launch_probe_mfma(fp8, a, b, c, n_tiles, k, stream) != hipSuccess) return FA_ERR_LAUNCH;
+    return FA_OK;
+}
+
 const char* fa_strerror(int code) {
     switch (code) {
         case FA_OK: return "success";

@@ -125,6 +125,59 @@ __global__ __launch_bounds__(256) void calib_mfma_lds_kernel(float* __restrict__
     out[blockIdx.x * blockDim.x + threadIdx.x] = checksum(acc, s);
 }
 
+// ---------------------------------------------------------------------------
+// Matrix-core probe: C = A B^T for independent 32 x 32 tiles on the matrix
+// core the attention kernels use, so tests can measure its accumulation
+// error against exact products.  One wave per tile: A [tile][32][k] and
+// B [tile][32][k] row-major (the contraction index fastest), C [tile][32][32]
+// fp32 with C[i][c] = sum_j A[i][j] B[c][j].  FP8 = false: bf16 operands on
+// v_mfma_f32_32x32x16_bf16 (k a multiple of 16); true: OCP E4M3 codes on
+// v_mfma_f32_32x32x64_f8f6f4 (k a multiple of 64).  Lane l supplies row
+// l & 31 of A (column l & 31 of B) and the contraction slots
+// KC/2 * (l >> 5) .. + KC/2 - 1 of each KC-long chunk; consecutive chunks
+// accumulate in the same fp32 accumulator, as the kernels chain them.
+// ---------------------------------------------------------------------------
+typedef int i32x8p __attribute__((ext_vector_type(8)));
+template <bool FP8>
+__global__ __launch_bounds__(256) void probe_mfma_kernel(const char* __restrict__ A, const char* __restrict__ B,
+                                                         float* __restrict__ C, int n_tiles, int k) {
+    const int tile = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (tile >= n_tiles) return;
+    const int lane = threadIdx.x & 63, l32 = lane & 31, hl = lane >> 5;
+    constexpr int EB = FP8 ? 1 : 2;            // bytes per element
+    constexpr int KC = FP8 ? 64 : 16;          // contraction per MFMA
+    const long row_bytes = (long)k * EB;
+    const char* a = A + ((long)tile * 32 + l32) * row_bytes + (KC / 2) * hl * EB;
+    const char* b = B + ((long)tile * 32 + l32) * row_bytes + (KC / 2) * hl * EB;
+    f32x16 acc = f32x16{};
+    for (int c0 = 0; c0 < k; c0 += KC) {
+        if constexpr (FP8) {
+            const u32x4* pa = reinterpret_cast<const u32x4*>(a + c0);
+            const u32x4* pb = reinterpret_cast<const u32x4*>(b + c0);
+            const i32x8p va = __builtin_bit_cast(i32x8p, __builtin_shufflevector(pa[0], pa[1], 0, 1, 2, 3, 4, 5, 6, 7));
+            const i32x8p vb = __builtin_bit_cast(i32x8p, __builtin_shufflevector(pb[0], pb[1], 0, 1, 2, 3, 4, 5, 6, 7));
+            acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, vb, acc, 0, 0, 0, 0, 0, 0);
+        } else {
+            const bf16x8 va = as_bf16x8(*reinterpret_cast<const u32x4*>(a + c0 * EB));
+            const bf16x8 vb = as_bf16x8(*reinterpret_cast<const u32x4*>(b + c0 * EB));
+            acc = mfma32x32x16(va, vb, acc);
+        }
+    }
+    float* dst = C + (long)tile * 32 * 32 + l32;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dst[(8 * (r >> 2) + 4 * hl + (r & 3)) * 32] = acc[r];
+}
+
+hipError_t launch_probe_mfma(int fp8, const void* a, const void* b, float* c, int n_tiles, int k,
+                             hipStream_t stream) {
+    const dim3 grid((unsigned)((n_tiles + 3) / 4)), block(256);
+    auto A = static_cast<const char*>(a);
+    auto B = static_cast<const char*>(b);
+    if (fp8) hipLaunchKernelGGL(probe_mfma_kernel<true>, grid, block, 0, stream, A, B, c, n_tiles, k);
+    else hipLaunchKernelGGL(probe_mfma_kernel<false>, grid, block, 0, stream, A, B, c, n_tiles, k);
+    return hipGetLastError();
+}
+
 hipError_t launch_calib_mfma(float* out, int n_workgroups, int waves, int iters, int mode,
                              hipStream_t stream) {
     const dim3 grid((unsigned)n_workgroups), block((unsigned)(64 * waves));

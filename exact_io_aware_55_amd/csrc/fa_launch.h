@@ -51,4 +51,9 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void
 hipError_t launch_calib_mfma(float* out, int n_workgroups, int waves, int iters, int mode,
                              hipStream_t stream);
 
+// Matrix-core probe: C[t] = A[t] B[t]^T for n_tiles 32 x 32 tiles with
+// contraction length k, on the bf16 (fp8 = 0) or E4M3 (fp8 = 1) MFMA.
+hipError_t launch_probe_mfma(int fp8, const void* a, const void* b, float* c, int n_tiles, int k,
+                             hipStream_t stream);
+
 }  // namespace fa

@@ -237,6 +237,19 @@ size_t fa_bwd_noalloc_max_workspace(void);
 int fa_calibrate_mfma(float* out, int n_workgroups, int waves_per_workgroup, int iters, int mode,
                       hipStream_t stream);
 
+/* Measurement aid (not part of attention): the matrix-core probe used to
+ * measure the accumulation error of the MFMA instructions the kernels use.
+ * For n_tiles independent 32 x 32 tiles it computes, in fp32 on the matrix
+ * core, C[t][i][c] = sum_j A[t][i][j] * B[t][c][j] with contraction length
+ * k, chaining k / 16 (bf16, fp8 = 0: v_mfma_f32_32x32x16_bf16) or k / 64
+ * (fp8 = 1: OCP E4M3 codes, v_mfma_f32_32x32x64_f8f6f4) MFMAs in one fp32
+ * accumulator.  a, b: device [n_tiles][32][k] row-major (bf16 or byte
+ * codes), 16-byte aligned; c: device fp32 [n_tiles][32][32], 4-byte aligned.
+ * INVALID_ARG for null pointers, counts below 1, fp8 not 0 or 1, or k not a
+ * multiple of 16 (bf16) / 64 (fp8); UNSUPPORTED when an operand reaches
+ * 2^31 bytes; MISALIGNED; LAUNCH. */
+int fa_probe_mfma(int fp8, const void* a, const void* b, float* c, int n_tiles, int k, hipStream_t stream);
+
 /* Human-readable text for a return code (static storage). */
 const char* fa_strerror(int code);
 

@@ -221,3 +221,19 @@ def test_calibration_argument_errors(lib):
                                      (4, 4, 10, -1), (4, 4, 10, 5)):
         assert f(V(FAKE), n_wg, waves, iters, mode, None) == binding.FA_ERR_INVALID_ARG
     assert f(V(FAKE + 2), 4, 4, 10, 0, None) == binding.FA_ERR_MISALIGNED
+
+
+def test_probe_argument_errors(lib):
+    """fa_probe_mfma (the matrix-core accumulation probe) rejects bad
+    arguments before any HIP call."""
+    V = ctypes.c_void_p
+    f = lib.fa_probe_mfma
+    ok = (V(FAKE), V(FAKE), V(FAKE))
+    assert f(0, None, V(FAKE), V(FAKE), 1, 16, None) == binding.FA_ERR_INVALID_ARG
+    assert f(2, *ok, 1, 64, None) == binding.FA_ERR_INVALID_ARG
+    assert f(0, *ok, 0, 16, None) == binding.FA_ERR_INVALID_ARG
+    assert f(0, *ok, 1, 24, None) == binding.FA_ERR_INVALID_ARG      # bf16: k a multiple of 16
+    assert f(1, *ok, 1, 96, None) == binding.FA_ERR_INVALID_ARG      # fp8: k a multiple of 64
+    assert f(1, *ok, 1 << 16, 1 << 16, None) == binding.FA_ERR_UNSUPPORTED
+    assert f(0, V(FAKE + 8), V(FAKE), V(FAKE), 1, 16, None) == binding.FA_ERR_MISALIGNED
+    assert f(0, V(FAKE), V(FAKE), V(FAKE + 2), 1, 16, None) == binding.FA_ERR_MISALIGNED
