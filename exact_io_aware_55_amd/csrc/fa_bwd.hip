@@ -119,7 +119,7 @@ __global__ __launch_bounds__(bwd::NT, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const __bf16* __restrict__ dO, const float* __restrict__ stats, int delta_off,
     __bf16* __restrict__ dK, __bf16* __restrict__ dV, int H, int G, int N, int window, int Npad,
-    float scale, float scale_log2, int nkb) {
+    float scale, float scale_log2, int nkb, int gen, int group) {
     using namespace bwd;
     constexpr int DC = D / 16;                 // k-chunks over features
     constexpr int DT = D / 32;                 // 32-feature sub-tiles
@@ -153,7 +153,7 @@ __global__ __launch_bounds__(bwd::NT, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     // the workgroup walks the query blocks of all of them (G = 1: one head)
     const int Hkv = H / G;
     int bhk, kb;                               // causal: key block 0 (the longest) first
-    order_blocks(blockIdx.x, gridDim.x, nkb, CAUSAL, false, bhk, kb, causal_group<D>());
+    order_blocks(blockIdx.x, gridDim.x, nkb, CAUSAL, false, bhk, kb, group);
     const int b = bhk / Hkv, hk = bhk - b * Hkv;
     const int row_stride = H * D;
     const unsigned row_bytes = (unsigned)row_stride * 2u;
@@ -212,8 +212,9 @@ __global__ __launch_bounds__(bwd::NT, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     __builtin_amdgcn_s_barrier();
 
     // ---- query steps: for each query head g of the group, blocks
-    // first..nsteps-1 in order, so the key blocks of one head that run at
-    // once read the same query blocks at about the same time (L2 hits) ----
+    // first..last in order (or the whole sequence reversed, see rev), so the
+    // key blocks of one head that run at once read the same query blocks at
+    // about the same time (L2 hits) ----
     // causal: queries k0 .. k0 + KB - 1 + window - 1 can see these keys
     // (query i sees keys j with i - window < j <= i; window >= N: plain causal)
     const int nsteps = (N + BR - 1) / BR;
@@ -221,7 +222,11 @@ __global__ __launch_bounds__(bwd::NT, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     const int last = CAUSAL ? min(nsteps - 1, (k0 + KB - 2 + window) / BR) : nsteps - 1;
     const int nst = last - first + 1;          // per query head
     const int nst_all = G * nst;
+    // causal workgroups of an even generation (those that start together)
+    // walk their steps from the last query block down to the diagonal
+    const bool rev = CAUSAL && !WIN && gen > 0 && !odd_generation(blockIdx.x, gen);
     auto step_of = [&](int it, int& g) {       // query block of step it, and its head
+        if (rev) it = nst_all - 1 - it;
         g = it / nst;
         return first + (it - g * nst);
     };
@@ -492,7 +497,7 @@ __global__ __launch_bounds__(bwdq::NT, 1) void bwd_dq_kernel(
     const __bf16* __restrict__ dO, const __bf16* __restrict__ O, const float* __restrict__ LSE,
     float* __restrict__ lse2, float* __restrict__ delta,
     __bf16* __restrict__ dQ, int H, int G, int N, int window, int Npad, float scale, float scale_log2,
-    int nqb) {
+    int nqb, int gen, int group) {
     using namespace bwdq;
     // K/V blocks resident in the LDS ring: 4 at d = 128, where one barrier
     // serves two blocks (129 KB of LDS), 3 at d = 64
@@ -518,7 +523,7 @@ __global__ __launch_bounds__(bwdq::NT, 1) void bwd_dq_kernel(
     const int tg = lane >> 4, tj = lane & 15;
 
     int bh, qb;                                // causal: longest query blocks first
-    order_blocks(blockIdx.x, gridDim.x, nqb, CAUSAL, true, bh, qb, causal_group<D>());
+    order_blocks(blockIdx.x, gridDim.x, nqb, CAUSAL, true, bh, qb, group);
     const int b = bh / H, h = bh - b * H;
     const int row_stride = H * D;
     const long head_off = ((long)b * N * H + h) * D;
@@ -548,6 +553,9 @@ __global__ __launch_bounds__(bwdq::NT, 1) void bwd_dq_kernel(
     const int t_lo = CAUSAL ? max(0, q0 - window + 1) / BC : 0;
     const int t_uhi = CAUSAL ? max(t_lo, min(ntiles, (q0 + 1) / BC)) : ntiles;
     const int t_ulo = CAUSAL ? min(t_uhi, max(t_lo, (max(0, q0 + BR - window) + BC - 1) / BC)) : 0;
+    // causal workgroups of an odd generation run their unmasked tiles from
+    // the diagonal down (position t visits tile sweep_block(t))
+    const bool rev = CAUSAL && !WIN && odd_generation(blockIdx.x, gen);
 
     unsigned ld_off[SEG_W];                    // lane's bytes relative to the tile's first row
 #pragma unroll
@@ -562,7 +570,7 @@ __global__ __launch_bounds__(bwdq::NT, 1) void bwd_dq_kernel(
         const unsigned kb = __builtin_amdgcn_readfirstlane(real ? lds0 + ((t - t_lo) % NSTAGE) * STAGE
                                                                 : lds0 + NSTAGE * STAGE);
         const unsigned segb = real ? 1024u : 0u;
-        const unsigned row0 = (unsigned)(real ? t * BC : 0) * kv_row_bytes;
+        const unsigned row0 = (unsigned)(real ? sweep_block(t, t_ulo, t_uhi, rev) * BC : 0) * kv_row_bytes;
 #pragma unroll
         for (int i = 0; i < SEG_W; ++i) {
             const int seg = wave * SEG_W + i;
@@ -632,7 +640,8 @@ __global__ __launch_bounds__(bwdq::NT, 1) void bwd_dq_kernel(
     const int tr0 = tr_r0 * 64 + ((tr_cl ^ dual_swz(tr_r0)) << 4) + ((tj & 1) << 3);
     const int tr1 = tr_r1 * 64 + ((tr_cl ^ dual_swz(tr_r1)) << 4) + ((tj & 1) << 3);
 
-    // one K/V tile: wait for its loads, start those of tile t + 2, then
+    // one K/V tile (sweep position t; masked positions are their own tile):
+    // wait for its loads, start those of position t + 2, then
     // S^T = K Q^T, dP^T = V dO^T (lane = query), dS^T, dQ^T += K^T dS^T
     auto tile = [&](int t, auto masked) {
         constexpr bool MASK = decltype(masked)::value;
@@ -812,10 +821,14 @@ hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const vo
     const dim3 grid((unsigned)(B * Hkv * nkb)), block(bwd::NT);
     const float sl2 = scale * kLog2e;
     const int delta_off = (int)((const char*)delta - (const char*)lse2);
-#define FA_BWD_LAUNCH(DD, CC, WW)                                                                    \
-    hipLaunchKernelGGL((bwd_dkdv_kernel<DD, CC, WW>), grid, block, 0, stream, Qp, Kp, Vp, dOp, lse2, \
-                       delta_off, dKp, dVp, H, G, N, win, Npad, scale, sl2, nkb)
     const bool narrow = causal && win < N;     // a window that hides keys
+#define FA_BWD_LAUNCH(DD, CC, WW)                                                                      \
+    do {                                                                                               \
+        const void* kf = (const void*)bwd_dkdv_kernel<DD, CC, WW>;                                     \
+        const Schedule sc = causal ? causal_schedule(kf, bwd::NT, nkb, d, N, narrow, stream) : Schedule{0, 1}; \
+        hipLaunchKernelGGL((bwd_dkdv_kernel<DD, CC, WW>), grid, block, 0, stream, Qp, Kp, Vp, dOp, lse2, \
+                           delta_off, dKp, dVp, H, G, N, win, Npad, scale, sl2, nkb, sc.gen, sc.group); \
+    } while (0)
     if (d == 128) {
         if (narrow) FA_BWD_LAUNCH(128, true, true);
         else if (causal) FA_BWD_LAUNCH(128, true, false);
@@ -848,14 +861,17 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void
     const bool stats = o != nullptr;
 #define FA_BWDQ_LAUNCH(DD, CC, WW)                                                                  \
     do {                                                                                            \
+        const void* kf = stats ? (const void*)bwd_dq_kernel<DD, CC, WW, true>                      \
+                               : (const void*)bwd_dq_kernel<DD, CC, WW, false>;                    \
+        const Schedule sc = causal ? causal_schedule(kf, bwdq::NT, nqb, d, N, narrow, stream) : Schedule{0, 1}; \
         if (stats)                                                                                  \
             hipLaunchKernelGGL((bwd_dq_kernel<DD, CC, WW, true>), grid, block, 0, stream, Qp, Kp,  \
                                Vp, dOp, Op, lse, lse2, delta, dQp, H, G, N, win, Npad, scale, sl2,  \
-                               nqb);                                                                \
+                               nqb, sc.gen, sc.group);                                              \
         else                                                                                        \
             hipLaunchKernelGGL((bwd_dq_kernel<DD, CC, WW, false>), grid, block, 0, stream, Qp, Kp, \
                                Vp, dOp, Op, lse, lse2, delta, dQp, H, G, N, win, Npad, scale, sl2,  \
-                               nqb);                                                                \
+                               nqb, sc.gen, sc.group);                                              \
     } while (0)
     if (d == 128) {
         if (narrow) FA_BWDQ_LAUNCH(128, true, true);

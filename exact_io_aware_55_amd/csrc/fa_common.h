@@ -96,14 +96,39 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
 // than index 0 (key blocks).  When every XCD's share is a whole number of
 // heads, the XCD takes its heads `group` at a time: the longest block of each
 // head of the group, then the next longest, and so on, so no long block
-// starts near the end of the grid.  Small groups keep the blocks running at
-// once on few heads, whose operand re-reads then stay in L2: at d = 128 pairs
-// of heads made the causal backward 4.7% faster than all heads at once and
-// cut the dK/dV kernel's L2 misses threefold at 16384 tokens.  At d = 64
-// pairs made the causal forward up to 12% slower, so there all heads go at
-// once.  Otherwise heads are taken one at a time, each longest block first.
+// starts near the end of the grid.  Otherwise heads are taken one at a time,
+// each longest block first.  The launcher picks `group` (causal_schedule):
+// one head at a time where a head's streamed operands exceed the L2, so
+// that a generation of workgroups (odd_generation) covers as much of one
+// head as it can; pairs of heads at d = 128 and all heads at d = 64 below
+// that, which measured fastest there (pairs made the d = 128 causal backward
+// 4.7% faster than all heads at once; at d = 64 pairs made the causal
+// forward up to 12% slower).  The FP8 forward uses causal_group.
 template <int D>
 constexpr int causal_group() { return D == 128 ? 2 : 1 << 20; }
+
+// Sweep direction of a causal workgroup.  A causal block's range of key (or
+// query) blocks depends on its index, so the workgroups an XCD runs at once
+// end at different times and their successors start one by one.  Ids on one
+// XCD (bid >> 3 = position in its sequence) start in generations of `gen`
+// workgroups, as many as the XCD holds at once: the first generation starts
+// together, the next one by one as the first ends, the third together again
+// when the second ends, and so on.  Workgroups that start together stay in
+// step if they sweep from the far end of their ranges toward the diagonal
+// (all read block 0, then 1, ...); workgroups that start one by one stay in
+// step if they sweep from the diagonal outward, because each starts as far
+// along the shared sweep as its range is shorter than its predecessor's.
+// Either way the workgroups of a head running at once read the same block at
+// about the same time, and the XCD's L2 serves the re-reads.  Result: odd
+// generation, i.e. started one by one (gen = 0: no alternation).
+__device__ __forceinline__ bool odd_generation(int bid, int gen) {
+    return gen > 0 && (((bid >> 3) / gen) & 1) != 0;
+}
+// Block visited at sweep position t: blocks [ulo, uhi) in reverse order when
+// rev is set, any other t as it is
+__device__ __forceinline__ int sweep_block(int t, int ulo, int uhi, bool rev) {
+    return rev && t >= ulo && t < uhi ? ulo + uhi - 1 - t : t;
+}
 __device__ __forceinline__ void order_blocks(int bid, int nblocks, int nb, bool causal, bool desc, int& bh,
                                              int& blk, int group) {
     int rank;

@@ -59,7 +59,7 @@ template <int D, bool CAUSAL, bool WIN>
 __global__ __launch_bounds__(fwd::NT, 1) void fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     __bf16* __restrict__ O, float* __restrict__ LSE, int H, int G, int N, int window, float scale_log2,
-    int nqb) {
+    int nqb, int gen, int group) {
     using namespace fwd;
     // keys per K/V block and blocks resident in the LDS ring: 128 keys in a
     // 2-stage ring at d = 128 (half the per-block barrier, load and loop work;
@@ -89,7 +89,7 @@ __global__ __launch_bounds__(fwd::NT, 1) void fwd_bf16_kernel(
 
     const int nblocks = gridDim.x;
     int bh, qb;                                // causal: longest query blocks first
-    order_blocks(blockIdx.x, nblocks, nqb, CAUSAL, true, bh, qb, causal_group<D>());
+    order_blocks(blockIdx.x, nblocks, nqb, CAUSAL, true, bh, qb, group);
     const int b = bh / H, h = bh - b * H;
     const int row_stride = H * D;              // elements between sequence rows (N*H*D < 2^31)
     const long head_off = ((long)b * N * H + h) * D;
@@ -117,6 +117,10 @@ __global__ __launch_bounds__(fwd::NT, 1) void fwd_bf16_kernel(
     const int t_lo = CAUSAL ? max(0, q0 - window + 1) / BC : 0;
     const int t_uhi = max(t_lo, min(N / BC, CAUSAL ? (q0 + 1) / BC : ntiles));
     const int t_ulo = CAUSAL ? min(t_uhi, max(t_lo, (max(0, q0 + BR - window) + BC - 1) / BC)) : 0;
+    // causal workgroups of an odd generation run their unmasked blocks from
+    // the diagonal down (position t visits block sweep_block(t)); the masked
+    // blocks and every other workgroup go in ascending order
+    const bool rev = CAUSAL && !WIN && odd_generation(blockIdx.x, gen);
 
     // Direct global -> LDS loads of one K/V block: each wave fills SEG_W 1 KB
     // segments of K and of V; lane i writes bytes [16 i, 16 i + 16) of its
@@ -136,7 +140,7 @@ __global__ __launch_bounds__(fwd::NT, 1) void fwd_bf16_kernel(
         const unsigned kb = __builtin_amdgcn_readfirstlane(real ? lds0 + ((t - t_lo) % NSTAGE) * STAGE
                                                                 : lds0 + NSTAGE * STAGE);
         const unsigned segb = real ? 1024u : 0u;
-        const unsigned row0 = (unsigned)(real ? t * BC : 0) * kv_row_bytes;
+        const unsigned row0 = (unsigned)(real ? sweep_block(t, t_ulo, t_uhi, rev) * BC : 0) * kv_row_bytes;
 #pragma unroll
         for (int i = 0; i < SEG_W; ++i) {
             const int seg = wave * SEG_W + i;
@@ -178,7 +182,8 @@ __global__ __launch_bounds__(fwd::NT, 1) void fwd_bf16_kernel(
     const int v_rd = TILE + tr_row * 64 + (((2 * (tr_g & 1) + ((tr_j & 3) >> 1)) ^ v_swz(tr_row)) << 4) +
                      ((tr_j & 1) << 3);
 
-    // One K/V block: wait for its loads (the next block may still be in
+    // One K/V block (sweep position t; masked positions are their own
+    // block): wait for its loads (the next block may still be in
     // flight), make every wave's part visible (the barrier also retires all
     // reads of block t - 1, whose stage the loads of block t + 2 refill), then
     // S^T = K Q^T, the online softmax and O^T += V^T P^T.
@@ -491,10 +496,13 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
     auto Vp = static_cast<const __bf16*>(v);
     auto Op = static_cast<__bf16*>(o);
     const int win = effective_window(window, N);
-    auto go = [&](auto kern) {
-        hipLaunchKernelGGL(kern, grid, block, 0, stream, Qp, Kp, Vp, Op, lse, H, G, N, win, sl2, nqb);
-    };
     const bool narrow = causal && win < N;
+    auto go = [&](auto kern) {
+        const Schedule sc = causal ? causal_schedule((const void*)kern, fwd::NT, nqb, d, N, narrow, stream)
+                                   : Schedule{0, 1};
+        hipLaunchKernelGGL(kern, grid, block, 0, stream, Qp, Kp, Vp, Op, lse, H, G, N, win, sl2, nqb, sc.gen,
+                           sc.group);
+    };
     if (d == 128) {
         if (!causal) go(fwd_bf16_kernel<128, false, false>);
         else narrow ? go(fwd_bf16_kernel<128, true, true>) : go(fwd_bf16_kernel<128, true, false>);

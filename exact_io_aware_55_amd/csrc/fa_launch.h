@@ -16,6 +16,22 @@ constexpr int kNoWindow = 1 << 30;
 // 32-bit window arithmetic (row + window, row - window) far from overflow
 // for any caller value up to INT_MAX.
 inline int effective_window(int window, int N) { return window > 0 && window < N ? window : kNoWindow; }
+// Launch order of a causal grid (order_blocks, odd_generation): `gen` is the
+// number of workgroups one XCD runs at once, from the kernel's occupancy and
+// the device's CU count, or 0 for no alternating sweeps (sliding windows,
+// whose blocks all have about the same range, and heads whose streamed
+// operands fit in one XCD's L2); `group` the number of heads an XCD takes
+// at a time.  kernel: the kernel's address; threads: its workgroup size; nb:
+// its blocks per head; d: head dimension; N: sequence length; window: a
+// sliding window narrower than N.  Host only; the occupancy is cached per
+// device and kernel.
+struct Schedule {
+    int gen;
+    int group;
+};
+Schedule causal_schedule(const void* kernel, int threads, int nb, int d, int N, bool window,
+                         hipStream_t stream);
+
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                            int H, int Hkv, int N, int d, float scale, bool causal, int window,
                            hipStream_t stream);

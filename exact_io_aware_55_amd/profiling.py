@@ -251,8 +251,8 @@ def scaling(copy_fetch, copy_write, out, B, H, d, runs):
         cells = [f"{byn[n][1] / 1e6:.1f} (x{byn[n][1] / byn[n][2]:.2f})" for n in ns]
         growth = [byn[ns[i]][1] / byn[ns[i - 1]][1] for i in range(1, len(ns))]
         worst = max(worst, *growth)
-        lines.append(f"| `{k}` | " + " | ".join(cells) + " | " + " | ".join(f"{g:.2f}" for g in growth) + " |")
-    tail = ["", f"Largest growth per doubling of N: {worst:.2f} (O(N d) traffic gives 2, traffic of "
+        lines.append(f"| `{k}` | " + " | ".join(cells) + " | " + " | ".join(f"{g:.3f}" for g in growth) + " |")
+    tail = ["", f"Largest growth per doubling of N: {worst:.3f} (O(N d) traffic gives 2, traffic of "
             "the N x N score matrix would give 4).  At the largest N the N x N bf16 score matrix of "
             f"all heads would be {B * H * ns[-1] ** 2 * 2 / 2 ** 30:.0f} GiB."]
     with open(out, "w") as fh:

@@ -48,9 +48,9 @@ def test_scaling_bytes_and_growth(tmp_path):
     text = out.read_text()
     fwd_row = next(line for line in text.splitlines() if line.startswith("| `fa::fwd_bf16"))
     # 1000 KiB read x 2 + 500 KiB written x 1 = 2500 KiB = 2.56 MB at N = 4096
-    assert "2.6 (x" in fwd_row and fwd_row.rstrip(" |").endswith("2.00 | 2.00")
+    assert "2.6 (x" in fwd_row and fwd_row.rstrip(" |").endswith("2.000 | 2.000")
     dkdv_row = next(line for line in text.splitlines() if line.startswith("| `fa::bwd_dkdv"))
-    assert dkdv_row.rstrip(" |").endswith("4.00 | 4.00")
+    assert dkdv_row.rstrip(" |").endswith("4.000 | 4.000")
 
 
 def test_traffic_table_and_json(tmp_path):
