@@ -120,9 +120,9 @@ def source_digest(*names):
 
 # kernel name -> (sources that define it, how its algorithmic work is counted)
 KERNELS = {
-    "fwd": ("fa_fwd.hip", "fa_common.h"),
-    "bwd_dkdv": ("fa_bwd.hip", "fa_common.h"),
-    "bwd_dq": ("fa_bwd.hip", "fa_common.h"),
+    "fwd": ("fa_fwd.hip", "fa_common.h", "fa_schedule.hip"),
+    "bwd_dkdv": ("fa_bwd.hip", "fa_common.h", "fa_schedule.hip"),
+    "bwd_dq": ("fa_bwd.hip", "fa_common.h", "fa_schedule.hip"),
 }
 
 

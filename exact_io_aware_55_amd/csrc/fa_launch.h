@@ -25,6 +25,10 @@ inline int effective_window(int window, int N) { return window > 0 && window < N
 // its blocks per head; d: head dimension; N: sequence length; window: a
 // sliding window narrower than N.  Host only; the occupancy is cached per
 // device and kernel.
+// Workgroups of `kernel` (with `threads` threads each) one XCD runs at once,
+// from its occupancy and the device's CU count (cached per device and
+// kernel); 0 if the runtime cannot say.
+int xcd_slots(const void* kernel, int threads, hipStream_t stream);
 struct Schedule {
     int gen;
     int group;

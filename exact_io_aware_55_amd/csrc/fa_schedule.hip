@@ -33,8 +33,9 @@ long l2_bytes(hipStream_t stream) {
     return 4l << 20;
 }
 
-// workgroups of `kernel` one XCD runs at once; 0 when the runtime cannot say
-int xcd_generation(const void* kernel, int threads, hipStream_t stream) {
+}  // namespace
+
+int xcd_slots(const void* kernel, int threads, hipStream_t stream) {
     int dev = 0;
     if (hipStreamGetDevice(stream, &dev) != hipSuccess) {
         (void)hipGetLastError();
@@ -56,7 +57,6 @@ int xcd_generation(const void* kernel, int threads, hipStream_t stream) {
     g_cache.push_back(Entry{dev, kernel, threads, gen});
     return gen;
 }
-}  // namespace
 
 Schedule causal_schedule(const void* kernel, int threads, int nb, int d, int N, bool window,
                          hipStream_t stream) {
@@ -71,7 +71,7 @@ Schedule causal_schedule(const void* kernel, int threads, int nb, int d, int N, 
     // slower in the backward; past that the L2 cannot hold them and the
     // generations' sweeps must line up.
     if ((long)N * d * 4 < (long)l2_bytes(stream)) return plain;
-    const int gen = xcd_generation(kernel, threads, stream);
+    const int gen = xcd_slots(kernel, threads, stream);
     if (gen <= 0) return plain;
     // enough heads that one generation holds the blocks of whole heads
     const int group = d == 64 ? plain.group : nb >= gen ? 1 : (gen + nb - 1) / nb;

@@ -36,10 +36,10 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 # bench.py stage -> (kernel symbol prefix, sources that define it)
 STAGES = {
-    "fwd": ("fa::fwd_bf16_kernel", ("fa_fwd.hip", "fa_common.h")),
+    "fwd": ("fa::fwd_bf16_kernel", ("fa_fwd.hip", "fa_common.h", "fa_schedule.hip")),
     "bwd_preprocess": ("fa::bwd_pre_kernel", ("fa_bwd.hip", "fa_common.h")),
-    "bwd_dkdv": ("fa::bwd_dkdv_kernel", ("fa_bwd.hip", "fa_common.h")),
-    "bwd_dq": ("fa::bwd_dq_kernel", ("fa_bwd.hip", "fa_common.h")),
+    "bwd_dkdv": ("fa::bwd_dkdv_kernel", ("fa_bwd.hip", "fa_common.h", "fa_schedule.hip")),
+    "bwd_dq": ("fa::bwd_dq_kernel", ("fa_bwd.hip", "fa_common.h", "fa_schedule.hip")),
 }
 
 

@@ -67,8 +67,20 @@ def test_traffic_table_and_json(tmp_path):
     table = json.load(open(out.parent / "traffic.json"))
     rec = table["fwd@b1_h1_n1024_d128_causal_fwd_bwd"]
     assert rec["bytes_per_launch"] == 1000 * 2 * 1024 + 400 * 1024
-    assert rec["source_sha"] == profiling.source_digest(("fa_fwd.hip", "fa_common.h"))
+    assert rec["source_sha"] == profiling.source_digest(("fa_fwd.hip", "fa_common.h", "fa_schedule.hip"))
     assert len(lines) == 1 and "fwd_bf16_kernel" in lines[0]
+
+
+def test_digest_sources_agree_with_bench():
+    """bench.py reports a stored traffic figure only while the digest of the
+    kernel's sources matches; the two files must hash the same sources."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(profiling.ROOT, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    for stage, srcs in bench.KERNELS.items():
+        assert tuple(profiling.STAGES[stage][1]) == tuple(srcs), stage
+        assert bench.source_digest(*srcs) == profiling.source_digest(srcs)
 
 
 def test_compulsory_bytes_forward():
