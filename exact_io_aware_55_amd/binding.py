@@ -16,6 +16,7 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfa.so")
+SYNC_LIB_PATH = os.path.join(_HERE, "libfa_sync.so")   # synchronisation check build
 
 EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_bwd_workspace_size", "fa_bwd", "fa_bwd_preprocess",
            "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_dq_stats", "fa_fwd_gqa", "fa_bwd_gqa", "fa_fwd_window",
@@ -35,8 +36,15 @@ _lib = None
 def load(path: str = LIB_PATH):
     """Load libfa.so once and declare the C signatures; raises if absent."""
     global _lib
-    if _lib is not None:
-        return _lib
+    if _lib is None:
+        _lib = open_library(path)
+    return _lib
+
+
+def open_library(path: str):
+    """A library with the C ABI of include/fa.h (libfa.so or its
+    synchronisation check build libfa_sync.so), signatures declared; raises
+    if absent.  Not cached: load() keeps the one the functions below use."""
     if not os.path.exists(path):
         raise RuntimeError(
             f"{path} not found: build it with `python -m exact_io_aware_55_amd.build` "
@@ -79,7 +87,6 @@ def load(path: str = LIB_PATH):
     lib.fa_probe_mfma.restype = i
     lib.fa_strerror.argtypes = [i]
     lib.fa_strerror.restype = ctypes.c_char_p
-    _lib = lib
     return lib
 
 

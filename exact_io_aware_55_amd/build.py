@@ -37,30 +37,49 @@ _VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 EXTRA = {"fa_bwd.hip": _VGPR_FORM, "fa_calib.hip": _VGPR_FORM}
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+# The synchronisation check build: the same sources with -DFA_DEBUG_SYNC,
+# which makes every pipelined kernel wait for all memory operations and meet
+# at a barrier at each block or step and before each LDS ring refill.  Its
+# outputs must equal libfa.so's bit for bit (a GPU test compares them).
+SYNC_LIB = os.path.join(PKG, "libfa_sync.so")
+VARIANTS = {LIB: ("", []), SYNC_LIB: ("sync", ["-DFA_DEBUG_SYNC"])}
+
+
+def _compile(job) -> str:
+    src, sub, defines = job
+    out_dir = os.path.join(BUILD, sub) if sub else BUILD
+    obj = os.path.join(out_dir, os.path.basename(src) + ".o")
     extra = EXTRA.get(os.path.basename(src), [])
-    cmd = [HIPCC, *FLAGS, *extra, "-I", os.path.join(ROOT, "include"), "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *extra, *defines, "-I", os.path.join(ROOT, "include"), "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{res.stdout}\n{res.stderr}")
     return obj
 
 
-def build_library(verbose: bool = False) -> str:
-    """Compile every csrc/*.hip and link libfa.so; returns the library path."""
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB)
-    if verbose:
-        print(f"built {LIB} from {len(srcs)} sources")
+    os.replace(tmp, lib)
+
+
+def build_library(verbose: bool = False) -> str:
+    """Compile every csrc/*.hip and link libfa.so and the synchronisation
+    check build libfa_sync.so; returns the path of libfa.so."""
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    jobs = []
+    for lib, (sub, defines) in VARIANTS.items():
+        os.makedirs(os.path.join(BUILD, sub) if sub else BUILD, exist_ok=True)
+        jobs += [(src, sub, defines) for src in srcs]
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
+        objs = list(ex.map(_compile, jobs))
+    for n, lib in enumerate(VARIANTS):
+        _link(objs[n * len(srcs):(n + 1) * len(srcs)], lib)
+        if verbose:
+            print(f"built {lib} from {len(srcs)} sources")
     return LIB
 
 

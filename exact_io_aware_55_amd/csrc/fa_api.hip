@@ -24,9 +24,12 @@ int check_shape(int B, int H, int N, int d, float scale) {
     if (B < 1 || H < 1 || N < 1) return FA_ERR_INVALID_ARG;
     if (!isfinite(scale)) return FA_ERR_INVALID_ARG;
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
-    // per-lane byte offsets within one batch's [N, H, d] rows stay below 2^31
-    if ((long long)N * H * d >= (1LL << 30)) return FA_ERR_UNSUPPORTED;
+    // per-lane byte offsets within one batch's [N, H, d] rows stay below 2^31:
+    // N * H * d < 2^30, tested as N * H < 2^30 / d (d divides 2^30), so no
+    // product can overflow (N, H < 2^31, so N * H < 2^62)
+    if ((long long)N * H >= (1LL << 30) / d) return FA_ERR_UNSUPPORTED;
     // grid size: B * H * ceil(N / 64) workgroups must fit a 32-bit grid
+    // (H * ceil(N / 64) < 2^24 after the test above, so this fits 64 bits)
     if ((long long)B * H * ((N + 63) / 64) >= (1LL << 31)) return FA_ERR_UNSUPPORTED;
     return FA_OK;
 }
@@ -330,6 +333,8 @@ int fa_calibrate_mfma(float* out, int n_workgroups, int waves_per_workgroup, int
                       hipStream_t stream) {
     if (!out || n_workgroups < 1 || waves_per_workgroup < 1 || waves_per_workgroup > 4 || iters < 1)
         return FA_ERR_INVALID_ARG;
+    // one checksum per thread at a 32-bit index
+    if (n_workgroups > (1 << 22)) return FA_ERR_UNSUPPORTED;
     if (mode < 0 || mode > 4) return FA_ERR_INVALID_ARG;
     if (reinterpret_cast<uintptr_t>(out) & 3u) return FA_ERR_MISALIGNED;
     if (fa::launch_calib_mfma(out, n_workgroups, waves_per_workgroup, iters, mode, stream) !=
@@ -341,7 +346,10 @@ int fa_calibrate_mfma(float* out, int n_workgroups, int waves_per_workgroup, int
 int fa_probe_mfma(int fp8, const void* a, const void* b, float* c, int n_tiles, int k, hipStream_t stream) {
     if (!a || !b || !c || n_tiles < 1 || k < 1 || (fp8 != 0 && fp8 != 1)) return FA_ERR_INVALID_ARG;
     if (k % (fp8 ? 64 : 16) != 0) return FA_ERR_INVALID_ARG;
-    if ((long long)n_tiles * 32 * k * (fp8 ? 1 : 2) >= (1LL << 31)) return FA_ERR_UNSUPPORTED;
+    // A and B hold n_tiles * 32 * k elements at 32-bit offsets; the row
+    // bytes are bounded first, so the total cannot overflow 64 bits
+    const long long row = 32LL * k * (fp8 ? 1 : 2);
+    if (row >= (1LL << 31) || n_tiles * row >= (1LL << 31)) return FA_ERR_UNSUPPORTED;
     if (!aligned16(a) || !aligned16(b) || (reinterpret_cast<uintptr_t>(c) & 3u)) return FA_ERR_MISALIGNED;
     if (fa::launch_probe_mfma(fp8, a, b, c, n_tiles, k, stream) != hipSuccess) return FA_ERR_LAUNCH;
     return FA_OK;

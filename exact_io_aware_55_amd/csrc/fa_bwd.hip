@@ -306,6 +306,7 @@ __global__ __launch_bounds__(bwd::NT, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
             FA_WAIT_VMCNT(DMA_W);
             __builtin_amdgcn_s_barrier();
         }
+        FA_SYNC_POINT();
 
         int g_unused;
         const int i0 = step_of(it, g_unused) * BR;
@@ -442,6 +443,7 @@ __global__ __launch_bounds__(bwd::NT, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
                 constexpr int uu = decltype(u)::value;
                 issue_reads(flag_int<uu + PF>{});
                 // the direct loads of step it + 2, one every other unit
+                if constexpr (uu == 1) FA_SYNC_POINT();
                 if constexpr (uu % 2 == 1 && uu / 2 < DMA_W) issue_load(next, uu / 2);
                 softmax_chunk(u);
                 products(u);
@@ -660,6 +662,7 @@ __global__ __launch_bounds__(bwdq::NT, 1) void bwd_dq_kernel(
             FA_WAIT_VMCNT(2 * SEG_W);
             __builtin_amdgcn_s_barrier();
         }
+        FA_SYNC_POINT();
         if constexpr (MASK) issue_tile(t + 2);
 
         const int j0 = t * BC;
@@ -708,7 +711,10 @@ __global__ __launch_bounds__(bwdq::NT, 1) void bwd_dq_kernel(
         // unmasked tiles start the loads of tile t + 2 here, behind the S^T and
         // dP^T reads, rather than as a burst at the top (masked tiles may
         // return early, so they issue first)
-        if constexpr (!MASK) issue_tile(t + 2);
+        if constexpr (!MASK) {
+            FA_SYNC_POINT();
+            issue_tile(t + 2);
+        }
         // dS^T = P^T (dP^T - D), P^T = exp2(S^T scale log2e - LSE log2e); on
         // diagonal tiles keys after the lane's query get exp2(-inf) = 0
         u32x4 dsb[4];

@@ -198,6 +198,24 @@ __device__ __forceinline__ void dma16(const void* base, unsigned offset, unsigne
 // s_waitcnt vmcnt(n) only (expcnt and lgkmcnt left alone), n <= 15
 #define FA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | (n))
 
+// Synchronisation check build (compiled with -DFA_DEBUG_SYNC, the library
+// libfa_sync.so): at the start of every K/V block or query step and before
+// every refill of an LDS ring stage, each wave waits for all of its memory
+// operations and meets the other waves at a barrier.  The pipelines then run
+// without any overlap of loads and reads; outputs must equal the normal
+// build's bit for bit, so a difference shows a missing wait or barrier.
+#ifdef FA_DEBUG_SYNC
+#define FA_SYNC_POINT()                    \
+    do {                                   \
+        __builtin_amdgcn_s_waitcnt(0);     \
+        __builtin_amdgcn_s_barrier();      \
+    } while (0)
+#else
+#define FA_SYNC_POINT() \
+    do {                \
+    } while (0)
+#endif
+
 // Packs two floats into one dword of two bf16 (round to nearest even).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));

@@ -191,6 +191,7 @@ __global__ __launch_bounds__(fwd::NT, 1) void fwd_bf16_kernel(
         constexpr bool MASK = decltype(mask_tag)::value;
         FA_WAIT_VMCNT((NSTAGE - 2) * 2 * SEG_W);
         __builtin_amdgcn_s_barrier();
+        FA_SYNC_POINT();
         if constexpr (MASK) issue_tile(t + NSTAGE - 1);  // masked blocks may return early
 
         const int j0 = t * BC;
@@ -228,7 +229,10 @@ __global__ __launch_bounds__(fwd::NT, 1) void fwd_bf16_kernel(
         }
         // unmasked blocks start the loads of block t + NSTAGE - 1 here,
         // behind the K reads, rather than as a burst at the top
-        if constexpr (!MASK) issue_tile(t + NSTAGE - 1);
+        if constexpr (!MASK) {
+            FA_SYNC_POINT();
+            issue_tile(t + NSTAGE - 1);
+        }
         // keep the V reads below the softmax (register pressure)
         __builtin_amdgcn_sched_barrier(0);
         // x = scale log2(e) s - m_sub in place, the exponent of P against the

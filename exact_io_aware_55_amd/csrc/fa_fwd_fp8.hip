@@ -201,6 +201,7 @@ __global__ __launch_bounds__(fwd8::NT, 1) void fwd_fp8_kernel(
         constexpr bool MASK = decltype(mask_tag)::value;
         FA_WAIT_VMCNT(NL);
         __builtin_amdgcn_s_barrier();
+        FA_SYNC_POINT();
         if constexpr (MASK) issue_tile(t + 2);
 
         const int j0 = t * BC;
@@ -222,7 +223,10 @@ __global__ __launch_bounds__(fwd8::NT, 1) void fwd_fp8_kernel(
                 s[kt] = mfma_fp8(join16(lds_read_u128(kb0 + o), lds_read_u128(kb1 + o)), qreg[m], s[kt]);
             }
         }
-        if constexpr (!MASK) issue_tile(t + 2);
+        if constexpr (!MASK) {
+            FA_SYNC_POINT();
+            issue_tile(t + 2);
+        }
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (MASK) {
             const int lim_n = N - j0 - 4 * hl;

@@ -233,7 +233,8 @@ size_t fa_bwd_noalloc_max_workspace(void);
  * modes 0 and 1 are the chip's dense bf16 rate with and without operand
  * switching (the second is what real data sees); the MFMA-busy counter of
  * mode 0 checks the busy-cycle normalisation.  INVALID_ARG for out null or
- * counts or mode out of range; MISALIGNED; LAUNCH. */
+ * counts or mode out of range; UNSUPPORTED for more than 2^22 workgroups;
+ * MISALIGNED; LAUNCH. */
 int fa_calibrate_mfma(float* out, int n_workgroups, int waves_per_workgroup, int iters, int mode,
                       hipStream_t stream);
 

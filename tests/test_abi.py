@@ -35,6 +35,15 @@ def test_library_exports_every_declared_symbol(lib):
         assert hasattr(lib, name), name
 
 
+def test_sync_check_build_exports_every_declared_symbol():
+    """The synchronisation check build (libfa_sync.so) has the same ABI and
+    rejects invalid arguments the same way."""
+    sync = binding.open_library(binding.SYNC_LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(sync, name), name
+    assert _fwd(sync, ptrs=(0,) + (FAKE,) * 4) == binding.FA_ERR_INVALID_ARG
+
+
 def test_strerror(lib):
     for code in (0, -1, -2, -3, -4, -5):
         assert len(binding.strerror(code)) > 3
@@ -62,6 +71,16 @@ def test_forward_argument_errors(lib, fn):
     assert _fwd(lib, fn, N=1 << 20, H=64, d=128) == binding.FA_ERR_UNSUPPORTED
     # the first size past the limit: N * H * d = 2^30 exactly
     assert _fwd(lib, fn, N=1 << 20, H=8, d=128) == binding.FA_ERR_UNSUPPORTED
+    # sizes whose products wrap 64 bits if formed in one expression
+    # (2^30 * 2^30 * 128 = 2^67): still rejected, never launched
+    assert _fwd(lib, fn, B=1 << 30, H=1 << 30, N=1 << 30, d=128) == binding.FA_ERR_UNSUPPORTED
+    assert _fwd(lib, fn, B=(1 << 31) - 1, H=(1 << 31) - 1, N=(1 << 31) - 1, d=64) == binding.FA_ERR_UNSUPPORTED
+    # the largest accepted N * H at d = 64 and at d = 128 pass the size test
+    # (the shape is checked before alignment, so a misaligned q reports that)
+    mis = (FAKE + 8,) + (FAKE,) * 4
+    assert _fwd(lib, fn, N=(1 << 24) - 1, H=1, d=64, ptrs=mis) == binding.FA_ERR_MISALIGNED
+    assert _fwd(lib, fn, N=1 << 24, H=1, d=64, ptrs=mis) == binding.FA_ERR_UNSUPPORTED
+    assert _fwd(lib, fn, N=(1 << 23) - 1, H=1, d=128, ptrs=mis) == binding.FA_ERR_MISALIGNED
     for i in range(5):
         ptrs = [FAKE] * 5
         ptrs[i] = FAKE + 8
@@ -221,6 +240,7 @@ def test_calibration_argument_errors(lib):
                                      (4, 4, 10, -1), (4, 4, 10, 5)):
         assert f(V(FAKE), n_wg, waves, iters, mode, None) == binding.FA_ERR_INVALID_ARG
     assert f(V(FAKE + 2), 4, 4, 10, 0, None) == binding.FA_ERR_MISALIGNED
+    assert f(V(FAKE), (1 << 22) + 1, 4, 10, 0, None) == binding.FA_ERR_UNSUPPORTED
 
 
 def test_probe_argument_errors(lib):
@@ -235,5 +255,8 @@ def test_probe_argument_errors(lib):
     assert f(0, *ok, 1, 24, None) == binding.FA_ERR_INVALID_ARG      # bf16: k a multiple of 16
     assert f(1, *ok, 1, 96, None) == binding.FA_ERR_INVALID_ARG      # fp8: k a multiple of 64
     assert f(1, *ok, 1 << 16, 1 << 16, None) == binding.FA_ERR_UNSUPPORTED
+    # products that would wrap 64 bits if formed in one expression
+    assert f(1, *ok, 1 << 30, 1 << 30, None) == binding.FA_ERR_UNSUPPORTED
+    assert f(0, *ok, (1 << 31) - 1, 1 << 30, None) == binding.FA_ERR_UNSUPPORTED
     assert f(0, V(FAKE + 8), V(FAKE), V(FAKE), 1, 16, None) == binding.FA_ERR_MISALIGNED
     assert f(0, V(FAKE), V(FAKE), V(FAKE + 2), 1, 16, None) == binding.FA_ERR_MISALIGNED
