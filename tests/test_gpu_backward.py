@@ -207,7 +207,8 @@ def test_bwd_sweep_n16384(gpu_lib, d):
 
 @pytest.mark.parametrize("N,d,H,heads", [(8192, 128, 32, [(0, 0), (0, 13), (0, 31)]),
                                          (16384, 128, 32, [(0, 17)]),
-                                         (16384, 64, 8, [(0, 5)])])
+                                         (16384, 64, 8, [(0, 5)]),
+                                         (9000, 128, 4, [(0, 2)])])
 def test_bwd_long_causal_alternating_sweeps(gpu_lib, N, d, H, heads):
     """Causal, B=1, at sizes where a head's streamed operands (two N x d
     bf16 tensors) no longer fit in one XCD's 4 MiB L2: the launch order then

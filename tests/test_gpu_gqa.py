@@ -81,6 +81,15 @@ def test_gqa_backward_full_size_group(gpu_lib):
     check_bwd(gpu_lib, 1, 2048, 64, 8, 128, True, seed=901, groups=[(0, 5)])
 
 
+def test_gqa_backward_long_causal_alternating_sweeps(gpu_lib):
+    """N = 8192, d = 128 causal: a head's K/V exceed one XCD's L2, so the
+    launch order reverses every other generation; the key-block kernel then
+    walks the query blocks of all four heads of a group in reverse order.
+    One K/V group (dK, dV summed over its heads) by the parity rule."""
+    print("\n[gqa bwd] B1 N8192 H8 Hkv2 d128 causal", flush=True)
+    check_bwd(gpu_lib, 1, 8192, 8, 2, 128, True, seed=902, groups=[(0, 1)])
+
+
 def test_gqa_bad_group_count_is_rejected(gpu_lib):
     x = make(1, 64, 6, 3, 64, seed=1)
     q = x["q"].to(DEV)
