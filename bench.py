@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--mfma-calibration", action="store_true",
                     help="run only the matrix-core calibration kernel (pure bf16 MFMA, and with 2 or "
                          "4 vector instructions per MFMA) and print its sustained rates")
+    ap.add_argument("--fp8-forward", action="store_true",
+                    help="run only the FP8 forward workloads (E4M3, the c2 and long causal shapes) "
+                         "and print their rates")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device-to-device copy of 1 GiB (3 times), the "
                          "reference for scaling HBM byte counters")
@@ -369,6 +372,10 @@ def main():
     if args.mfma_calibration:
         print(json.dumps({"mfma_calibration": mfma_calibration(torch, binding),
                           "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}), flush=True)
+        return
+    if args.fp8_forward:
+        print(json.dumps({"fp8_forward": fp8_workloads(torch, binding, inputs, workloads, args.seed),
+                          "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s"}), flush=True)
         return
     if args.sweep:
         rows = shape_sweep(torch, binding, inputs, workloads, args.seed)

@@ -8,9 +8,9 @@ summary::
 
     python -m exact_io_aware_55_amd.profiling trace DIR OUT.md TITLE COMMAND
     python -m exact_io_aware_55_amd.profiling traffic FETCH WRITE COPY_FETCH COPY_WRITE OUT.md WORKLOAD
-    python -m exact_io_aware_55_amd.profiling counters MFMA_DIR LDS_DIR TRACE_DIR OUT.md WORKLOAD
+    python -m exact_io_aware_55_amd.profiling counters MFMA_DIR LDS_DIR TRACE_DIR OUT.md WORKLOAD [BENCH_ARGS]
     python -m exact_io_aware_55_amd.profiling scaling COPY_FETCH COPY_WRITE OUT.md B H d N:FETCH:WRITE ...
-    python -m exact_io_aware_55_amd.profiling valu VALU_DIR TRACE_DIR OUT.md WORKLOAD
+    python -m exact_io_aware_55_amd.profiling valu VALU_DIR TRACE_DIR OUT.md WORKLOAD [BENCH_ARGS]
     python -m exact_io_aware_55_amd.profiling calibration RATES.json MFMA_DIR OUT.md
 
 ``DIR`` holds a ``--kernel-trace --stats`` run (``*_kernel_stats.csv``); the
@@ -144,7 +144,12 @@ def _trace_ns(folder):
     return {_short(r["Name"]): float(r["AverageNs"]) for r in rows}
 
 
-def counters(mfma_dir, lds_dir, trace_dir, out, workload):
+HEADLINE_ARGS = "--steps 2 --warmup 1 --no-naive --no-cpu --no-extra"
+
+
+def counters(mfma_dir, lds_dir, trace_dir, out, workload, bench_args=HEADLINE_ARGS):
+    """Matrix-core busy cycles and bf16 MFMA operations, LDS conflicts and
+    activity per kernel; bench_args are the bench.py arguments of the runs."""
     m, l = _counter_rows(mfma_dir), _counter_rows(lds_dir)
     tns = _trace_ns(trace_dir)
     xcc, cus, simds = _agent(mfma_dir)
@@ -154,12 +159,12 @@ def counters(mfma_dir, lds_dir, trace_dir, out, workload):
              "that receives the profiler output):", "", "```",
              "rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_BUSY_CU_CYCLES "
              "GRBM_GUI_ACTIVE --output-format csv -d $OUT/pmc_mfma -o bench -- "
-             "python3 $REPO/bench.py --steps 2 --warmup 1 --no-naive --no-cpu --no-extra",
+             f"python3 $REPO/bench.py {bench_args}",
              "rocprofv3 --pmc SQ_LDS_BANK_CONFLICT SQ_LDS_ADDR_CONFLICT SQ_LDS_IDX_ACTIVE SQ_INSTS_LDS "
              "SQ_BUSY_CU_CYCLES --output-format csv -d $OUT/pmc_lds -o bench -- "
-             "python3 $REPO/bench.py --steps 2 --warmup 1 --no-naive --no-cpu --no-extra",
+             f"python3 $REPO/bench.py {bench_args}",
              "python -m exact_io_aware_55_amd.profiling counters $OUT/pmc_mfma $OUT/pmc_lds "
-             f"$OUT/prof profiles/<this file> {workload}",
+             f"$OUT/prof profiles/<this file> {workload}" + ("" if bench_args == HEADLINE_ARGS else f" '{bench_args}'"),
              "```", "",
              f"Derived columns (the GPU reports {xcc} XCDs, {cus} CUs, {simds} SIMDs per CU):",
              "- clock = GRBM_GUI_ACTIVE / XCDs / launch duration, the duration taken from the "
@@ -174,6 +179,8 @@ def counters(mfma_dir, lds_dir, trace_dir, out, workload):
              "LDS address conflicts | LDS instructions (M) | LDS active |",
              "|---|---|---|---|---|---|---|---|---|"]
     for k, c in m.items():
+        if not c.get("SQ_VALU_MFMA_BUSY_CYCLES"):
+            continue                           # no matrix-core work (copies, fills)
         grbm = c.get("GRBM_GUI_ACTIVE", 0.0) / xcc
         ns = tns.get(k, c["_ns"])
         clock = grbm / ns if ns else 0.0
@@ -185,6 +192,10 @@ def counters(mfma_dir, lds_dir, trace_dir, out, workload):
                      f"{d.get('SQ_LDS_BANK_CONFLICT', float('nan')):.0f} | "
                      f"{d.get('SQ_LDS_ADDR_CONFLICT', float('nan')):.0f} | "
                      f"{d.get('SQ_INSTS_LDS', 0.0) / 1e6:.1f} | {100 * act:.0f}% |")
+    if any("fp8" in k for k in m):
+        lines += ["", "The flops column counts bf16 MFMA operations only: the profiler exposes no "
+                  "fp8 MFMA-operation counter on this chip (its MFMA-operation counters are F16, BF16, "
+                  "F32 and F64), so the fp8 kernels read 0 there; their MFMA busy is counted."]
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
 
@@ -264,7 +275,7 @@ VALU_COUNTERS = ("SQ_INSTS_VALU SQ_INSTS_VALU_TRANS_F32 SQ_INSTS_MFMA SQ_VALU_MF
                  "SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_LDS SQ_INSTS_LDS GRBM_GUI_ACTIVE")
 
 
-def valu(valu_dir, trace_dir, out, workload):
+def valu(valu_dir, trace_dir, out, workload, bench_args=HEADLINE_ARGS):
     """Vector and transcendental instructions per MFMA, co-execution of the
     vector unit with the matrix core, and wave waiting, per kernel."""
     c_all = _counter_rows(valu_dir)
@@ -275,9 +286,9 @@ def valu(valu_dir, trace_dir, out, workload):
              "`cd /tmp && export TMPDIR=/tmp`; `$REPO` is the repository root, `$OUT` the folder "
              "that receives the profiler output):", "", "```",
              f"rocprofv3 --pmc {VALU_COUNTERS} --output-format csv -d $OUT/pmc_valu -o bench -- "
-             "python3 $REPO/bench.py --steps 2 --warmup 1 --no-naive --no-cpu --no-extra",
+             f"python3 $REPO/bench.py {bench_args}",
              f"python -m exact_io_aware_55_amd.profiling valu $OUT/pmc_valu $OUT/prof profiles/<this file> "
-             f"{workload}", "```", "",
+             f"{workload}" + ("" if bench_args == HEADLINE_ARGS else f" '{bench_args}'"), "```", "",
              "Derived columns (per launch; SQ_INSTS_VALU counts the MFMA instructions too, so vector "
              "instructions = SQ_INSTS_VALU - SQ_INSTS_MFMA; the SQ_WAVE_CYCLES and SQ_WAIT_ANY counters "
              "count in units of 4 cycles, which cancels in their ratio):",
@@ -375,7 +386,7 @@ def main(argv):
     if len(argv) >= 5 and argv[0] == "trace":
         trace(argv[1], argv[2], argv[3], argv[4])
     elif len(argv) >= 6 and argv[0] == "counters":
-        counters(argv[1], argv[2], argv[3], argv[4], argv[5])
+        counters(argv[1], argv[2], argv[3], argv[4], argv[5], *argv[6:7])
     elif len(argv) >= 8 and argv[0] == "scaling":
         runs = []
         for spec in argv[7:]:
@@ -383,7 +394,7 @@ def main(argv):
             runs.append((int(n), fdir, wdir))
         scaling(argv[1], argv[2], argv[3], int(argv[4]), int(argv[5]), int(argv[6]), runs)
     elif len(argv) >= 5 and argv[0] == "valu":
-        valu(argv[1], argv[2], argv[3], argv[4])
+        valu(argv[1], argv[2], argv[3], argv[4], *argv[5:6])
     elif len(argv) >= 4 and argv[0] == "calibration":
         calibration(argv[1], argv[2], argv[3])
     elif len(argv) >= 7 and argv[0] == "traffic":
