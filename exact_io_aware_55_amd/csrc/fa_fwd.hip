@@ -23,10 +23,11 @@
 //  * exponentials are v_exp_f32 (base 2) with scale * log2(e) folded into one
 //    FMA per score, which turns S^T in place into the exponents
 //    x = scale log2(e) s - m (masked keys: -inf).
-//  * the running maximum is raised lazily: at d = 128 the exponentials run
-//    against it with no block maximum, and a block sum that grows too large
-//    sends the wave through a rescaling slow path; at d = 64 the block
-//    maximum comes first and only a large rise rescales.
+//  * the running maximum is raised lazily: the exponentials run against it
+//    with no block maximum, and a block sum that grows too large sends the
+//    wave through a rescaling slow path.  At d = 64 the kernel is held to 128
+//    registers per wave, so four waves share each SIMD (two workgroups per
+//    CU); the few values that do not fit are spilled outside the block loop.
 #include <type_traits>
 
 #include "fa_common.h"
@@ -56,7 +57,7 @@ __device__ __forceinline__ int v_swz(int row) { return ((row >> 1) & 1) << 1; }
 // WIN: a sliding window narrower than N (causal only); without it the
 // causal mask is one compare per score
 template <int D, bool CAUSAL, bool WIN>
-__global__ __launch_bounds__(fwd::NT, 1) void fwd_bf16_kernel(
+__global__ __launch_bounds__(fwd::NT, D == 64 ? 4 : 1) void fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     __bf16* __restrict__ O, float* __restrict__ LSE, int H, int G, int N, int window, float scale_log2,
     int nqb, int gen, int group) {
@@ -312,28 +313,17 @@ __global__ __launch_bounds__(fwd::NT, 1) void fwd_bf16_kernel(
                 for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
             return halves_max(mx);
         };
-        if constexpr (D == 128) {
-            // Exponentials first, against the running maximum.  A lane whose
-            // block sum exceeds 2^16, or whose row has no maximum yet, sends
-            // the wave through the slow path (block maximum, rescale,
-            // exponentials again).  A lane sums BC / 2 values of its query,
-            // so its sum passes 2^16 only through an x above 8: the slow path
-            // always raises the maximum, and on the fast path P < 2^16 keeps
-            // P, l and O far from the fp32 range.
-            exps();
-            if (__builtin_expect(
-                    __builtin_amdgcn_ballot_w64(!(ls0 + ls1 <= 65536.f) || m_run == -INFINITY) != 0, 0)) {
-                raise(block_max());
-                exps();
-            }
-        } else {
-            // Block maximum first; the running maximum is raised only when the
-            // block's exceeds it by more than 8 (log2 units), so P < 2^8.  At
-            // d = 64 a block has a quarter of the products, too few to hide a
-            // branch that waits for the row sum.
-            const float mx = block_max();
-            if (__builtin_expect(__builtin_amdgcn_ballot_w64(mx > 8.f || m_run == -INFINITY) != 0, 0))
-                raise(mx);
+        // Exponentials first, against the running maximum.  A lane whose
+        // block sum exceeds 2^16, or whose row has no maximum yet, sends the
+        // wave through the slow path (block maximum, rescale, exponentials
+        // again).  A lane sums BC / 2 <= 64 values of its query, so its sum
+        // passes 2^16 only through an x above 8: the slow path always raises
+        // the maximum, and on the fast path P < 2^16 keeps P, l and O far
+        // from the fp32 range.
+        exps();
+        if (__builtin_expect(
+                __builtin_amdgcn_ballot_w64(!(ls0 + ls1 <= 65536.f) || m_run == -INFINITY) != 0, 0)) {
+            raise(block_max());
             exps();
         }
         l_run += ls0 + ls1;
