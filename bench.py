@@ -58,6 +58,9 @@ def parse():
     ap.add_argument("--fp8-forward", action="store_true",
                     help="run only the FP8 forward workloads (E4M3, the c2 and long causal shapes) "
                          "and print their rates")
+    ap.add_argument("--torch-sdpa-reference", action="store_true",
+                    help="run only torch's scaled_dot_product_attention (flash and memory-efficient "
+                         "backends) at --B/--H/--N/--d, both masks, as a reference beside the kernels")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device-to-device copy of 1 GiB (3 times), the "
                          "reference for scaling HBM byte counters")
@@ -86,6 +89,38 @@ def copy_calibration():
 MFMA_CALIBRATION = [("const_w2", 512, 0), ("random_w2", 512, 1), ("random_valu2_w2", 512, 2),
                     ("random_valu4_w2", 512, 3), ("random_lds_w2", 512, 4), ("random_w1", 256, 1),
                     ("const_w1", 256, 0)]
+
+
+def torch_sdpa_reference(torch, B, H, N, d, seed):
+    """torch's own scaled_dot_product_attention on the same shape, with each
+    fused backend this build offers (flash, memory-efficient), forward alone
+    and forward + backward, both masks: a reference from a production
+    library on the same GPU, not part of the measured path."""
+    import torch.nn.functional as F
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+
+    g = torch.Generator(device="cuda:0").manual_seed(seed)
+    shape = (B, H, N, d)
+    q, k, v, do = (torch.randn(shape, generator=g, device="cuda:0", dtype=torch.bfloat16) for _ in range(4))
+    for t in (q, k, v):
+        t.requires_grad_(True)
+    out = {}
+    for causal in (False, True):
+        flops = 4.0 * N * N * d * B * H * (0.5 if causal else 1.0)
+        for name, backend in (("flash", SDPBackend.FLASH_ATTENTION),
+                              ("memory_efficient", SDPBackend.EFFICIENT_ATTENTION)):
+            key = f"{name}_{'causal' if causal else 'noncausal'}"
+            try:
+                with sdpa_kernel(backend):
+                    fwd = lambda: F.scaled_dot_product_attention(q, k, v, is_causal=causal)
+                    step = lambda: fwd().backward(do)
+                    fwd_ms, step_ms = median_ms(torch, fwd), median_ms(torch, step)
+                out[key] = {"fwd_ms": round(fwd_ms, 4), "fwd_tflops": round(flops / fwd_ms / 1e9, 1),
+                            "fwd_bwd_ms": round(step_ms, 4),
+                            "fwd_bwd_tflops": round(3.5 * flops / step_ms / 1e9, 1)}
+            except Exception as exc:              # a backend this build lacks
+                out[key] = {"error": str(exc)[:200]}
+    return out
 
 
 def mfma_calibration(torch, binding, iters=4000, launches=10):
@@ -372,6 +407,12 @@ def main():
     if args.mfma_calibration:
         print(json.dumps({"mfma_calibration": mfma_calibration(torch, binding),
                           "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}), flush=True)
+        return
+    if args.torch_sdpa_reference:
+        print(json.dumps({"torch_sdpa_reference": torch_sdpa_reference(torch, args.B, args.H, args.N, args.d,
+                                                                       args.seed),
+                          "config": {"workload": f"b{args.B}_h{args.H}_n{args.N}_d{args.d}"},
+                          "unit": "TFLOP/s", "dtype": "bf16"}), flush=True)
         return
     if args.fp8_forward:
         print(json.dumps({"fp8_forward": fp8_workloads(torch, binding, inputs, workloads, args.seed),
