@@ -112,6 +112,24 @@ def test_fp8_bad_descale_gives_nan_rows_of_that_head_only(gpu_lib):
     check_heads(o, lse, x, 64 ** -0.5, False, None, "healthy heads", heads=[(0, 0), (0, 1)])
 
 
+@pytest.fixture(scope="module")
+def fp8_c2_run(gpu_lib):
+    """The FP8 forward at the forward benchmark shape (B=4 H=32 N=4096 d=128,
+    non-causal), in the launch configuration the benchmark times."""
+    x = inputs.make_qkv_fp8(4, 4096, 32, 128, seed=38)
+    o, lse = run(gpu_lib, x, False)
+    return x, o.cpu(), lse.cpu()
+
+
+@pytest.mark.parametrize("b", [0, 1, 2, 3])
+def test_fp8_forward_full_size_every_head(fp8_c2_run, b):
+    """Every head of batch entry b at the benchmark shape: each element of O
+    within the E4M3 bound, the head's relative L2 and LSE."""
+    x, o, lse = fp8_c2_run
+    print(f"\n[fp8 fwd] B4 N4096 H32 d128 b={b}", flush=True)
+    check_heads(o, lse, x, 128 ** -0.5, False, None, f"b={b}", heads=[(b, h) for h in range(32)])
+
+
 def test_fp8_forward_full_size_sampled(gpu_lib):
     """B=4 H=32 N=4096 d=128 non-causal (the forward benchmark shape), in the
     launch configuration the benchmark times: sampled rows against the
