@@ -201,22 +201,20 @@ def test_bwd_sweep_n16384(gpu_lib, d):
     full_size_properties(x, grads)
 
 
-@pytest.mark.parametrize("N,d,H,heads", [(8192, 128, 32, [(0, 0), (0, 13), (0, 31)]),
-                                         (16384, 128, 32, [(0, 17)]),
-                                         (16384, 64, 8, [(0, 5)]),
-                                         (9000, 128, 4, [(0, 2)])])
-def test_bwd_long_causal_alternating_sweeps(gpu_lib, N, d, H, heads):
+@pytest.mark.parametrize("N,d,H", [(8192, 128, 32), (16384, 128, 32), (16384, 64, 8), (9000, 128, 4)])
+def test_bwd_long_causal_alternating_sweeps(gpu_lib, N, d, H):
     """Causal, B=1, at sizes where a head's streamed operands (two N x d
     bf16 tensors) no longer fit in one XCD's 4 MiB L2: the launch order then
     reverses the sweep of every other generation of workgroups (odd ones of
     the query-block kernels, even ones of the key-block kernel), so each head
-    has blocks swept both ways.  Forward and backward of the listed heads by
-    the parity rule, the sum invariants on every head."""
+    has blocks swept both ways.  Forward and backward of every head by the
+    parity rule (N=16384, d=128 is the long-context benchmark shape), and the
+    sum invariants."""
     name = f"causal B1 H{H} N{N} d{d}"
     print(f"\n[bwd] {name}", flush=True)
     x = inputs.make_qkv(1, N, H, d, torch.bfloat16, seed=N + d, with_do=True)
     grads, o, lse = run(gpu_lib, x, True, with_forward=True)
-    check_parity(x, d ** -0.5, True, o=o, lse=lse, grads=grads, groups=heads, what=name)
+    check_parity(x, d ** -0.5, True, o=o, lse=lse, grads=grads, what=name)
     assert torch.equal(o[0, 0].cpu(), x["v"][0, 0])
     full_size_properties(x, grads)
 
