@@ -194,6 +194,27 @@ def test_glossary_worked_example():
     assert printed / 50 <= err <= printed * 5, err
 
 
+@pytest.mark.parametrize("N", [7, 64])
+def test_lse_merge_of_key_halves_is_full_causal_attention(N):
+    """Attention over two disjoint key ranges, merged through their LSEs
+    (LSE = log(e^LSE_a + e^LSE_b), O = e^(LSE_a - LSE) O_a + e^(LSE_b - LSE) O_b),
+    equals attention over all keys: the identity the GPU merge test and the
+    sequence-split design rely on.  Queries of the second half see every key
+    of the first half (unmasked) and the second half causally."""
+    g = np.random.default_rng(N)
+    q, k, v = (g.standard_normal((N, 16)) for _ in range(3))
+    half = N // 2
+    ro, rl = head_forward(q, k, v, 0.3, True)
+    oa, la = head_forward(q[half:], k[:half], v[:half], 0.3, False)
+    ob, lb = head_forward(q[half:], k[half:], v[half:], 0.3, True)
+    lse = np.logaddexp(la, lb)
+    o = np.exp(la - lse)[:, None] * oa + np.exp(lb - lse)[:, None] * ob
+    assert np.allclose(o, ro[half:], rtol=0, atol=1e-12)
+    assert np.allclose(lse, rl[half:], rtol=0, atol=1e-12)
+    # a wrong merge (plain average of the two halves) is far off
+    assert not np.allclose(0.5 * (oa + ob), ro[half:], atol=1e-3)
+
+
 def test_lse_statistical_sanity():
     """For N(0,1) keys, sum_j exp(s_j) ~ N exp(scale^2 |q|^2 / 2), so
     LSE_i ~ ln N + |q_i|^2 / (2 d) at scale 1/sqrt(d).  Catches a wrong log
