@@ -56,11 +56,16 @@ def parse():
                     help="run only the matrix-core calibration kernel (pure bf16 MFMA, and with 2 or "
                          "4 vector instructions per MFMA) and print its sustained rates")
     ap.add_argument("--fp8-forward", action="store_true",
-                    help="run only the FP8 forward workloads (E4M3, the c2 and long causal shapes) "
+                    help="run only the FP8 forward workloads (E4M3; B4 H32 N4096 d128, and B1 H32 N16384 d128 causal) "
                          "and print their rates")
     ap.add_argument("--torch-sdpa-reference", action="store_true",
                     help="run only torch's scaled_dot_product_attention (flash and memory-efficient "
                          "backends) at --B/--H/--N/--d, both masks, as a reference beside the kernels")
+    ap.add_argument("--mall-flush", action="store_true",
+                    help="run only the cache-flush check: single fwd and fwd+bwd calls on "
+                         "B4 H32 N4096 d128 and B1 H32 N16384 d128 causal, timed one by one, "
+                         "with and without a 512 MiB overwrite between calls (outside the "
+                         "timed region)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device-to-device copy of 1 GiB (3 times), the "
                          "reference for scaling HBM byte counters")
@@ -120,6 +125,71 @@ def torch_sdpa_reference(torch, B, H, N, d, seed):
                             "fwd_bwd_tflops": round(3.5 * flops / step_ms / 1e9, 1)}
             except Exception as exc:              # a backend this build lacks
                 out[key] = {"error": str(exc)[:200]}
+    return out
+
+
+# Shapes for the cache-flush check: the headline shape and the long causal one.
+FLUSH_WORKLOADS = [
+    ("b4_h32_n4096_d128", 4, 32, 4096, 128, False),
+    ("b1_h32_n16384_d128_causal", 1, 32, 16384, 128, True),
+]
+FLUSH_BYTES = 512 << 20          # twice the 256 MB Infinity Cache
+
+
+def mall_flush(torch, binding, inputs, workloads, seed, reps=50, warmup=10):
+    """Each call timed alone (events on the current stream around that call
+    only), 50 reps after 10 warm-up calls, once back to back and once with a
+    512 MiB buffer overwritten between calls so that neither L2 nor the
+    Infinity Cache holds anything of the previous call.  The fill runs outside
+    the events; a synchronisation after it keeps its tail out of the next
+    call's time.  Reports medians and minima, and the median's change."""
+    dev = torch.device("cuda:0")
+    junk = torch.empty(FLUSH_BYTES // 4, device=dev, dtype=torch.float32)
+    out = {}
+    for name, B, H, N, d, causal in FLUSH_WORKLOADS:
+        x = inputs.make_qkv(B, N, H, d, torch.bfloat16, seed=seed, with_do=True)
+        q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "do"))
+        o, lse = binding.forward(q, k, v, causal=causal)
+        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+        ws = torch.empty(binding.bwd_workspace_size(B, H, N, d), device=dev, dtype=torch.uint8)
+        _, calls = binding.backward_steps(q, k, v, o, do, lse, causal=causal, workspace=ws, out=grads)
+
+        def fwd():
+            binding.forward(q, k, v, causal=causal, out=o, lse=lse)
+
+        def step():
+            fwd()
+            for c in calls:
+                c()
+
+        res = {}
+        for tag, f, fl in (("fwd", fwd, workloads.fwd_flops(B, H, N, d, causal)),
+                           ("fwd_bwd", step, workloads.fwd_flops(B, H, N, d, causal)
+                            + workloads.bwd_flops(B, H, N, d, causal))):
+            for flush in (False, True):
+                for _ in range(warmup):
+                    f()
+                ms = []
+                for r in range(reps):
+                    if flush:
+                        junk.fill_(float(r))
+                    torch.cuda.synchronize()
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    f()
+                    e1.record()
+                    torch.cuda.synchronize()
+                    ms.append(e0.elapsed_time(e1))
+                ms.sort()
+                key = f"{tag}_{'flushed' if flush else 'warm'}"
+                res[key] = {"median_ms": round(ms[reps // 2], 4), "min_ms": round(ms[0], 4),
+                            "median_tflops": round(fl / (ms[reps // 2] * 1e-3) / 1e12, 1)}
+            warm, cold = res[f"{tag}_warm"]["median_ms"], res[f"{tag}_flushed"]["median_ms"]
+            res[f"{tag}_median_change"] = round(cold / warm - 1, 4)
+        out[name] = res
+        print(f"[mall flush] {name}: {json.dumps(res)}", file=sys.stderr, flush=True)
+        del q, k, v, do, o, lse, grads, ws, calls
+        torch.cuda.empty_cache()
     return out
 
 
@@ -413,6 +483,10 @@ def main():
                                                                        args.seed),
                           "config": {"workload": f"b{args.B}_h{args.H}_n{args.N}_d{args.d}"},
                           "unit": "TFLOP/s", "dtype": "bf16"}), flush=True)
+        return
+    if args.mall_flush:
+        print(json.dumps({"mall_flush": mall_flush(torch, binding, inputs, workloads, args.seed),
+                          "flush_bytes": FLUSH_BYTES, "unit": "ms", "dtype": "bf16"}), flush=True)
         return
     if args.fp8_forward:
         print(json.dumps({"fp8_forward": fp8_workloads(torch, binding, inputs, workloads, args.seed),
