@@ -14,7 +14,12 @@
 //   3  mode 1 plus two FMAs and two exp2 per MFMA;
 //   4  mode 1 with the A operand read from LDS by one ds_read_b128 per MFMA
 //      (1 KB per wave), eight reads in flight, as the attention kernels read
-//      their K/V or Q/dO operands.
+//      their K/V or Q/dO operands;
+//   5  mode 4 plus three FMAs and one exp2 per MFMA: the forward's mix per
+//      MFMA (one score per lane: exponent FMA, exp2, row sum, half a
+//      conversion, loop and mask work);
+//   6  mode 5 with each LDS read feeding two MFMAs (0.5 KB per MFMA), the
+//      mix of a forward whose waves hold 64 queries instead of 32.
 // A checksum per thread is written so the compiler keeps the work.
 #include "fa_common.h"
 
@@ -92,7 +97,10 @@ __global__ __launch_bounds__(256) void calib_mfma_kernel(float* __restrict__ out
     out[blockIdx.x * blockDim.x + threadIdx.x] = checksum(acc, s);
 }
 
-// mode 4: random B operands in registers, A operands read from LDS
+// modes 4 - 6: random B operands in registers, A operands read from LDS, one
+// read per REUSE MFMAs; NFMA FMAs and NEXP exp2 per MFMA on independent
+// registers
+template <int REUSE, int NFMA, int NEXP>
 __global__ __launch_bounds__(256) void calib_mfma_lds_kernel(float* __restrict__ out, int iters) {
     __shared__ __attribute__((aligned(16))) char lds[4 * CH * 1024];   // 8 KB per wave
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -107,21 +115,33 @@ __global__ __launch_bounds__(256) void calib_mfma_lds_kernel(float* __restrict__
     f32x16 acc[CH];
 #pragma unroll
     for (int c = 0; c < CH; ++c) acc[c] = f32x16{};
-    bf16x8 op[CH];
+    constexpr int NOP = CH / REUSE;            // reads in flight
+    bf16x8 op[NOP];
 #pragma unroll
-    for (int c = 0; c < CH; ++c) op[c] = lds_read_b128(base + c * 1024);
+    for (int c = 0; c < NOP; ++c) op[c] = lds_read_b128(base + c * 1024);
+    constexpr int NV = NFMA + NEXP > 0 ? NFMA + NEXP : 1;
+    float xv[NV];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) xv[v] = 0.25f * (float)(lane + v);
 #pragma clang loop unroll(disable)
     for (int it = 0; it < 2 * iters; ++it) {
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
-            const bf16x8 cur = op[c];
-            op[c] = lds_read_b128(base + ((c + it + 1) & (CH - 1)) * 1024);
+            const int o = c / REUSE;
+            const bf16x8 cur = op[o];
+            if (c % REUSE == REUSE - 1) op[o] = lds_read_b128(base + ((o + it + 1) & (CH - 1)) * 1024);
             acc[c] = mfma32x32x16(cur, b[(c + 3) & (CH - 1)], acc[c]);
+#pragma unroll
+            for (int v = 0; v < NFMA; ++v) xv[v] = __builtin_fmaf(xv[v], 0.999f, 0.001f);
+#pragma unroll
+            for (int v = 0; v < NEXP; ++v) xv[NFMA + v] = fast_exp2(-xv[NFMA + v]);
         }
     }
     float s = 0.f;
 #pragma unroll
-    for (int c = 0; c < CH; ++c) s += (float)op[c][c];
+    for (int v = 0; v < NFMA + NEXP; ++v) s += xv[v];
+#pragma unroll
+    for (int c = 0; c < NOP; ++c) s += (float)op[c][c];
     out[blockIdx.x * blockDim.x + threadIdx.x] = checksum(acc, s);
 }
 
@@ -186,7 +206,9 @@ hipError_t launch_calib_mfma(float* out, int n_workgroups, int waves, int iters,
         case 1: hipLaunchKernelGGL((calib_mfma_kernel<true, 0>), grid, block, 0, stream, out, iters); break;
         case 2: hipLaunchKernelGGL((calib_mfma_kernel<true, 2>), grid, block, 0, stream, out, iters); break;
         case 3: hipLaunchKernelGGL((calib_mfma_kernel<true, 4>), grid, block, 0, stream, out, iters); break;
-        case 4: hipLaunchKernelGGL(calib_mfma_lds_kernel, grid, block, 0, stream, out, iters); break;
+        case 4: hipLaunchKernelGGL((calib_mfma_lds_kernel<1, 0, 0>), grid, block, 0, stream, out, iters); break;
+        case 5: hipLaunchKernelGGL((calib_mfma_lds_kernel<1, 3, 1>), grid, block, 0, stream, out, iters); break;
+        case 6: hipLaunchKernelGGL((calib_mfma_lds_kernel<2, 3, 1>), grid, block, 0, stream, out, iters); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
