@@ -94,7 +94,8 @@ def copy_calibration():
 MFMA_CALIBRATION = [("const_w2", 512, 0), ("random_w2", 512, 1), ("random_valu2_w2", 512, 2),
                     ("random_valu4_w2", 512, 3), ("random_lds_w2", 512, 4), ("random_w1", 256, 1),
                     ("const_w1", 256, 0), ("random_lds_valu4_w2", 512, 5), ("random_lds_valu4_w1", 256, 5),
-                    ("random_lds_half_valu4_w2", 512, 6), ("random_lds_half_valu4_w1", 256, 6)]
+                    ("random_lds_half_valu4_w2", 512, 6), ("random_lds_half_valu4_w1", 256, 6),
+                    ("random_lds_valu2p5_w2", 512, 7), ("random_lds_valu2p5_w1", 256, 7)]
 
 
 def torch_sdpa_reference(torch, B, H, N, d, seed):

@@ -304,7 +304,8 @@ def calibrate_mfma(n_workgroups, waves=4, iters=4096, mode=0, out=None):
     (fa_calibrate_mfma; ``mode`` 0 constant operands, 1 random operands, 2 and
     3 random plus 2 or 4 vector instructions per MFMA, 4 random with the A
     operand from LDS, 5 mode 4 plus three FMAs and one exp2 per MFMA, 6 mode
-    5 with each LDS read feeding two MFMAs).  Returns (checksum tensor, flops of the launch)."""
+    5 with each LDS read feeding two MFMAs, 7 mode 4 plus four FMAs and one
+    exp2 per two MFMAs).  Returns (checksum tensor, flops of the launch)."""
     lib = load()
     dev = torch.device("cuda", torch.cuda.current_device())
     n = n_workgroups * 64 * waves

@@ -335,7 +335,7 @@ int fa_calibrate_mfma(float* out, int n_workgroups, int waves_per_workgroup, int
         return FA_ERR_INVALID_ARG;
     // one checksum per thread at a 32-bit index
     if (n_workgroups > (1 << 22)) return FA_ERR_UNSUPPORTED;
-    if (mode < 0 || mode > 6) return FA_ERR_INVALID_ARG;
+    if (mode < 0 || mode > 7) return FA_ERR_INVALID_ARG;
     if (reinterpret_cast<uintptr_t>(out) & 3u) return FA_ERR_MISALIGNED;
     if (fa::launch_calib_mfma(out, n_workgroups, waves_per_workgroup, iters, mode, stream) !=
         hipSuccess)

@@ -19,7 +19,9 @@
 //      MFMA (one score per lane: exponent FMA, exp2, row sum, half a
 //      conversion, loop and mask work);
 //   6  mode 5 with each LDS read feeding two MFMAs (0.5 KB per MFMA), the
-//      mix of a forward whose waves hold 64 queries instead of 32.
+//      mix of a forward whose waves hold 64 queries instead of 32;
+//   7  mode 4 plus four FMAs and one exp2 per two MFMAs: the dK/dV kernel's
+//      mix per MFMA (2.5 vector instructions, half of one an exp2).
 // A checksum per thread is written so the compiler keeps the work.
 #include "fa_common.h"
 
@@ -97,10 +99,10 @@ __global__ __launch_bounds__(256) void calib_mfma_kernel(float* __restrict__ out
     out[blockIdx.x * blockDim.x + threadIdx.x] = checksum(acc, s);
 }
 
-// modes 4 - 6: random B operands in registers, A operands read from LDS, one
-// read per REUSE MFMAs; NFMA FMAs and NEXP exp2 per MFMA on independent
-// registers
-template <int REUSE, int NFMA, int NEXP>
+// modes 4 - 7: random B operands in registers, A operands read from LDS, one
+// read per REUSE MFMAs; NFMA FMAs and NEXP exp2 beside every EVERY-th MFMA
+// on independent registers
+template <int REUSE, int NFMA, int NEXP, int EVERY = 1>
 __global__ __launch_bounds__(256) void calib_mfma_lds_kernel(float* __restrict__ out, int iters) {
     __shared__ __attribute__((aligned(16))) char lds[4 * CH * 1024];   // 8 KB per wave
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -131,10 +133,12 @@ __global__ __launch_bounds__(256) void calib_mfma_lds_kernel(float* __restrict__
             const bf16x8 cur = op[o];
             if (c % REUSE == REUSE - 1) op[o] = lds_read_b128(base + ((o + it + 1) & (CH - 1)) * 1024);
             acc[c] = mfma32x32x16(cur, b[(c + 3) & (CH - 1)], acc[c]);
+            if (c % EVERY == 0) {
 #pragma unroll
-            for (int v = 0; v < NFMA; ++v) xv[v] = __builtin_fmaf(xv[v], 0.999f, 0.001f);
+                for (int v = 0; v < NFMA; ++v) xv[v] = __builtin_fmaf(xv[v], 0.999f, 0.001f);
 #pragma unroll
-            for (int v = 0; v < NEXP; ++v) xv[NFMA + v] = fast_exp2(-xv[NFMA + v]);
+                for (int v = 0; v < NEXP; ++v) xv[NFMA + v] = fast_exp2(-xv[NFMA + v]);
+            }
         }
     }
     float s = 0.f;
@@ -209,6 +213,7 @@ hipError_t launch_calib_mfma(float* out, int n_workgroups, int waves, int iters,
         case 4: hipLaunchKernelGGL((calib_mfma_lds_kernel<1, 0, 0>), grid, block, 0, stream, out, iters); break;
         case 5: hipLaunchKernelGGL((calib_mfma_lds_kernel<1, 3, 1>), grid, block, 0, stream, out, iters); break;
         case 6: hipLaunchKernelGGL((calib_mfma_lds_kernel<2, 3, 1>), grid, block, 0, stream, out, iters); break;
+        case 7: hipLaunchKernelGGL((calib_mfma_lds_kernel<1, 4, 1, 2>), grid, block, 0, stream, out, iters); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

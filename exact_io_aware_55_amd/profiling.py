@@ -316,7 +316,8 @@ def valu(valu_dir, trace_dir, out, workload, bench_args=HEADLINE_ARGS):
 CALIB_MODES = {0: "constant operands", 1: "random operands", 2: "random + FMA + exp2 per MFMA",
                3: "random + 2 FMA + 2 exp2 per MFMA", 4: "random, A operand from LDS",
                5: "random, A from LDS + 3 FMA + exp2 per MFMA",
-               6: "random, A from LDS read once per 2 MFMAs + 3 FMA + exp2 per MFMA"}
+               6: "random, A from LDS read once per 2 MFMAs + 3 FMA + exp2 per MFMA",
+               7: "random, A from LDS + 4 FMA + exp2 per 2 MFMAs"}
 
 
 def calibration(rates_json, mfma_dir, out):
@@ -362,11 +363,13 @@ def calibration(rates_json, mfma_dir, out):
              "| run | mode | waves per SIMD | TFLOP/s | of nameplate | clock (GHz) | MFMA busy | "
              "counted / executed flops |", "|---|---|---|---|---|---|---|---|"]
     mode_kernel = {0: ("<false, 0>", None), 1: ("<true, 0>", None), 2: ("<true, 2>", None),
-                   3: ("<true, 4>", None), 4: ("calib_mfma_lds_kernel<1, 0, 0>", None),
-                   5: ("calib_mfma_lds_kernel<1, 3, 1>", None), 6: ("calib_mfma_lds_kernel<2, 3, 1>", None)}
+                   3: ("<true, 4>", None), 4: ("calib_mfma_lds_kernel<1, 0, 0, 1>", None),
+                   5: ("calib_mfma_lds_kernel<1, 3, 1, 1>", None), 6: ("calib_mfma_lds_kernel<2, 3, 1, 1>", None),
+                   7: ("calib_mfma_lds_kernel<1, 4, 1, 2>", None)}
     for label, r in rates.items():
         mode = {"const": 0, "random": 1, "random_valu2": 2, "random_valu4": 3, "random_lds": 4,
-                "random_lds_valu4": 5, "random_lds_half_valu4": 6}[label.rsplit("_", 1)[0]]
+                "random_lds_valu4": 5, "random_lds_half_valu4": 6,
+                "random_lds_valu2p5": 7}[label.rsplit("_", 1)[0]]
         waves = int(label.rsplit("_w", 1)[1])
         grid = 256 * 4 * 64 * waves
         key = [k for k in groups if mode_kernel[mode][0] in k[0] and k[1] == grid]

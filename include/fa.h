@@ -230,7 +230,8 @@ size_t fa_bwd_noalloc_max_workspace(void);
  * and two exp2 per MFMA; 4 mode 1 with the A operand read from LDS (one
  * ds_read_b128 per MFMA); 5 mode 4 plus three FMAs and one exp2 per MFMA
  * (the forward's mix per MFMA); 6 mode 5 with each LDS read feeding two
- * MFMAs (0.5 KB per MFMA, the mix of 64 queries per wave).  out: device fp32 with n_workgroups * 64 *
+ * MFMAs (0.5 KB per MFMA, the mix of 64 queries per wave); 7 mode 4 plus
+ * four FMAs and one exp2 per two MFMAs (the dK/dV kernel's mix).  out: device fp32 with n_workgroups * 64 *
  * waves_per_workgroup elements (checksums, 4-byte aligned).  The rates of
  * modes 0 and 1 are the chip's dense bf16 rate with and without operand
  * switching (the second is what real data sees); the MFMA-busy counter of

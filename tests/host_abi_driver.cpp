@@ -148,7 +148,7 @@ int main(int argc, char** argv) {
 
     // calibration and probe
     expect("calib null", fa_calibrate_mfma(nullptr, 4, 4, 10, 0, nullptr), FA_ERR_INVALID_ARG);
-    expect("calib mode", fa_calibrate_mfma((float*)F, 4, 4, 10, 7, nullptr), FA_ERR_INVALID_ARG);
+    expect("calib mode", fa_calibrate_mfma((float*)F, 4, 4, 10, 8, nullptr), FA_ERR_INVALID_ARG);
     expect("calib misaligned", fa_calibrate_mfma((float*)fake(2), 4, 4, 10, 0, nullptr), FA_ERR_MISALIGNED);
     expect("probe k", fa_probe_mfma(0, F, F, (float*)F, 1, 24, nullptr), FA_ERR_INVALID_ARG);
     expect("probe size", fa_probe_mfma(1, F, F, (float*)F, 1 << 16, 1 << 16, nullptr), FA_ERR_UNSUPPORTED);

@@ -237,7 +237,7 @@ def test_calibration_argument_errors(lib):
     f = lib.fa_calibrate_mfma
     assert f(None, 4, 4, 10, 0, None) == binding.FA_ERR_INVALID_ARG
     for n_wg, waves, iters, mode in ((0, 4, 10, 0), (4, 0, 10, 0), (4, 5, 10, 0), (4, 4, 0, 0),
-                                     (4, 4, 10, -1), (4, 4, 10, 7)):
+                                     (4, 4, 10, -1), (4, 4, 10, 8)):
         assert f(V(FAKE), n_wg, waves, iters, mode, None) == binding.FA_ERR_INVALID_ARG
     assert f(V(FAKE + 2), 4, 4, 10, 0, None) == binding.FA_ERR_MISALIGNED
     assert f(V(FAKE), (1 << 22) + 1, 4, 10, 0, None) == binding.FA_ERR_UNSUPPORTED
