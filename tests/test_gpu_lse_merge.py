@@ -12,7 +12,14 @@ queries) and the second half causal, and merged with
     O   = exp(LSE_a - LSE) O_a + exp(LSE_b - LSE) O_b.
 The merged rows, and the first half's rows from a third call, are compared
 with the oracle's full causal attention: every head within the fixed bf16
-lines (max-abs 2e-2, relative L2 5e-3) and LSE within 1e-3."""
+lines (max-abs 2e-2, relative L2 5e-3) and LSE within 1e-3.
+
+The backward splits the same way: with the full sequence's O and LSE (what
+the merge above yields), the backward of each (query half, key half) pair
+that can see anything gives that pair's share of the gradients (P = exp(S -
+LSE) and D = rowsum(dO * O) are row-global), and dQ of a query half is the
+sum over its key halves, dK and dV of a key half the sum over its query
+halves."""
 
 import numpy as np
 import pytest
@@ -60,3 +67,57 @@ def test_causal_rows_from_two_key_halves(gpu_lib, N, d):
             assert max_abs(o_all[b, :, h], ro) <= 2e-2, tag
             assert rel_l2(o_all[b, :, h], ro) <= 5e-3, tag
             assert max_abs(l_all[b, h], rl) <= LSE_MAX_ABS, tag
+
+
+def half_spacing(x):
+    """Half the bf16 spacing at each element of x (0 where x = 0): the most
+    one rounding of a partial gradient to bf16 can move it."""
+    a = np.abs(x)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    return np.where(a > 0, 2.0 ** (e - 8), 0.0)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [1024, 2000])
+def test_causal_gradients_from_query_and_key_halves(gpu_lib, N, d):
+    """Three backward calls over the visible (query half, key half) pairs:
+    (1, 1) causal, (2, 1) unmasked, (2, 2) causal.  The assembled dQ, dK, dV
+    are held to the oracle's full causal backward within the fixed lines plus
+    half a bf16 spacing of every partial that was rounded before the sum."""
+    B, H = 2, 4
+    half = N // 2
+    print(f"\n[lse merge bwd] B{B} H{H} N{N} d{d}", flush=True)
+    x = inputs.make_qkv(B, N, H, d, torch.bfloat16, seed=N + d + 7, with_do=True)
+    q, k, v, do = (x[n].to(DEV) for n in ("q", "k", "v", "do"))
+    o, lse = gpu_lib.forward(q, k, v, causal=True)
+    rows = lambda t, lo, hi: t[:, lo:hi].contiguous()
+    lrows = lambda lo, hi: lse[:, :, lo:hi].contiguous()
+    h1, h2 = (0, half), (half, N)
+    pair = lambda qh, kh, causal: gpu_lib.backward(rows(q, *qh), rows(k, *kh), rows(v, *kh), rows(o, *qh),
+                                                   rows(do, *qh), lrows(*qh), causal=causal)
+    dq11, dk11, dv11 = pair(h1, h1, True)
+    dq21, dk21, dv21 = pair(h2, h1, False)
+    dq22, dk22, dv22 = pair(h2, h2, True)
+    torch.cuda.synchronize()
+
+    f64 = inputs.to_f64
+    parts = {
+        "dq": ([f64(dq11)], [f64(dq21), f64(dq22)]),
+        "dk": ([f64(dk11), f64(dk21)], [f64(dk22)]),
+        "dv": ([f64(dv11), f64(dv21)], [f64(dv22)]),
+    }
+    got, slack = {}, {}
+    for name, (first, second) in parts.items():
+        got[name] = np.concatenate([sum(first), sum(second)], axis=1)          # [B, N, H, d]
+        sl = lambda ps: sum(half_spacing(p) for p in ps) if len(ps) > 1 else np.zeros_like(ps[0])
+        slack[name] = np.concatenate([sl(first), sl(second)], axis=1)
+    qn, kn, vn, dn = (inputs.to_f64(x[n]) for n in ("q", "k", "v", "do"))
+    for b in range(B):
+        for h in range(H):
+            ref = dict(zip(("dq", "dk", "dv"),
+                           oracle.head_backward(qn[b, :, h], kn[b, :, h], vn[b, :, h], dn[b, :, h], d ** -0.5, True)))
+            for name in ("dq", "dk", "dv"):
+                g, r, sl = got[name][b, :, h], ref[name], slack[name][b, :, h]
+                tag = f"N{N} d{d} head {(b, h)} {name}"
+                assert np.all(np.abs(g - r) <= 2e-2 + sl), f"{tag}: max excess {np.max(np.abs(g - r) - sl):.3e}"
+                assert np.linalg.norm(g - r) <= 5e-3 * np.linalg.norm(r) + np.linalg.norm(sl), tag
