@@ -15,5 +15,6 @@ from .attention import (  # noqa: F401
     head_forward_blockwise,
     head_probabilities,
     kv_head,
+    merge,
 )
 from .fp8 import decode_e4m3, dequantize, forward_fp8, forward_rows_fp8  # noqa: F401

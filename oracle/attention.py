@@ -287,3 +287,27 @@ def backward(q, k, v, do, scale, causal, heads=None, window=None):
         dk[b, :, g, :] += bb
         dv[b, :, g, :] += c
     return dq, dk, dv
+
+
+def merge(o_a, lse_a, o_b, lse_b):
+    """Attention over the union of two disjoint key ranges, from the results
+    over each range: the running-maximum rescaling of the explainer's
+    "Tiling" section (and the glossary's online softmax) applied once to two
+    finished blocks.  With L = log(exp(LSE_a) + exp(LSE_b)),
+
+        O = exp(LSE_a - L) O_a + exp(LSE_b - L) O_b,   LSE = L.
+
+    o_a, o_b: [B, N, H, d]; lse_a, lse_b: [B, H, N].  A row that sees no key
+    in either range (both LSEs -inf) gets O = 0 and LSE = -inf; NaN
+    propagates.  Returns fp64 (O, LSE)."""
+    la, lb = _f64(lse_a), _f64(lse_b)
+    m = np.maximum(la, lb)                    # NaN in either stays NaN
+    empty = m == -np.inf
+    ms = np.where(empty, 0.0, m)
+    ea, eb = np.exp(la - ms), np.exp(lb - ms)
+    tot = np.where(empty, 1.0, ea + eb)
+    lse = np.where(empty, -np.inf, ms + np.log(tot))
+    wa = np.where(empty, 0.0, ea / tot).transpose(0, 2, 1)[..., None]   # [B, N, H, 1]
+    wb = np.where(empty, 0.0, eb / tot).transpose(0, 2, 1)[..., None]
+    return wa * _f64(o_a) + wb * _f64(o_b), lse
+

@@ -18,6 +18,13 @@ from exact_io_aware_55_amd import workloads
 
 from oracle import (backward, forward, forward_rows, head_backward, head_forward, kv_head,
                     head_forward_blockwise, head_probabilities)
+from oracle import forward as oracle_forward
+from oracle import merge as oracle_merge
+
+
+def oracle_forward_keys(q, k, v, scale):
+    """Non-causal attention of all queries over a range of keys ([B,N,H,d])."""
+    return oracle_forward(q, k, v, scale, False)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -213,6 +220,79 @@ def test_lse_merge_of_key_halves_is_full_causal_attention(N):
     assert np.allclose(lse, rl[half:], rtol=0, atol=1e-12)
     # a wrong merge (plain average of the two halves) is far off
     assert not np.allclose(0.5 * (oa + ob), ro[half:], atol=1e-3)
+    # the oracle's merge (B = H = 1 layout) is that identity
+    mo, ml = oracle_merge(oa[None, :, None], la[None, None], ob[None, :, None], lb[None, None])
+    assert np.allclose(mo[0, :, 0], ro[half:], rtol=0, atol=1e-12)
+    assert np.allclose(ml[0, 0], rl[half:], rtol=0, atol=1e-12)
+
+
+def pin_merge_thirds(merge):
+    """Non-causal attention over three key ranges merged as (a b) c, as
+    a (b c), and as (b a) c equals attention over all keys, for two batches
+    and three heads with different data (catches a transposed LSE layout or
+    a head mix-up)."""
+    g = np.random.default_rng(7)
+    B, N, H, d = 2, 60, 3, 8
+    q, k, v = (g.standard_normal((B, N, H, d)) for _ in range(3))
+    full_o, full_l = oracle_forward(q, k, v, 0.4, False)
+    parts = []
+    for lo, hi in ((0, 17), (17, 41), (41, N)):
+        o, l = oracle_forward_keys(q, k[:, lo:hi], v[:, lo:hi], 0.4)
+        parts.append((o, l))
+    (oa, la), (ob, lb), (oc, lc) = parts
+    for o, l in (merge(*merge(oa, la, ob, lb), oc, lc),
+                 merge(oa, la, *merge(ob, lb, oc, lc)),
+                 merge(*merge(ob, lb, oa, la), oc, lc)):
+        assert np.allclose(o, full_o, rtol=0, atol=1e-12)
+        assert np.allclose(l, full_l, rtol=0, atol=1e-12)
+
+
+def test_merge_over_key_thirds_in_any_grouping():
+    pin_merge_thirds(oracle_merge)
+
+
+def _merge_swapped_weights(o_a, lse_a, o_b, lse_b):
+    o, l = oracle_merge(o_a, lse_a, o_b, lse_b)
+    w = np.exp(lse_a - l).transpose(0, 2, 1)[..., None]
+    return (1 - w) * o_a + w * o_b, l
+
+
+def _merge_max_lse(o_a, lse_a, o_b, lse_b):
+    o, _ = oracle_merge(o_a, lse_a, o_b, lse_b)
+    return o, np.maximum(lse_a, lse_b)
+
+
+@pytest.mark.parametrize("mutant", [_merge_swapped_weights, _merge_max_lse], ids=lambda f: f.__name__)
+def test_merge_pin_catches_mutants(mutant):
+    """Planted mistakes in the merge (the two weights swapped; LSE taken as
+    the larger of the two instead of their log-sum) fail the thirds pin."""
+    with pytest.raises(AssertionError):
+        pin_merge_thirds(mutant)
+
+
+def test_merge_with_an_empty_range_and_special_rows():
+    """A range that sees no key (LSE = -inf, any O) leaves the other result
+    exactly as it is; two empty ranges give O = 0 and LSE = -inf; NaN in an
+    LSE propagates to its row only."""
+    g = np.random.default_rng(8)
+    B, N, H, d = 1, 5, 2, 4
+    oa, ob = g.standard_normal((B, N, H, d)), g.standard_normal((B, N, H, d))
+    la, lb = g.standard_normal((B, H, N)), np.full((B, H, N), -np.inf)
+    o, l = oracle_merge(oa, la, ob, lb)
+    assert np.array_equal(o, oa) and np.array_equal(l, la)
+    o, l = oracle_merge(ob, lb, oa, la)
+    assert np.array_equal(o, oa) and np.array_equal(l, la)
+    o, l = oracle_merge(oa, np.full_like(la, -np.inf), ob, lb)
+    assert np.all(o == 0) and np.all(l == -np.inf)
+    la2 = la.copy()
+    la2[0, 1, 3] = np.nan
+    o, l = oracle_merge(oa, la2, ob, la)
+    assert np.isnan(l[0, 1, 3]) and np.all(np.isnan(o[0, 3, 1]))
+    assert np.isfinite(np.delete(l.ravel(), 1 * N + 3)).all()
+    # equal LSEs give the plain average, each weight exactly one half
+    o, l = oracle_merge(oa, la, ob, la)
+    assert np.allclose(o, 0.5 * (oa + ob), rtol=0, atol=1e-15)
+    assert np.allclose(l, la + np.log(2.0), rtol=0, atol=1e-15)
 
 
 def test_lse_statistical_sanity():
