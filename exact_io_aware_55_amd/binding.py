@@ -20,7 +20,8 @@ SYNC_LIB_PATH = os.path.join(_HERE, "libfa_sync.so")   # synchronisation check b
 
 EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_bwd_workspace_size", "fa_bwd", "fa_bwd_preprocess",
            "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_dq_stats", "fa_fwd_gqa", "fa_bwd_gqa", "fa_fwd_window",
-           "fa_bwd_window", "fa_fwd_fp8", "fa_bwd_noalloc", "fa_bwd_noalloc_max_workspace", "fa_calibrate_mfma", "fa_probe_mfma", "fa_strerror")
+           "fa_bwd_window", "fa_fwd_fp8", "fa_bwd_noalloc", "fa_bwd_noalloc_max_workspace", "fa_merge",
+           "fa_calibrate_mfma", "fa_probe_mfma", "fa_strerror")
 
 FA_OK = 0
 FA_ERR_INVALID_ARG = -1
@@ -81,6 +82,8 @@ def open_library(path: str):
     lib.fa_bwd_noalloc.restype = i
     lib.fa_bwd_noalloc_max_workspace.argtypes = []
     lib.fa_bwd_noalloc_max_workspace.restype = sz
+    lib.fa_merge.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, vp]
+    lib.fa_merge.restype = i
     lib.fa_calibrate_mfma.argtypes = [vp, i, i, i, i, vp]
     lib.fa_calibrate_mfma.restype = i
     lib.fa_probe_mfma.argtypes = [i, vp, vp, vp, i, i, vp]
@@ -297,6 +300,35 @@ def backward_noalloc(q, k, v, o, do, lse, causal=False, scale=None, out=None):
     _check(lib.fa_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk),
                               _ptr(dv), B, H, N, d, _scale(scale, d), int(bool(causal)), _stream()))
     return dq, dk, dv
+
+
+def _overlap(a, b):
+    """True if two tensors share any byte of memory without being the same
+    buffer (a partial overlap)."""
+    a0, b0 = a.data_ptr(), b.data_ptr()
+    a1, b1 = a0 + a.numel() * a.element_size(), b0 + b.numel() * b.element_size()
+    return a0 < b1 and b0 < a1 and not (a0 == b0 and a1 == b1)
+
+
+def merge(o_a, lse_a, o_b, lse_b, out=None, lse_out=None):
+    """Attention over the union of two disjoint key ranges from the results
+    over each (fa_merge): O = exp(LSE_a - L) O_a + exp(LSE_b - L) O_b with
+    L = log(exp(LSE_a) + exp(LSE_b)).  o_a, o_b: bf16 [B,N,H,d]; lse_a, lse_b:
+    fp32 [B,H,N].  ``out`` may be o_a or o_b and ``lse_out`` lse_a or lse_b
+    (accumulation in place).  Returns (O, LSE)."""
+    lib = load()
+    B, N, H, d = _check_inputs(torch.bfloat16, o_a, o_b)
+    dev = o_a.device
+    _need(lse_a, "lse_a", torch.float32, (B, H, N), dev)
+    _need(lse_b, "lse_b", torch.float32, (B, H, N), dev)
+    o = torch.empty_like(o_a) if out is None else _need(out, "out", torch.bfloat16, o_a.shape, dev)
+    lse = _lse_out(lse_out, B, H, N, dev)
+    for t, srcs in ((o, (o_a, o_b)), (lse, (lse_a, lse_b))):
+        if any(_overlap(t, x) for x in srcs):
+            raise ValueError("an output may be one of the inputs but must not partly overlap one")
+    _check(lib.fa_merge(_ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b), _ptr(o), _ptr(lse), B, H, N, d,
+                        _stream()))
+    return o, lse
 
 
 def calibrate_mfma(n_workgroups, waves=4, iters=4096, mode=0, out=None):

@@ -329,6 +329,19 @@ int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, c
                     stream);
 }
 
+int fa_merge(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b, void* o, float* lse,
+             int B, int H, int N, int d, hipStream_t stream) {
+    if (!o_a || !lse_a || !o_b || !lse_b || !o || !lse) return FA_ERR_INVALID_ARG;
+    const int rc = check_shape(B, H, N, d, 1.0f);
+    if (rc != FA_OK) return rc;
+    // one thread per 8 features: the grid must fit 32 bits
+    if ((long long)B * H * N * (d / 8) / 256 >= (1LL << 31)) return FA_ERR_UNSUPPORTED;
+    for (const void* p : {o_a, (const void*)lse_a, o_b, (const void*)lse_b, (const void*)o, (const void*)lse})
+        if (!aligned16(p)) return FA_ERR_MISALIGNED;
+    if (fa::launch_merge(o_a, lse_a, o_b, lse_b, o, lse, B, H, N, d, stream) != hipSuccess) return FA_ERR_LAUNCH;
+    return FA_OK;
+}
+
 int fa_calibrate_mfma(float* out, int n_workgroups, int waves_per_workgroup, int iters, int mode,
                       hipStream_t stream) {
     if (!out || n_workgroups < 1 || waves_per_workgroup < 1 || waves_per_workgroup > 4 || iters < 1)

@@ -76,4 +76,8 @@ hipError_t launch_calib_mfma(float* out, int n_workgroups, int waves, int iters,
 hipError_t launch_probe_mfma(int fp8, const void* a, const void* b, float* c, int n_tiles, int k,
                              hipStream_t stream);
 
+// Merge of two (O, LSE) results over disjoint key ranges (fa_merge).
+hipError_t launch_merge(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b, void* o,
+                        float* lse, int B, int H, int N, int d, hipStream_t stream);
+
 }  // namespace fa

@@ -219,6 +219,25 @@ int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, c
                    int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
 size_t fa_bwd_noalloc_max_workspace(void);
 
+/* Merge of two attention results over disjoint key ranges of the same
+ * queries into the result over their union (explainer page "Flash
+ * Attention", section "Tiling": the rescaling of a partial output by
+ * exp(m_old - m_new) when the running maximum grows, applied once to two
+ * finished results).  Per row, with L = log(exp(lse_a) + exp(lse_b)):
+ *     o = exp(lse_a - L) o_a + exp(lse_b - L) o_b,   lse = L,
+ * in fp32, o rounded to bf16 once.  This combines the results of devices
+ * that each hold a range of the keys.  o_a, o_b, o: device bf16 [B,N,H,d];
+ * lse_a, lse_b, lse: device fp32 [B,H,N]; all 16-byte aligned.  A range of
+ * weight 0 (its LSE -inf, or so far below the other's that its weight
+ * underflows) contributes nothing, whatever its o holds; a row with both
+ * LSEs -inf gets o = 0 and lse = -inf; NaN in either LSE gives a NaN row;
+ * NaN or Inf in an o of nonzero weight propagates.  o may be o_a or o_b and
+ * lse may be lse_a or lse_b (accumulation in place); no other overlap is
+ * allowed.  Shapes as fa_fwd.  INVALID_ARG for null pointers or B/H/N < 1;
+ * UNSUPPORTED for d or sizes as fa_fwd; MISALIGNED; LAUNCH. */
+int fa_merge(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b, void* o, float* lse,
+             int B, int H, int N, int d, hipStream_t stream);
+
 /* Measurement aid (not part of attention): the matrix-core calibration
  * kernel of the roofline harness.  Launches n_workgroups workgroups of
  * waves_per_workgroup (1..4) waves; each wave runs `iters` rounds of 16

@@ -297,9 +297,10 @@ def merge(o_a, lse_a, o_b, lse_b):
 
         O = exp(LSE_a - L) O_a + exp(LSE_b - L) O_b,   LSE = L.
 
-    o_a, o_b: [B, N, H, d]; lse_a, lse_b: [B, H, N].  A row that sees no key
-    in either range (both LSEs -inf) gets O = 0 and LSE = -inf; NaN
-    propagates.  Returns fp64 (O, LSE)."""
+    o_a, o_b: [B, N, H, d]; lse_a, lse_b: [B, H, N].  A range of weight 0
+    (LSE -inf) contributes nothing, whatever its O holds; a row that sees no
+    key in either range (both LSEs -inf) gets O = 0 and LSE = -inf; NaN in an
+    LSE propagates to its row.  Returns fp64 (O, LSE)."""
     la, lb = _f64(lse_a), _f64(lse_b)
     m = np.maximum(la, lb)                    # NaN in either stays NaN
     empty = m == -np.inf
@@ -309,5 +310,7 @@ def merge(o_a, lse_a, o_b, lse_b):
     lse = np.where(empty, -np.inf, ms + np.log(tot))
     wa = np.where(empty, 0.0, ea / tot).transpose(0, 2, 1)[..., None]   # [B, N, H, 1]
     wb = np.where(empty, 0.0, eb / tot).transpose(0, 2, 1)[..., None]
-    return wa * _f64(o_a) + wb * _f64(o_b), lse
+    ta = np.where(wa == 0, 0.0, wa * _f64(o_a))
+    tb = np.where(wb == 0, 0.0, wb * _f64(o_b))
+    return ta + tb, lse
 

@@ -146,6 +146,22 @@ int main(int argc, char** argv) {
            FA_ERR_SCRATCH);
     expect("noalloc max", (int)(fa_bwd_noalloc_max_workspace() == (size_t{16} << 20)), 1);
 
+    // merge of two results over disjoint key ranges
+    for (int i = 0; i < 6; ++i) {
+        void* p[6] = {F, F, F, F, F, F};
+        p[i] = nullptr;
+        auto call = [&](int B, int N, int d) {
+            return fa_merge(p[0], (const float*)p[1], p[2], (const float*)p[3], p[4], (float*)p[5], B, 2, N, d,
+                            nullptr);
+        };
+        expect("merge null", call(1, 8, 64), FA_ERR_INVALID_ARG);
+        p[i] = fake(4);
+        expect("merge misaligned", call(1, 8, 64), FA_ERR_MISALIGNED);
+        p[i] = F;
+        expect("merge d", call(1, 8, 96), FA_ERR_UNSUPPORTED);
+        expect("merge size INT_MAX", call(1 << 30, 1 << 30, 128), FA_ERR_UNSUPPORTED);
+    }
+
     // calibration and probe
     expect("calib null", fa_calibrate_mfma(nullptr, 4, 4, 10, 0, nullptr), FA_ERR_INVALID_ARG);
     expect("calib mode", fa_calibrate_mfma((float*)F, 4, 4, 10, 8, nullptr), FA_ERR_INVALID_ARG);

@@ -229,6 +229,25 @@ def test_missing_library_fails_loudly(tmp_path):
         binding._lib = saved
 
 
+def test_merge_argument_errors(lib):
+    """fa_merge checks its pointers, shape and alignment before any HIP call."""
+    V = ctypes.c_void_p
+    f = lib.fa_merge
+    ok = [V(FAKE)] * 6
+    for i in range(6):
+        p = list(ok)
+        p[i] = None
+        assert f(*p, 1, 1, 8, 64, None) == binding.FA_ERR_INVALID_ARG
+        p[i] = V(FAKE + 4)
+        assert f(*p, 1, 1, 8, 64, None) == binding.FA_ERR_MISALIGNED
+    assert f(*ok, 0, 1, 8, 64, None) == binding.FA_ERR_INVALID_ARG
+    assert f(*ok, 1, 1, 0, 64, None) == binding.FA_ERR_INVALID_ARG
+    for d in (0, 32, 96, 256):
+        assert f(*ok, 1, 1, 8, d, None) == binding.FA_ERR_UNSUPPORTED
+    assert f(*ok, 1, 8, 1 << 20, 128, None) == binding.FA_ERR_UNSUPPORTED
+    assert f(*ok, (1 << 31) - 1, (1 << 31) - 1, (1 << 31) - 1, 128, None) == binding.FA_ERR_UNSUPPORTED
+
+
 def test_calibration_argument_errors(lib):
     """fa_calibrate_mfma (the roofline harness's matrix-core calibration)
     rejects null or misaligned output and out-of-range counts before any

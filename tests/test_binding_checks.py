@@ -191,3 +191,43 @@ def test_valid_arguments_reach_the_library(lib):
         lib.backward(q, k, v, o, do, lse)
     with pytest.raises(AssertionError, match="fa_fwd"):
         lib.forward(q, k, v)
+
+
+def merge_args():
+    return bf(B, N, H, D), torch.zeros(B, H, N), bf(B, N, H, D), torch.zeros(B, H, N)
+
+
+@pytest.mark.parametrize("which", ["o_a", "o_b", "lse_a", "lse_b", "out", "lse_out"])
+@pytest.mark.parametrize("bad", ["dtype", "shape", "layout"])
+def test_merge_rejects_bad_tensors(lib, which, bad):
+    oa, la, ob, lb = merge_args()
+    kw = {}
+    if which in ("o_a", "o_b", "out"):
+        t = BAD_OUT[bad]((B, N, H, D))
+    else:
+        t = BAD_LSE[bad]()
+    args = {"o_a": oa, "lse_a": la, "o_b": ob, "lse_b": lb}
+    if which in args:
+        args[which] = t
+    else:
+        kw[which] = t
+    with pytest.raises(ValueError):
+        lib.merge(args["o_a"], args["lse_a"], args["o_b"], args["lse_b"], **kw)
+
+
+def test_merge_outputs_in_place_or_apart(lib):
+    """An output may be one of the inputs (accumulation in place) or apart
+    from them, never a partial overlap of one."""
+    oa, la, ob, lb = merge_args()
+    big = bf(2 * B, N, H, D)
+    with pytest.raises(ValueError, match="overlap"):
+        lib.merge(big[:B], la, ob, lb, out=big[1:B + 1])
+    lbig = torch.zeros(2 * B, H, N)
+    with pytest.raises(ValueError, match="overlap"):
+        lib.merge(oa, lbig[:B], ob, lb, lse_out=lbig[1:B + 1])
+    # in place and apart both get past validation (the stub refuses the launch)
+    with pytest.raises(AssertionError, match="fa_merge"):
+        lib.merge(oa, la, ob, lb, out=oa, lse_out=la)
+    with pytest.raises(AssertionError, match="fa_merge"):
+        lib.merge(oa, la, ob, lb)
+
