@@ -66,6 +66,10 @@ def parse():
                          "B4 H32 N4096 d128 and B1 H32 N16384 d128 causal, timed one by one, "
                          "with and without a 512 MiB overwrite between calls (outside the "
                          "timed region)")
+    ap.add_argument("--lse-merge", action="store_true",
+                    help="run only fa_merge (two attention results over disjoint key ranges "
+                         "combined through their LSEs) at B1 H32 N16384 d128, apart and in place, "
+                         "against the HBM bandwidth")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device-to-device copy of 1 GiB (3 times), the "
                          "reference for scaling HBM byte counters")
@@ -195,6 +199,40 @@ def mall_flush(torch, binding, inputs, workloads, seed, reps=50, warmup=10):
     return out
 
 
+# fa_merge: HBM-bound; its algorithmic bytes per launch read both O and both
+# LSE arrays and write one of each.
+MERGE_WORKLOAD = ("merge_b1_h32_n16384_d128", 1, 32, 16384, 128)
+
+
+def lse_merge(torch, binding):
+    """fa_merge at B1 H32 N16384 d128 (two 128 MiB bf16 O arrays and their
+    LSEs), timed like the other workloads, apart and in place, against the
+    HBM bandwidth (8 TB/s).  The counter-measured bytes per launch are
+    reported when profiles/traffic.json holds them for these sources."""
+    name, B, H, N, d = MERGE_WORKLOAD
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(3)
+    oa, ob = (torch.randn(B, N, H, d, generator=g, device=dev).to(torch.bfloat16) for _ in range(2))
+    la, lb = (torch.randn(B, H, N, generator=g, device=dev) * 4 for _ in range(2))
+    o, lse = torch.empty_like(oa), torch.empty_like(la)
+    algo = 3 * oa.numel() * 2 + 3 * la.numel() * 4
+    out = {"workload": name, "algorithmic_bytes": algo}
+    for tag, f in (("apart", lambda: binding.merge(oa, la, ob, lb, out=o, lse_out=lse)),
+                   ("in_place", lambda: binding.merge(oa, la, ob, lb, out=oa, lse_out=la))):
+        ms = median_ms(torch, f)
+        gbps = algo / (ms * 1e-3) / 1e9
+        out[tag] = {"ms": round(ms, 4), "gbps": round(gbps, 1), "frac_of_hbm": round(gbps / PEAK_HBM_GBS, 4)}
+    out["traffic"] = measured_traffic("merge", name)
+    # the practical HBM rate on the same box: torch's device copy of 256 MiB
+    # (reads and writes 256 MiB each)
+    src = torch.ones(1 << 28, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    ms = median_ms(torch, lambda: dst.copy_(src))
+    gbps = 2 * src.numel() / (ms * 1e-3) / 1e9
+    out["copy_reference"] = {"ms": round(ms, 4), "gbps": round(gbps, 1), "frac_of_hbm": round(gbps / PEAK_HBM_GBS, 4)}
+    return out
+
+
 def mfma_calibration(torch, binding, iters=4000, launches=10):
     """Sustained rate of the calibration kernel (fa_calibrate_mfma): eight
     independent chains of 32x32x16 bf16 MFMAs per wave, back to back, against
@@ -233,6 +271,7 @@ KERNELS = {
     "fwd": ("fa_fwd.hip", "fa_common.h", "fa_schedule.hip"),
     "bwd_dkdv": ("fa_bwd.hip", "fa_common.h", "fa_schedule.hip"),
     "bwd_dq": ("fa_bwd.hip", "fa_common.h", "fa_schedule.hip"),
+    "merge": ("fa_merge.hip", "fa_common.h"),
 }
 
 
@@ -489,6 +528,10 @@ def main():
     if args.mall_flush:
         print(json.dumps({"mall_flush": mall_flush(torch, binding, inputs, workloads, args.seed),
                           "flush_bytes": FLUSH_BYTES, "unit": "ms", "dtype": "bf16"}), flush=True)
+        return
+    if args.lse_merge:
+        print(json.dumps({"lse_merge": lse_merge(torch, binding), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                          "dtype": "bf16"}), flush=True)
         return
     if args.fp8_forward:
         print(json.dumps({"fp8_forward": fp8_workloads(torch, binding, inputs, workloads, args.seed),

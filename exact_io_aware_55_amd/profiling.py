@@ -30,6 +30,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -40,6 +41,7 @@ STAGES = {
     "bwd_preprocess": ("fa::bwd_pre_kernel", ("fa_bwd.hip", "fa_common.h")),
     "bwd_dkdv": ("fa::bwd_dkdv_kernel", ("fa_bwd.hip", "fa_common.h", "fa_schedule.hip")),
     "bwd_dq": ("fa::bwd_dq_kernel", ("fa_bwd.hip", "fa_common.h", "fa_schedule.hip")),
+    "merge": ("fa::merge_kernel", ("fa_merge.hip", "fa_common.h")),
 }
 
 
@@ -60,6 +62,20 @@ def _one(pattern):
 
 
 def _short(name):
+    """Kernel name without its return type and parameter list.  A name the
+    profiler left mangled (fa::<ident><integer or bool template arguments>)
+    is read into the same form."""
+    m = re.match(r"_ZN2fa(\d+)", name)
+    if m:
+        n = int(m.group(1))
+        ident, rest = name[m.end():m.end() + n], name[m.end() + n:]
+        t = re.match(r"I((?:L[ib]\d+E)+)E", rest)
+        args = ""
+        if t:
+            vals = [("true" if v == "1" else "false") if k == "b" else v
+                    for k, v in re.findall(r"L([ib])(\d+)E", t.group(1))]
+            args = "<" + ", ".join(vals) + ">"
+        return f"fa::{ident}{args}"
     return name.split("(")[0].replace("void ", "").strip()
 
 
@@ -389,6 +405,48 @@ def calibration(rates_json, mfma_dir, out):
         fh.write("\n".join(lines) + "\n")
 
 
+MERGE_ARGS = "--lse-merge"
+
+
+def merge_profile(trace_dir, fetch, write, copy_fetch, copy_write, out, workload="merge_b1_h32_n16384_d128"):
+    """fa_merge's kernel time (trace) and HBM bytes (FETCH_SIZE / WRITE_SIZE
+    scaled by the copy calibration) against its algorithmic bytes: both O
+    arrays and both LSE arrays read, one of each written."""
+    shape = {p[0]: int(p[1:]) for p in workload.split("_") if p[:1] in "bhnd" and p[1:].isdigit()}
+    B, H, N, d = shape["b"], shape["h"], shape["n"], shape["d"]
+    algo = 3 * B * N * H * d * 2 + 3 * B * H * N * 4
+    stats = [r for r in csv.DictReader(open(_one(os.path.join(trace_dir, "**", "*kernel_stats.csv"))))
+             if _short(r["Name"]).startswith(STAGES["merge"][0])]
+    fs, ws, lines = traffic(fetch, write, copy_fetch, copy_write, out, workload, {"merge": algo})
+    head = [f"# fa_merge (two attention results over disjoint key ranges), {workload}", "",
+            "Commands (from the repository root on one MI355X, after `cd /tmp && export TMPDIR=/tmp`; "
+            "`$REPO` is the repository root, `$OUT` the folder that receives the profiler output):", "",
+            "```",
+            f"rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/prof -o merge -- python3 $REPO/bench.py {MERGE_ARGS}",
+            f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d $OUT/pmc_fetch -o merge -- python3 $REPO/bench.py {MERGE_ARGS}",
+            f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d $OUT/pmc_write -o merge -- python3 $REPO/bench.py {MERGE_ARGS}",
+            "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $OUT/pmc_copy_fetch -o copy -- "
+            "python3 $REPO/bench.py --copy-calibration",
+            "rocprofv3 --pmc WRITE_SIZE --output-format csv -d $OUT/pmc_copy_write -o copy -- "
+            "python3 $REPO/bench.py --copy-calibration",
+            "python -m exact_io_aware_55_amd.profiling merge $OUT/prof $OUT/pmc_fetch $OUT/pmc_write "
+            "$OUT/pmc_copy_fetch $OUT/pmc_copy_write profiles/<this file>",
+            "```", "",
+            f"Algorithmic bytes per launch: {algo / 1e6:.1f} MB (two bf16 O arrays and two fp32 LSE arrays "
+            "read, one of each written).  Counter bytes: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) "
+            f"scaled by a plain 1 GiB copy's (x{fs:.4f} and x{ws:.4f}).", "",
+            "| kernel | calls traced | average (us) | GB/s (algorithmic) | of 8 TB/s |", "|---|---|---|---|---|"]
+    for r in stats:
+        t = float(r["AverageNs"])
+        gbps = algo / t
+        head.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {t / 1e3:.1f} | {gbps:.0f} | "
+                    f"{100 * gbps / 8000:.1f}% |")
+    head += ["", "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | read MB (scaled) | written MB | algorithmic MB | "
+             "measured / algorithmic |", "|---|---|---|---|---|---|---|"]
+    with open(out, "w") as fh:
+        fh.write("\n".join(head + lines) + "\n")
+
+
 def main(argv):
     if len(argv) >= 5 and argv[0] == "trace":
         trace(argv[1], argv[2], argv[3], argv[4])
@@ -402,6 +460,8 @@ def main(argv):
         scaling(argv[1], argv[2], argv[3], int(argv[4]), int(argv[5]), int(argv[6]), runs)
     elif len(argv) >= 5 and argv[0] == "valu":
         valu(argv[1], argv[2], argv[3], argv[4], *argv[5:6])
+    elif len(argv) >= 7 and argv[0] == "merge":
+        merge_profile(*argv[1:7])
     elif len(argv) >= 4 and argv[0] == "calibration":
         calibration(argv[1], argv[2], argv[3])
     elif len(argv) >= 7 and argv[0] == "traffic":
