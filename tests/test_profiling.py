@@ -87,3 +87,15 @@ def test_compulsory_bytes_forward():
     # Q, K, V read and O written (bf16) plus one fp32 statistic per row
     t = 4 * 4096 * 32 * 128 * 2
     assert profiling.compulsory_bytes(4, 32, 4096, 128, False)["fwd"] == 4 * t + 4 * 32 * 4096 * 4
+
+
+def test_kernel_names_mangled_or_not():
+    """The profiler demangles most kernel names but can leave one mangled;
+    both forms map to the same short name, so a stage's kernel is found
+    either way."""
+    assert profiling._short("void fa::fwd_bf16_kernel<128, true, false>(int, float)") == \
+        "fa::fwd_bf16_kernel<128, true, false>"
+    assert profiling._short("_ZN2fa12merge_kernelILi128EEEvPKDF16bPKfS2_S4_PDF16bPfiil") == "fa::merge_kernel<128>"
+    assert profiling._short("_ZN2fa15bwd_dkdv_kernelILi64ELb1ELb0EEEvPKDF16b") == \
+        "fa::bwd_dkdv_kernel<64, true, false>"
+    assert profiling._short("_ZN2fa12merge_kernelILi64EEEv").startswith(profiling.STAGES["merge"][0])
