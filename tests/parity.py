@@ -23,17 +23,6 @@ def rel_l2(got, ref):
     return float(num / den) if den > 0 else float(num)
 
 
-def assert_bf16_close(got, ref, what="", terms=1):
-    """Fixed bf16 tolerances.  ``terms``: the output is a sum of that many
-    per-head gradients (a K/V head shared by a group of query heads); the
-    max-abs bound is per head, so it applies to the group mean (the sum's
-    bound scales by ``terms``), and the scale-free relative L2 is unchanged."""
-    ma, rl = max_abs(got, ref), rel_l2(got, ref)
-    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
-    assert ma <= BF16_MAX_ABS * terms and rl <= BF16_REL_L2, f"{what}: max_abs={ma:.3e} rel_l2={rl:.3e}"
-    return ma, rl
-
-
 def assert_lse_close(got, ref, what=""):
     ma = max_abs(got, ref)
     assert ma <= LSE_MAX_ABS, f"{what}: lse max_abs={ma:.3e}"
