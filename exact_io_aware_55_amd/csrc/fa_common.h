@@ -153,12 +153,6 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ u32x4 ld_global16(const void* p) {
     return *reinterpret_cast<const u32x4*>(p);
 }
-__device__ __forceinline__ void st_lds16(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
-__device__ __forceinline__ void st_lds8(void* p, const u32x2& v) { *reinterpret_cast<u32x2*>(p) = v; }
-__device__ __forceinline__ void st_lds4(void* p, uint32_t v) { *reinterpret_cast<uint32_t*>(p) = v; }
-__device__ __forceinline__ bf16x8 ld_lds_bf16x8(const void* p) {
-    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
-}
 // LDS (address space 3) byte pointers, for reads whose offsets should fold
 // into the instruction's immediate field
 typedef __attribute__((address_space(3))) char lds_char;
@@ -253,11 +247,6 @@ __device__ __forceinline__ float halves_sum(float x) {
                                                     __builtin_bit_cast(unsigned, x), false, false);
     return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
 }
-
-// XOR swizzle of 16-byte chunks within a 128-byte LDS row (8 chunks): keeps
-// 16-lane 128-bit reads of one logical chunk from consecutive rows on
-// distinct banks, for both 32- and 64-bank LDS organisations.
-__device__ __forceinline__ int swz8(int row) { return (row ^ (row >> 3)) & 7; }
 
 // Swizzle of 16-byte chunks in 64-byte LDS rows for tiles read both ways:
 // 16 bytes per lane down 32 consecutive rows (ds_read_b128) and transposed
