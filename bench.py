@@ -647,6 +647,8 @@ def main():
     if not args.no_extra:
         out["other_workloads"] = other_workloads(torch, binding, inputs, workloads, args.seed)
         out["fp8_forward"] = fp8_workloads(torch, binding, inputs, workloads, args.seed)
+        out["lse_merge"] = lse_merge(torch, binding)
+        torch.cuda.empty_cache()
         out["mfma_calibration"] = mfma_calibration(torch, binding, launches=4)
 
     if not args.no_naive:
