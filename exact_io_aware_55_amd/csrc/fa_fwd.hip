@@ -188,16 +188,13 @@ __global__ __launch_bounds__(fwd::NT, D == 64 ? 4 : 1) void fwd_bf16_kernel(
     // flight), make every wave's part visible (the barrier also retires all
     // reads of block t - 1, whose stage the loads of block t + 2 refill), then
     // S^T = K Q^T, the online softmax and O^T += V^T P^T.
-    auto block = [&](int t, auto mask_tag) {
+    // NL: the block's first NL 32-key tiles are computed; on a masked causal
+    // block the tiles whose keys all follow the wave's last query are
+    // invisible to every query of the wave and are skipped (their P is 0)
+    auto block = [&](int t, auto mask_tag, auto nl_tag) {
         constexpr bool MASK = decltype(mask_tag)::value;
-        FA_WAIT_VMCNT((NSTAGE - 2) * 2 * SEG_W);
-        __builtin_amdgcn_s_barrier();
-        FA_SYNC_POINT();
-        if constexpr (MASK) issue_tile(t + NSTAGE - 1);  // masked blocks may return early
-
+        constexpr int NL = decltype(nl_tag)::value;
         const int j0 = t * BC;
-        // every key after this wave's queries, or before all of their windows
-        if (MASK && CAUSAL && (j0 > qw + 31 || j0 + BC - 1 < qw - window + 1)) return;
         // per-iteration bases; the empty asm keeps the compiler from
         // hoisting base + offset sums into separate registers, so the
         // offsets fold into the LDS instructions
@@ -207,17 +204,17 @@ __global__ __launch_bounds__(fwd::NT, D == 64 ? 4 : 1) void fwd_bf16_kernel(
         const lds_char* vb = stage + v_rd;
         asm volatile("" : "+v"(kb0), "+v"(kb1), "+v"(vb));
         // S^T = K Q^T for the block's 32-key tiles
-        // feature-chunk major: KT independent accumulator chains, and the K
+        // feature-chunk major: NL independent accumulator chains, and the K
         // operands of chunk c + 1 read while the products of chunk c run
-        f32x16 s[KT];
-        bf16x8 kop[2][KT];
+        f32x16 s[NL];
+        bf16x8 kop[2][NL];
         auto read_k = [&](int c, bf16x8* dst) {
 #pragma unroll
-            for (int kt = 0; kt < KT; ++kt)
+            for (int kt = 0; kt < NL; ++kt)
                 dst[kt] = lds_read_b128(((c & 1) ? kb1 : kb0) + (c >> 1) * SUB + kt * 32 * 64);
         };
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt) s[kt] = f32x16{};
+        for (int kt = 0; kt < NL; ++kt) s[kt] = f32x16{};
         read_k(0, kop[0]);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -225,7 +222,7 @@ __global__ __launch_bounds__(fwd::NT, D == 64 ? 4 : 1) void fwd_bf16_kernel(
             if (c + 1 < DC) read_k(c + 1, kop[(c + 1) & 1]);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int kt = 0; kt < KT; ++kt) s[kt] = mfma32x32x16(kop[c & 1][kt], qreg[c], s[kt]);
+            for (int kt = 0; kt < NL; ++kt) s[kt] = mfma32x32x16(kop[c & 1][kt], qreg[c], s[kt]);
             __builtin_amdgcn_sched_barrier(0);
         }
         // unmasked blocks start the loads of block t + NSTAGE - 1 here,
@@ -241,7 +238,7 @@ __global__ __launch_bounds__(fwd::NT, D == 64 ? 4 : 1) void fwd_bf16_kernel(
         // is exactly 0 (also when scale == 0)
         const float m_sub = m_run == -INFINITY ? 0.f : m_run;
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt)
+        for (int kt = 0; kt < NL; ++kt)
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[kt][r] = __builtin_fmaf(s[kt][r], scale_log2, -m_sub);
         // A masked block masks only the waves that do not see all of it:
@@ -257,7 +254,7 @@ __global__ __launch_bounds__(fwd::NT, D == 64 ? 4 : 1) void fwd_bf16_kernel(
                 const int lim_c = my_q - j0 - 4 * hl;     // causal: off <= lim_c
                 const int lim_w = lim_c - window + 1;     // window: off >= lim_w
 #pragma unroll
-                for (int kt = 0; kt < KT; ++kt)
+                for (int kt = 0; kt < NL; ++kt)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int off = kt * 32 + (r >> 2) * 8 + (r & 3);
@@ -268,12 +265,12 @@ __global__ __launch_bounds__(fwd::NT, D == 64 ? 4 : 1) void fwd_bf16_kernel(
         }
         // P = exp2(x): the row sum accumulates the fp32 values (so LSE keeps
         // fp32 accuracy), the PV product uses P rounded to bf16
-        u32x4 pw[2 * KT];
+        u32x4 pw[2 * NL];
         float ls0, ls1;
         auto exps = [&]() {
             float la[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kt = 0; kt < KT; ++kt)
+            for (int kt = 0; kt < NL; ++kt)
 #pragma unroll
                 for (int r = 0; r < 16; r += 2) {
                     const float p0 = fast_exp2(s[kt][r]);
@@ -301,14 +298,14 @@ __global__ __launch_bounds__(fwd::NT, D == 64 ? 4 : 1) void fwd_bf16_kernel(
             for (int i = 0; i < DT; ++i) oacc[i] *= alpha;
             const float delta = m_new == -INFINITY ? 0.f : m_new - m_sub;
 #pragma unroll
-            for (int kt = 0; kt < KT; ++kt)
+            for (int kt = 0; kt < NL; ++kt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) s[kt][r] -= delta;
         };
         auto block_max = [&]() {
             float mx = s[0][0];
 #pragma unroll
-            for (int kt = 0; kt < KT; ++kt)
+            for (int kt = 0; kt < NL; ++kt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
             return halves_max(mx);
@@ -344,8 +341,8 @@ __global__ __launch_bounds__(fwd::NT, D == 64 ? 4 : 1) void fwd_bf16_kernel(
         read_v(0, vop[0]);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int cc = 0; cc < 2 * KT; ++cc) {
-            if (cc + 1 < 2 * KT) read_v(cc + 1, vop[(cc + 1) & 1]);
+        for (int cc = 0; cc < 2 * NL; ++cc) {
+            if (cc + 1 < 2 * NL) read_v(cc + 1, vop[(cc + 1) & 1]);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt)
@@ -354,12 +351,36 @@ __global__ __launch_bounds__(fwd::NT, D == 64 ? 4 : 1) void fwd_bf16_kernel(
         }
         __builtin_amdgcn_sched_barrier(0);
     };
+    auto step = [&](int t, auto mask_tag) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        FA_WAIT_VMCNT((NSTAGE - 2) * 2 * SEG_W);
+        __builtin_amdgcn_s_barrier();
+        FA_SYNC_POINT();
+        if constexpr (MASK) issue_tile(t + NSTAGE - 1);  // masked blocks may return early
+
+        const int j0 = t * BC;
+        // every key after this wave's queries, or before all of their windows
+        if (MASK && CAUSAL && (j0 > qw + 31 || j0 + BC - 1 < qw - window + 1)) return;
+        if constexpr (MASK && CAUSAL) {
+            const int nl = min(KT, (qw + 31 - j0) / 32 + 1);   // >= 1 after the test above
+            if (nl >= KT) block(t, mask_tag, flag_int<KT>{});
+            else if constexpr (KT == 4) {
+                if (nl == 3) block(t, mask_tag, flag_int<3>{});
+                else if (nl == 2) block(t, mask_tag, flag_int<2>{});
+                else block(t, mask_tag, flag_int<1>{});
+            } else {
+                block(t, mask_tag, flag_int<1>{});
+            }
+        } else {
+            block(t, mask_tag, flag_int<KT>{});
+        }
+    };
 #pragma clang loop unroll(disable)
-    for (int t = t_lo; t < t_ulo; ++t) block(t, std::true_type{});
+    for (int t = t_lo; t < t_ulo; ++t) step(t, std::true_type{});
 #pragma clang loop unroll(disable)
-    for (int t = t_ulo; t < t_uhi; ++t) block(t, std::false_type{});
+    for (int t = t_ulo; t < t_uhi; ++t) step(t, std::false_type{});
 #pragma clang loop unroll(disable)
-    for (int t = t_uhi; t < ntiles; ++t) block(t, std::true_type{});
+    for (int t = t_uhi; t < ntiles; ++t) step(t, std::true_type{});
     FA_WAIT_VMCNT(0);                          // the loads past the last block
 
     // ---- epilogue: O = O / l, LSE = m ln2 + ln l ----
