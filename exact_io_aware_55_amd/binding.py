@@ -397,3 +397,30 @@ def backward_steps(q, k, v, o, do, lse, causal=False, scale=None, workspace=None
     for call in calls:
         call()
     return (dq, dk, dv), calls
+
+
+class _Attention(torch.autograd.Function):
+    """forward / backward of the library as one autograd node: O is
+    returned; the backward consumes O and LSE saved from the forward."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, causal, scale, window):
+        o, lse = forward(q, k, v, causal=causal, scale=scale, window=window)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.causal, ctx.scale, ctx.window = causal, scale, window
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse = ctx.saved_tensors
+        dq, dk, dv = backward(q, k, v, o, do.contiguous(), lse, causal=ctx.causal, scale=ctx.scale,
+                              window=ctx.window)
+        return dq, dk, dv, None, None, None
+
+
+def attention(q, k, v, causal=False, scale=None, window=None):
+    """O of :func:`forward` as a differentiable torch operation: gradients
+    with respect to q, k and v come from :func:`backward` (grouped-query
+    attention and sliding windows as there).  bf16 [B,N,H,d] tensors."""
+    return _Attention.apply(q, k, v, bool(causal) or window is not None, scale, window)
+
