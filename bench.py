@@ -223,7 +223,7 @@ def lse_merge(torch, binding):
         gbps = algo / (ms * 1e-3) / 1e9
         out[tag] = {"ms": round(ms, 4), "gbps": round(gbps, 1), "frac_of_hbm": round(gbps / PEAK_HBM_GBS, 4)}
     out["traffic"] = measured_traffic("merge", name)
-    # the practical HBM rate on the same box: torch's device copy of 256 MiB
+    # the practical HBM rate on the same GPU: torch's device copy of 256 MiB
     # (reads and writes 256 MiB each)
     src = torch.ones(1 << 28, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
