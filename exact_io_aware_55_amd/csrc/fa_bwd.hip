@@ -288,8 +288,8 @@ __global__ __launch_bounds__(bwd::NT, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     const int a_rd0 = l32 * 64 + ((hl ^ dual_swz(l32)) << 4);        // Q/dO rows, even c
     const int a_rd1 = l32 * 64 + (((2 + hl) ^ dual_swz(l32)) << 4);  // odd c
 
-#pragma clang loop unroll(disable)
-    for (int it = 0; it < nst_all; ++it) {
+    // One query step (its position it in the sweep), masked or not.
+    auto step = [&](int it, auto masked) {
         // 3 stages: this step's loads are done once at most one step's loads
         // are in flight; after the barrier nobody reads the stage of step
         // it - 1, which the loads of step it + 2 (spread over the units below)
@@ -450,7 +450,33 @@ __global__ __launch_bounds__(bwd::NT, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
                 __builtin_amdgcn_sched_barrier(0);
             });
         };
-        body(flag_t<CAUSAL>{});
+        body(masked);
+    };
+    if constexpr (CAUSAL) {
+        // Only two kinds of step need the mask's compares and select: those
+        // whose queries start before the block's last key (one of them can
+        // precede a key; the first nm steps of each query head's range), and
+        // with a window those whose last query lies window rows or more past
+        // the block's first key (from step sw on).  The others run in loops
+        // of their own without it (one body per loop: no register copies).
+        // When the sweep runs from the last query block down (never with a
+        // window) the nm diagonal steps come last.
+        const int nm = min(nst, (k0 + KB - 2) / BR - first + 1);
+        const int sw = WIN ? min(nst, max(nm, (k0 + window) / BR - first)) : nst;
+        for (int gi = 0; gi < G; ++gi) {
+            const int base = gi * nst;
+            const int u_lo = base + (rev ? 0 : nm);           // unmasked steps [u_lo, u_hi)
+            const int u_hi = base + (rev ? nst - nm : sw);
+#pragma clang loop unroll(disable)
+            for (int it = base; it < u_lo; ++it) step(it, flag_t<true>{});
+#pragma clang loop unroll(disable)
+            for (int it = u_lo; it < u_hi; ++it) step(it, flag_t<false>{});
+#pragma clang loop unroll(disable)
+            for (int it = u_hi; it < base + nst; ++it) step(it, flag_t<true>{});
+        }
+    } else {
+#pragma clang loop unroll(disable)
+        for (int it = 0; it < nst_all; ++it) step(it, flag_t<false>{});
     }
     FA_WAIT_VMCNT(0);                          // the loads past the last step
     // the accumulators are read below by VALU after MFMAs the compiler does
