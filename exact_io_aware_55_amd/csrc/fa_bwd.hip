@@ -173,7 +173,6 @@ __global__ __launch_bounds__(bwd::NT, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     const int k0 = kb * KB;
     const int key_local = wave * 32 + l32;
     const int my_key = k0 + key_local;         // key of this lane in S / P / dS
-    const bool key_ok = my_key < N;
 
     // transposing-read lane pattern: rows R_w = 4 (tg >> 1) + (tj >> 2) (+8 for
     // the second read), 8 bytes at column 16 (tg & 1) + 4 (tj & 3) of a 32-wide
@@ -484,24 +483,27 @@ __global__ __launch_bounds__(bwd::NT, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     FA_MFMA_DRAIN();
 
     // epilogue: dK = scale * (dK^T)^T, dV; C layout of dV^T / dK^T: lane = key
-    // column, registers = feature rows 8g + 4h + t
-    if (key_ok) {
-        __bf16* dkr = dK + kv_off + (long)my_key * kv_stride;
-        __bf16* dvr = dV + kv_off + (long)my_key * kv_stride;
+    // column, registers = feature rows 8g + 4h + t.  Both go out through the
+    // wave's part of the ring, whole rows per store.
+    static_assert(NW * 2 * RowStage<D>::BYTES <= RING, "row staging fits in the ring");
+    __syncthreads();                           // every wave is done with the ring
+    char* rk = smem + wave * 2 * RowStage<D>::BYTES;
+    char* rv = rk + RowStage<D>::BYTES;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int d = dt * 32 + g * 8 + hl * 4;
-                const f32x16& kk = dkacc[dt];
-                const f32x16& vv = dvacc[dt];
-                *reinterpret_cast<u32x2*>(dkr + d) =
-                    u32x2{pack_bf16x2(kk[g * 4] * scale, kk[g * 4 + 1] * scale),
-                          pack_bf16x2(kk[g * 4 + 2] * scale, kk[g * 4 + 3] * scale)};
-                *reinterpret_cast<u32x2*>(dvr + d) =
-                    u32x2{pack_bf16x2(vv[g * 4], vv[g * 4 + 1]), pack_bf16x2(vv[g * 4 + 2], vv[g * 4 + 3])};
-            }
-    }
+        for (int g = 0; g < 4; ++g) {
+            const f32x16& kk = dkacc[dt];
+            const f32x16& vv = dvacc[dt];
+            RowStage<D>::put(rk, dt * 4 + g,
+                             u32x2{pack_bf16x2(kk[g * 4] * scale, kk[g * 4 + 1] * scale),
+                                   pack_bf16x2(kk[g * 4 + 2] * scale, kk[g * 4 + 3] * scale)});
+            RowStage<D>::put(rv, dt * 4 + g,
+                             u32x2{pack_bf16x2(vv[g * 4], vv[g * 4 + 1]), pack_bf16x2(vv[g * 4 + 2], vv[g * 4 + 3])});
+        }
+    const int kw = k0 + wave * 32;             // first key of this wave
+    RowStage<D>::store(rk, dK + kv_off + (long)kw * kv_stride, kv_stride, N - kw);
+    RowStage<D>::store(rv, dV + kv_off + (long)kw * kv_stride, kv_stride, N - kw);
 }
 
 // ---------------------------------------------------------------------------
@@ -805,19 +807,19 @@ __global__ __launch_bounds__(bwdq::NT, 1) void bwd_dq_kernel(
     }
     FA_WAIT_VMCNT(0);                          // the loads past the last tile
 
-    // epilogue: dQ = scale * dQ^T^T -> bf16; lane = query, registers = features
-    if (my_q < N) {
-        __bf16* dst = dQ + head_off + (long)my_q * row_stride;
+    // epilogue: dQ = scale * dQ^T^T -> bf16; lane = query, registers = features;
+    // out through the wave's part of the ring, whole rows per store
+    static_assert(NW * RowStage<D>::BYTES <= NSTAGE * STAGE, "row staging fits in the ring");
+    __syncthreads();                           // every wave is done with the ring
+    char* rs = smem + wave * RowStage<D>::BYTES;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int d = dt * 32 + g * 8 + hl * 4;
-                *reinterpret_cast<u32x2*>(dst + d) =
-                    u32x2{pack_bf16x2(dqacc[dt][g * 4] * scale, dqacc[dt][g * 4 + 1] * scale),
-                          pack_bf16x2(dqacc[dt][g * 4 + 2] * scale, dqacc[dt][g * 4 + 3] * scale)};
-            }
-    }
+        for (int g = 0; g < 4; ++g)
+            RowStage<D>::put(rs, dt * 4 + g,
+                             u32x2{pack_bf16x2(dqacc[dt][g * 4] * scale, dqacc[dt][g * 4 + 1] * scale),
+                                   pack_bf16x2(dqacc[dt][g * 4 + 2] * scale, dqacc[dt][g * 4 + 3] * scale)});
+    RowStage<D>::store(rs, dQ + head_off + (long)qw * row_stride, row_stride, N - qw);
 }
 
 int bwd_rows_padded(int N) { return (N + bwd::ROWPAD - 1) / bwd::ROWPAD * bwd::ROWPAD; }

@@ -167,6 +167,57 @@ __device__ __forceinline__ const lds_char* as_lds(const void* p) {
 }
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
 
+// Row-major bf16 output through LDS.  A wave holds 32 rows x D features with
+// one row per lane (lane & 31) and, of 16-byte chunk c (features 8c .. 8c + 7),
+// the four features 8c + 4 (lane >> 5) .. + 3 in registers: the layout of a
+// transposed 32x32 MFMA result.  Stored from there, each store instruction
+// would put 16 bytes into each of 32 rows, and the L2 may write a 128-byte
+// line back before its other pieces arrive (partial writes that add bytes,
+// depending on timing).  So the rows go to the wave's LDS region (chunks
+// XOR-swizzled by the row, so that the 32 rows of one chunk hit different
+// banks) and come back with D / 8 lanes per row: every store instruction then
+// writes whole rows.  The region must not be in use by other waves.
+template <int D>
+struct RowStage {
+    static constexpr int BYTES = 32 * D * 2;   // LDS bytes per wave
+    static constexpr int NCH = D / 8;          // 16-byte chunks per row
+    static constexpr int RPI = 64 / NCH;       // rows per store instruction
+    __device__ __forceinline__ static int swz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+    __device__ __forceinline__ static int at(int r, int c) { return r * (2 * D) + ((c ^ swz(r)) << 4); }
+    // The lane index is formed afresh (mbcnt) in put and store, so that no
+    // value derived from it has to stay live, or spill, through the main loop.
+    __device__ __forceinline__ static int lane_id() {
+        return (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    }
+    // the lane's 8 bytes of chunk c of its row
+    __device__ __forceinline__ static void put(void* region, int c, u32x2 v) {
+        const int lane = lane_id();
+        auto p = (__attribute__((address_space(3))) char*)(region) + at(lane & 31, c) + ((lane >> 5) << 3);
+        *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(p) = v;
+    }
+    // rows 0 .. nrows - 1 to dst + r * stride elements; nrows is the same
+    // for the whole wave (all LDS reads are issued before the first store)
+    __device__ __forceinline__ static void store(const void* region, __bf16* dst, long stride, int nrows) {
+        constexpr int NI = 32 / RPI;
+        const int lane = lane_id();
+        const int rr = lane / NCH, c = lane % NCH;
+        u32x4 v[NI];
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+            v[i] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+                as_lds(region) + at(i * RPI + rr, c));
+        __bf16* p = dst + (long)rr * stride + 8 * c;
+        if (nrows >= 32) {
+#pragma unroll
+            for (int i = 0; i < NI; ++i) *reinterpret_cast<u32x4*>(p + (long)i * RPI * stride) = v[i];
+        } else {
+#pragma unroll
+            for (int i = 0; i < NI; ++i)
+                if (i * RPI + rr < nrows) *reinterpret_cast<u32x4*>(p + (long)i * RPI * stride) = v[i];
+        }
+    }
+};
+
 // 16-byte direct global -> LDS load (global_load_lds_dwordx4): every lane
 // reads 16 bytes at base + offset and the wave writes them to LDS at
 // lds_base + 16 * lane.  Issued through asm so the compiler does not order

@@ -386,19 +386,21 @@ __global__ __launch_bounds__(fwd::NT, D == 64 ? 4 : 1) void fwd_bf16_kernel(
     // ---- epilogue: O = O / l, LSE = m ln2 + ln l ----
     const float l_tot = halves_sum(l_run);
     const float inv = 1.f / l_tot;
-    if (my_q < N) {
-        __bf16* dst = O + head_off + (long)my_q * row_stride;
+    // O rows through the wave's part of the ring, whole rows per store
+    // (rows past N hold finite or non-finite values and are not stored)
+    static_assert(NW * RowStage<D>::BYTES <= NSTAGE * STAGE, "row staging fits in the ring");
+    __syncthreads();                           // every wave is done with the ring
+    char* rs = smem + wave * RowStage<D>::BYTES;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int d = dt * 32 + g * 8 + hl * 4;
-                const uint32_t w0 = pack_bf16x2(oacc[dt][g * 4 + 0] * inv, oacc[dt][g * 4 + 1] * inv);
-                const uint32_t w1 = pack_bf16x2(oacc[dt][g * 4 + 2] * inv, oacc[dt][g * 4 + 3] * inv);
-                *reinterpret_cast<u32x2*>(dst + d) = u32x2{w0, w1};
-            }
-        if (hl == 0) LSE[(long)bh * N + my_q] = m_run * kLn2 + __logf(l_tot);
-    }
+        for (int g = 0; g < 4; ++g) {
+            const uint32_t w0 = pack_bf16x2(oacc[dt][g * 4 + 0] * inv, oacc[dt][g * 4 + 1] * inv);
+            const uint32_t w1 = pack_bf16x2(oacc[dt][g * 4 + 2] * inv, oacc[dt][g * 4 + 3] * inv);
+            RowStage<D>::put(rs, dt * 4 + g, u32x2{w0, w1});
+        }
+    RowStage<D>::store(rs, O + head_off + (long)qw * row_stride, row_stride, N - qw);
+    if (my_q < N && hl == 0) LSE[(long)bh * N + my_q] = m_run * kLn2 + __logf(l_tot);
 }
 
 // ---------------------------------------------------------------------------

@@ -94,7 +94,11 @@ __global__ __launch_bounds__(fwd8::NT, 1) void fwd_fp8_kernel(
     constexpr int KP = BC / 64;                // 64-key P V products per feature tile
     static_assert((2 * SEGS) % NW == 0 && NL >= 1, "segments per wave");
     static_assert(NL <= 15, "vmcnt immediate");
-    __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * STAGE + 1024];
+    // the ring, then 1 KB for the direct loads past the last block; at least
+    // the epilogue's row staging (32 KB at d = 64, more than that ring)
+    constexpr int SMEM = NSTAGE * STAGE + 1024 > NW * RowStage<D>::BYTES ? NSTAGE * STAGE + 1024
+                                                                         : NW * RowStage<D>::BYTES;
+    __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -326,19 +330,19 @@ __global__ __launch_bounds__(fwd8::NT, 1) void fwd_fp8_kernel(
     // ---- epilogue: O = descale_v * O / l, LSE = m ln2 + ln l ----
     const float l_tot = halves_sum(l_run);
     const float f = dv / l_tot;
-    if (my_q < N) {
-        __bf16* dst = O + head_off + (long)my_q * row_stride;
+    // O rows through the wave's part of the LDS, whole rows per store
+    __syncthreads();                           // every wave is done with the ring
+    char* rs = smem + wave * RowStage<D>::BYTES;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int d = dt * 32 + g * 8 + hl * 4;
-                const uint32_t w0 = pack_bf16x2(oacc[dt][g * 4 + 0] * f, oacc[dt][g * 4 + 1] * f);
-                const uint32_t w1 = pack_bf16x2(oacc[dt][g * 4 + 2] * f, oacc[dt][g * 4 + 3] * f);
-                *reinterpret_cast<u32x2*>(dst + d) = u32x2{w0, w1};
-            }
-        if (hl == 0) LSE[(long)bh * N + my_q] = m_run * kLn2 + __logf(l_tot);
-    }
+        for (int g = 0; g < 4; ++g) {
+            const uint32_t w0 = pack_bf16x2(oacc[dt][g * 4 + 0] * f, oacc[dt][g * 4 + 1] * f);
+            const uint32_t w1 = pack_bf16x2(oacc[dt][g * 4 + 2] * f, oacc[dt][g * 4 + 3] * f);
+            RowStage<D>::put(rs, dt * 4 + g, u32x2{w0, w1});
+        }
+    RowStage<D>::store(rs, O + head_off + (long)qw * row_stride, row_stride, N - qw);
+    if (my_q < N && hl == 0) LSE[(long)bh * N + my_q] = m_run * kLn2 + __logf(l_tot);
 }
 
 hipError_t launch_fwd_fp8(const void* q, const void* k, const void* v, const float* q_descale,
