@@ -173,17 +173,19 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_b
 // transposed 32x32 MFMA result.  Stored from there, each store instruction
 // would put 16 bytes into each of 32 rows, and the L2 may write a 128-byte
 // line back before its other pieces arrive (partial writes that add bytes,
-// depending on timing).  So the rows go to the wave's LDS region (chunks
-// XOR-swizzled by the row, so that the 32 rows of one chunk hit different
-// banks) and come back with D / 8 lanes per row: every store instruction then
-// writes whole rows.  The region must not be in use by other waves.
+// depending on timing).  So the rows go to the wave's LDS region and come
+// back with D / 8 lanes per row: every store instruction then writes whole
+// rows.  Chunk c of row r sits at chunk c ^ (r mod D / 8), and the 8-byte half
+// a lane writes is flipped when bit 3 of its row is set, so that each group
+// of 16 lanes of an 8-byte write (rows r .. r + 15, one chunk) covers 128
+// distinct bytes of the 32 banks; the reads swap those rows' halves back.
+// The region must not be in use by other waves.
 template <int D>
 struct RowStage {
     static constexpr int BYTES = 32 * D * 2;   // LDS bytes per wave
     static constexpr int NCH = D / 8;          // 16-byte chunks per row
     static constexpr int RPI = 64 / NCH;       // rows per store instruction
-    __device__ __forceinline__ static int swz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
-    __device__ __forceinline__ static int at(int r, int c) { return r * (2 * D) + ((c ^ swz(r)) << 4); }
+    __device__ __forceinline__ static int at(int r, int c) { return r * (2 * D) + ((c ^ (r & (NCH - 1))) << 4); }
     // The lane index is formed afresh (mbcnt) in put and store, so that no
     // value derived from it has to stay live, or spill, through the main loop.
     __device__ __forceinline__ static int lane_id() {
@@ -192,7 +194,8 @@ struct RowStage {
     // the lane's 8 bytes of chunk c of its row
     __device__ __forceinline__ static void put(void* region, int c, u32x2 v) {
         const int lane = lane_id();
-        auto p = (__attribute__((address_space(3))) char*)(region) + at(lane & 31, c) + ((lane >> 5) << 3);
+        const int half = (lane >> 5) ^ ((lane >> 3) & 1);
+        auto p = (__attribute__((address_space(3))) char*)(region) + at(lane & 31, c) + (half << 3);
         *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(p) = v;
     }
     // rows 0 .. nrows - 1 to dst + r * stride elements; nrows is the same
@@ -203,9 +206,12 @@ struct RowStage {
         const int rr = lane / NCH, c = lane % NCH;
         u32x4 v[NI];
 #pragma unroll
-        for (int i = 0; i < NI; ++i)
-            v[i] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+        for (int i = 0; i < NI; ++i) {
+            const u32x4 w = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
                 as_lds(region) + at(i * RPI + rr, c));
+            // the RPI rows of one read share bit 3 (RPI is 4 or 8)
+            v[i] = ((i * RPI) & 8) ? __builtin_shufflevector(w, w, 2, 3, 0, 1) : w;
+        }
         __bf16* p = dst + (long)rr * stride + 8 * c;
         if (nrows >= 32) {
 #pragma unroll
