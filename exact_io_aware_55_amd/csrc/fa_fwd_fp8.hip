@@ -187,6 +187,11 @@ __global__ __launch_bounds__(fwd8::NT, 1) void fwd_fp8_kernel(
     f32x16 oacc[DT];
 #pragma unroll
     for (int i = 0; i < DT; ++i) oacc[i] = f32x16{};
+    // packed E4M3 P of a block (the B operands of O^T += V^T P^T), carried
+    // from block to block so that each packing starts from a live register
+    i32x8 pw[KP];
+#pragma unroll
+    for (int j = 0; j < KP; ++j) pw[j] = i32x8{};
     // running maximum (log2 units): raised only when a block's probabilities
     // grow too large (see below), so P = exp2(x - m) stays <= 256 < 448
     float m_run = -INFINITY;
@@ -253,7 +258,6 @@ __global__ __launch_bounds__(fwd8::NT, 1) void fwd_fp8_kernel(
         // O and l, exponentials again.  Every P that reaches the E4M3 product
         // is then at most 2^8 < 448, and O, l and LSE all use the same m.
         constexpr float kSumMax = 256.f;
-        i32x8 pw[KP];
         float ls0, ls1;
         auto exps = [&](float m_sub) {
             ls0 = 0.f;
@@ -270,13 +274,16 @@ __global__ __launch_bounds__(fwd8::NT, 1) void fwd_fp8_kernel(
                     }
                     ls0 += p[0] + p[2];
                     ls1 += p[1] + p[3];
-                    int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+                    // the two converts overwrite both halves of the word, so
+                    // its previous contents (last block's) are never seen
+                    const int e8 = (kt & 1) * 4 + (r >> 2);
+                    int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], pw[kt >> 1][e8], false);
                     w = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w, true);
-                    pw[kt >> 1][(kt & 1) * 4 + (r >> 2)] = w;
+                    pw[kt >> 1][e8] = w;
                 }
         };
         exps(m_run == -INFINITY ? 0.f : m_run);
-        if (__builtin_amdgcn_ballot_w64(!(ls0 + ls1 <= kSumMax) || m_run == -INFINITY) != 0) {
+        if (__builtin_expect(__builtin_amdgcn_ballot_w64(!(ls0 + ls1 <= kSumMax) || m_run == -INFINITY) != 0, 0)) {
             float mx = s[0][0];
             if constexpr (POS) {
 #pragma unroll
